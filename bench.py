@@ -1,0 +1,260 @@
+"""Benchmark: streaming chunk attention on one MI355X.
+
+One step = one steady-state chunk of a stream through the whole hot path:
+  sa_chunk_attend  -> rope_apply (RoPE of Q and K fused into their writes,
+                      V transposed into the cache) + chunk_attention
+                      (+ attn_combine when the key range is split)
+  sa_kv_append     -> kv_ring_append (RoPE of K fused, V transposed), evicting
+                      the oldest window chunk
+over seeded synthetic bf16 inputs already resident in HBM (a pool of 8
+distinct chunks cycled). The stream is filled to steady state (sink + full
+window) before the warm-up, so every timed chunk attends to
+(S + W + 1) * Nc keys. RoPE refresh and sink replacement do not occur in the
+default workload's schedule; they are timed separately and reported as extra
+fields.
+
+Output: one JSON line. value = attended query tokens/s (B * Nc per step);
+ms_per_step = ms per chunk. roofline = the chunk_attention kernel alone,
+algorithmic FLOPs 4*B*H*D*Nc*Nk over visible keys / its mean duration from
+HIP events recorded on the launch stream, against the MI355X dense bf16 peak.
+cpu_baseline = the fp64 NumPy oracle on a bounded sample of one steady chunk.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan1.3b]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attended query tokens/sec + ms/chunk; % bf16 MFMA peak (1 MI355X)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan1.3b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget for the oracle baseline sample")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attention_kernels.hip", "sa_internal.h"):
+        h.update(open(os.path.join(ROOT, "causal_windowed_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload, src_hash):
+    """HBM bytes per chunk_attention launch from a committed rocprofv3 --pmc summary, or None.
+
+    The summary records the kernel source hash it was taken with; a different
+    hash means the kernel changed since, and the figure is not reported.
+    """
+    path = os.path.join(PROFILES, f"chunk_attention_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """Time the fp64 oracle on a bounded sample of one steady-state chunk."""
+    import numpy as np
+    import synth
+    from oracle import HistoryOracle, StreamSpec
+    from dataclasses import replace
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:
+        blas = []
+    threads = max([t for _, t in blas if t] or [1])
+    steady = w.sink_chunks + w.window_chunks
+    heads_done, elapsed = 0, 0.0
+    for h in range(w.heads):
+        spec = replace(StreamSpec.from_workload(w), heads=1)
+        orc = HistoryOracle(spec)
+        for c in range(steady):
+            _, k, v = synth.chunk_qkv(w, c)
+            orc.append(k[:, :, h:h + 1], v[:, :, h:h + 1])
+        q, k, v = synth.chunk_qkv(w, steady)
+        t0 = time.perf_counter()
+        orc.attend(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+        if elapsed >= budget_s:
+            break
+    per_chunk_s = elapsed * w.heads / heads_done
+    return {
+        "value": w.batch * w.tokens_per_chunk / per_chunk_s,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{heads_done} of {w.heads} heads of one steady-state chunk "
+                   f"({w.tokens_per_chunk} query rows x {(steady + 1) * w.tokens_per_chunk} keys, fp64 "
+                   f"NumPy incl. RoPE), {elapsed:.1f} s, scaled to all heads"),
+        "seconds_per_chunk": per_chunk_s,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(a stream's caches live on one GPU; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import causal_windowed_attention_amd as cwa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("the benchmark workloads are bf16")
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
+                          w.sink_chunks, w.window_chunks, dtype="bf16")
+    s = cwa.Stream(cfg, device=dev)
+    nc = w.tokens_per_chunk
+    steady = w.sink_chunks + w.window_chunks
+    pool = []
+    for i in range(8):
+        q, k, v = synth.chunk_qkv(w, 100 + i)
+        pool.append(tuple(torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v)))
+    out = torch.empty_like(pool[0][0])
+
+    def step(i):
+        q, k, v = pool[i % len(pool)]
+        s.chunk_attend(q, k, v, out=out)
+        s.kv_append(k, v)
+
+    # ---- full stream from empty (warm-up chunks included), once -----------------
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(w.n_chunks):
+        step(i)
+    torch.cuda.synchronize()
+    stream_ms = (time.perf_counter() - t0) * 1e3
+    # after n_chunks >= S + W commits the stream is in steady state
+    assert s.query()["visible_keys"] == (steady + 1) * nc
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+    value = w.batch * nc * args.steps / dt
+
+    # ---- per-kernel durations: HIP events on the launch stream ------------------
+    s.set_option(cwa.SA_OPT_PROFILE, 1)
+    for k_id in range(cwa.SA_K_COUNT):
+        s.profile_read(k_id, reset=True)
+    for i in range(args.profile_steps):
+        step(i)
+    kern = {}
+    for name, k_id in (("rope_apply", cwa.SA_K_ROPE_APPLY), ("chunk_attention", cwa.SA_K_CHUNK_ATTENTION),
+                       ("attn_combine", cwa.SA_K_ATTN_COMBINE), ("kv_ring_append", cwa.SA_K_KV_APPEND)):
+        ms, n = s.profile_read(k_id, reset=True)
+        if n:
+            kern[name] = ms / n
+    st = s.query()
+    # refresh and sink update (not in this workload's schedule): timed separately
+    for _ in range(3):
+        s.rope_refresh(-1, 0)
+        s.sink_update(*[torch.cat([pool[0][j]] * w.sink_chunks, dim=1) for j in (1, 2)])
+    for name, k_id in (("rope_refresh", cwa.SA_K_ROPE_REFRESH), ("sink_update", cwa.SA_K_SINK_UPDATE)):
+        ms, n = s.profile_read(k_id, reset=True)
+        if n:
+            kern[name] = ms / n
+    s.set_option(cwa.SA_OPT_PROFILE, 0)
+
+    nk = st["visible_keys"]
+    flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk
+    attn_ms = kern["chunk_attention"]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    elem = w.batch * nc * w.heads * w.head_dim * 2
+    d_t = w.head_dim - 4 * (w.head_dim // 6)
+    gbs = lambda bytes_, ms: bytes_ / (ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(w.name, src_hash)
+    attend_ms = attn_ms + kern.get("rope_apply", 0.0) + kern.get("attn_combine", 0.0)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+            "frame": [w.frame_h, w.frame_w], "frames_per_chunk": w.frames_per_chunk,
+            "tokens_per_chunk": nc, "sink_chunks": w.sink_chunks, "window_chunks": w.window_chunks,
+            "visible_keys": nk, "step": "one steady-state chunk: attend (rope_apply + chunk_attention"
+            + (" + attn_combine" if st["last_kv_splits"] > 1 else "") + ") + append (kv_ring_append)",
+            "kv_splits": st["last_kv_splits"], "q_tiles": st["last_q_tiles"],
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "kernel": "chunk_attention_bf16<128>",
+            "flops_per_launch": flops,
+            "mean_ms": attn_ms,
+            "kernel_source_hash": src_hash,
+        },
+        "kernels_ms": kern,
+        "kernels_gbs": {
+            "rope_apply": gbs(6 * elem, kern["rope_apply"]) if "rope_apply" in kern else None,
+            "kv_ring_append": gbs(4 * elem, kern["kv_ring_append"]) if "kv_ring_append" in kern else None,
+            # temporal pairs of the window's rows, read and written
+            "rope_refresh": gbs(2 * w.batch * w.heads * w.window_chunks * nc * d_t * 2,
+                                kern["rope_refresh"]) if "rope_refresh" in kern else None,
+        },
+        "attend_ms": attend_ms,
+        "attend_tokens_per_s": w.batch * nc / (attend_ms * 1e-3),
+        "pct_bf16_peak_attend": flops / (attend_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stream_cold_start": {"chunks": w.n_chunks, "ms": stream_ms, "ms_per_chunk": stream_ms / w.n_chunks},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    s.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

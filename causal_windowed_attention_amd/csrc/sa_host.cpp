@@ -1,0 +1,633 @@
+// Host side of the streaming chunk attention library: config validation,
+// workspace layout, stream bookkeeping (sink, window ring, positions), launch
+// planning and the C ABI declared in include/sa.h.
+//
+// Cache layout. Per (b, h) the cache has n_slots = S + W + 1 physical chunk
+// slots: slots [0, S) hold the sink, slots [S, S + W + 1) are the window ring.
+// The ring has one slot more than the window so the chunk being attended can
+// be staged in the slot that holds no visible chunk: the r-th window commit
+// lands in ring slot r mod (W + 1), and the next chunk is staged in ring slot
+// ring_commits mod (W + 1) (or in the next sink slot while the sink fills).
+// A commit of the staged chunk therefore needs no copy. With this assignment
+// the slots the next attend sees (committed sink chunks, the last min(r, W)
+// window commits and the staging slot) are always the physical prefix
+// [0, visible_chunks), so the attention kernel reads one contiguous key range
+// per (b, h) and skips everything else.
+//
+// Stream semantics follow StreamDiffusionV2 ("Sommario tecnico" 2.A.1: chunked
+// B x T' x H x W processing; 2.A.2: sink updates and periodic RoPE offset
+// resets at chunk boundaries) and SANA-Streaming ("Transformer a diffusione
+// ibrido": softmax over a sliding local window plus a persistent sink chunk).
+#include "../../include/sa.h"
+#include "sa_internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+namespace {
+
+using sa::AttnParams;
+using sa::CombineParams;
+using sa::RefreshParams;
+using sa::RopeWriteParams;
+
+constexpr size_t kAlign = 256;
+constexpr int32_t kMaxPosition = 1 << 30;   // guard against int32 overflow when max_t == 0
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Derived {
+  int32_t B, H, D, Hf, Wf, F, S, W, R, n_slots, Nc, dt, dh, dw, max_t, dtype, elem;
+  int32_t key_stride, q_tiles, max_splits;
+  double theta;
+  float scale;
+  size_t k_off, k_bytes, vt_off, vt_bytes, q_off, q_bytes, part_off, part_bytes, tab_off, tab_bytes,
+      total;
+};
+
+sa_status derive(const sa_config* c, Derived* d) {
+  if (c == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  if (c->batch < 1 || c->heads < 1 || c->frame_h < 1 || c->frame_w < 1 || c->frames_per_chunk < 1 ||
+      c->sink_chunks < 0 || c->window_chunks < 0 || c->max_t < 0 || c->head_dim < 2 ||
+      c->head_dim % 2 != 0)
+    return SA_ERR_INVALID_ARGUMENT;
+  if (c->dtype != SA_F32 && c->dtype != SA_BF16) return SA_ERR_INVALID_ARGUMENT;
+  if (!(c->rope_theta >= 0.0) || !(c->softmax_scale >= 0.f) || !std::isfinite(c->rope_theta) ||
+      !std::isfinite(c->softmax_scale))
+    return SA_ERR_INVALID_ARGUMENT;
+  if (c->rope_theta != 0.0 && c->rope_theta <= 1.0) return SA_ERR_INVALID_ARGUMENT;
+  d->B = c->batch; d->H = c->heads; d->D = c->head_dim; d->Hf = c->frame_h; d->Wf = c->frame_w;
+  d->F = c->frames_per_chunk; d->S = c->sink_chunks; d->W = c->window_chunks; d->max_t = c->max_t;
+  d->dtype = c->dtype;
+  d->elem = c->dtype == SA_BF16 ? 2 : 4;
+  if (c->rope_dim_t == 0 && c->rope_dim_h == 0 && c->rope_dim_w == 0) {
+    d->dh = d->dw = 2 * (d->D / 6);
+    d->dt = d->D - 2 * d->dh;
+  } else {
+    d->dt = c->rope_dim_t; d->dh = c->rope_dim_h; d->dw = c->rope_dim_w;
+    if (d->dt < 0 || d->dh < 0 || d->dw < 0 || d->dt % 2 || d->dh % 2 || d->dw % 2 ||
+        d->dt + d->dh + d->dw != d->D)
+      return SA_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t nc = static_cast<int64_t>(d->F) * d->Hf * d->Wf;
+  if (nc > (1 << 20)) return SA_ERR_UNSUPPORTED;
+  d->Nc = static_cast<int32_t>(nc);
+  if (static_cast<int64_t>(d->S) + d->W + 1 > (1 << 16)) return SA_ERR_UNSUPPORTED;
+  d->R = d->W + 1;
+  d->n_slots = d->S + d->R;
+  const int64_t keys = static_cast<int64_t>(d->n_slots) * d->Nc;
+  if (keys > (1 << 24)) return SA_ERR_UNSUPPORTED;
+  if (d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(d->F) * (d->dt / 2) > sa::kMaxTemporalPairs) return SA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(d->B) * d->H > 65535) return SA_ERR_UNSUPPORTED;
+  if (d->max_t > 0 && static_cast<int64_t>(d->S) * d->F > d->max_t) return SA_ERR_POSITION_RANGE;
+  d->theta = c->rope_theta == 0.0 ? 10000.0 : c->rope_theta;
+  d->scale = c->softmax_scale == 0.f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->D)))
+                                     : c->softmax_scale;
+  d->key_stride = static_cast<int32_t>(align_up(static_cast<size_t>(keys), 64));
+  const int bm = d->dtype == SA_BF16 ? sa::kBf16BlockM : sa::kF32BlockM;
+  d->q_tiles = (d->Nc + bm - 1) / bm;
+  // partial buffers only where splitting can help filling the chip
+  const int64_t blocks = static_cast<int64_t>(d->B) * d->H * d->q_tiles;
+  int64_t ms = (1024 + blocks - 1) / blocks;
+  d->max_splits = static_cast<int32_t>(ms < 1 ? 1 : (ms > sa::kMaxKvSplits ? sa::kMaxKvSplits : ms));
+
+  const size_t bh = static_cast<size_t>(d->B) * d->H;
+  d->k_bytes = bh * static_cast<size_t>(keys) * d->D * d->elem;
+  d->vt_bytes = bh * static_cast<size_t>(d->D) * d->key_stride * d->elem;
+  d->q_bytes = bh * static_cast<size_t>(d->Nc) * d->D * d->elem;
+  d->part_bytes = d->max_splits > 1
+                      ? static_cast<size_t>(d->max_splits) * bh * d->Nc * (static_cast<size_t>(d->D) + 1) * 4
+                      : 0;
+  d->tab_bytes = (static_cast<size_t>(d->Hf) * (d->dh / 2) + static_cast<size_t>(d->Wf) * (d->dw / 2)) * 8;
+  size_t off = 0;
+  d->k_off = off; off = align_up(off + d->k_bytes, kAlign);
+  d->vt_off = off; off = align_up(off + d->vt_bytes, kAlign);
+  d->q_off = off; off = align_up(off + d->q_bytes, kAlign);
+  d->part_off = off; off = align_up(off + d->part_bytes, kAlign);
+  d->tab_off = off; off = align_up(off + d->tab_bytes, kAlign);
+  d->total = off;
+  return SA_OK;
+}
+
+struct SlotMeta {
+  int32_t kind = SA_SLOT_EMPTY;
+  int64_t chunk_id = 0;
+  int32_t t0 = 0;
+};
+
+struct Prof {
+  double total_ms = 0.0;
+  int64_t launches = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> free_pairs;
+};
+
+}  // namespace
+
+struct sa_stream {
+  Derived d;
+  char* ws = nullptr;          // null: planning handle
+  // state (D3)
+  int64_t n_appends = 0, ring_commits = 0;
+  int32_t t_next = 0, sink_fill = 0;
+  std::vector<SlotMeta> slots;
+  bool staged_valid = false;
+  int32_t staged_t = 0, staged_slot = -1;
+  // last plan (D4)
+  int32_t last_q_tiles = 0, last_kv_splits = 0, last_key_tiles = 0, last_delta = 0;
+  int32_t kv_splits_opt = 0;
+  bool profile = false;
+  Prof prof[SA_K_COUNT];
+
+  int32_t window_valid() const {
+    if (sink_fill < d.S) return 0;
+    return static_cast<int32_t>(ring_commits < d.W ? ring_commits : d.W);
+  }
+  int32_t staging_slot() const {
+    if (sink_fill < d.S) return sink_fill;
+    return d.S + static_cast<int32_t>(ring_commits % d.R);
+  }
+  int32_t visible_chunks() const { return sink_fill + window_valid() + 1; }
+  bool planning() const { return ws == nullptr; }
+  void* kcache() const { return ws + d.k_off; }
+  void* vtcache() const { return ws + d.vt_off; }
+  void* qscratch() const { return ws + d.q_off; }
+  const float2* h_cs() const { return reinterpret_cast<const float2*>(ws + d.tab_off); }
+  const float2* w_cs() const { return h_cs() + static_cast<size_t>(d.Hf) * (d.dh / 2); }
+};
+
+namespace {
+
+sa_status positions_ok(const sa_stream* s, int64_t last_pos_exclusive) {
+  if (s->d.max_t > 0 && last_pos_exclusive > s->d.max_t) return SA_ERR_POSITION_RANGE;
+  if (last_pos_exclusive > kMaxPosition) return SA_ERR_POSITION_RANGE;
+  return SA_OK;
+}
+
+double freq(const Derived& d, int seg_len, int j) {
+  return std::pow(d.theta, -2.0 * j / seg_len);
+}
+
+// Temporal (cos, sin) table for frames t0 .. t0+F-1: [frame][d_t/2].
+void fill_temporal(const Derived& d, int64_t t0, int n_frames, float2* out) {
+  const int np = d.dt / 2;
+  for (int f = 0; f < n_frames; ++f)
+    for (int j = 0; j < np; ++j) {
+      const double a = static_cast<double>(t0 + f) * freq(d, d.dt, j);
+      out[f * np + j] = make_float2(static_cast<float>(std::cos(a)), static_cast<float>(std::sin(a)));
+    }
+}
+
+void base_write_params(const sa_stream* s, RopeWriteParams* p) {
+  std::memset(p, 0, sizeof(*p));
+  const Derived& d = s->d;
+  p->kcache = s->kcache();
+  p->vtcache = s->vtcache();
+  p->h_cs = s->h_cs();
+  p->w_cs = s->w_cs();
+  p->k_bh_stride = static_cast<int64_t>(d.n_slots) * d.Nc * d.D;
+  p->vt_bh_stride = static_cast<int64_t>(d.D) * d.key_stride;
+  p->key_stride = d.key_stride;
+  p->n_tokens = d.Nc;
+  p->in_tokens = d.Nc;
+  p->B = d.B; p->H = d.H; p->D = d.D; p->Hf = d.Hf; p->Wf = d.Wf;
+  p->dt = d.dt; p->dh = d.dh; p->dw = d.dw;
+  p->n_frames = d.F;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Launch with optional event timing on the launch stream.
+template <typename F>
+sa_status timed(sa_stream* s, int kid, hipStream_t st, F&& launch) {
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (s->profile) {
+    Prof& pr = s->prof[kid];
+    if (!pr.free_pairs.empty()) {
+      ev = pr.free_pairs.back();
+      pr.free_pairs.pop_back();
+    } else {
+      if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess)
+        return SA_ERR_DEVICE;
+    }
+    if (hipEventRecord(ev.first, st) != hipSuccess) return SA_ERR_DEVICE;
+  }
+  if (launch() != hipSuccess) return SA_ERR_DEVICE;
+  if (s->profile) {
+    if (hipEventRecord(ev.second, st) != hipSuccess) return SA_ERR_DEVICE;
+    s->prof[kid].pending.push_back(ev);
+  }
+  return SA_OK;
+}
+
+int choose_splits(const sa_stream* s, int key_tiles) {
+  const Derived& d = s->d;
+  int splits = s->kv_splits_opt;
+  if (splits <= 0) {
+    // Fill the chip: 256 CUs x 2 resident workgroups. Split the key range only
+    // when the (b, h, q-tile) grid leaves more than a quarter of the slots idle.
+    const int64_t blocks = static_cast<int64_t>(d.B) * d.H * d.q_tiles;
+    const int64_t slots = 512;
+    splits = 1;
+    if (blocks * 4 < slots * 3) {
+      splits = static_cast<int>((slots + blocks - 1) / blocks);
+      if (splits > d.max_splits) splits = d.max_splits;
+    }
+  }
+  if (splits > key_tiles) splits = key_tiles;
+  if (splits < 1) splits = 1;
+  return splits;
+}
+
+void commit_meta(sa_stream* s) {
+  const int32_t slot = s->staging_slot();
+  SlotMeta& m = s->slots[slot];
+  m.chunk_id = s->n_appends;
+  m.t0 = s->t_next;
+  if (s->sink_fill < s->d.S) {
+    m.kind = SA_SLOT_SINK;
+    s->sink_fill += 1;
+  } else {
+    m.kind = SA_SLOT_WINDOW;
+    s->ring_commits += 1;
+    if (s->ring_commits > s->d.W) {   // the commit W+1 back leaves the window
+      const int64_t evicted = s->ring_commits - 1 - s->d.W;
+      s->slots[s->d.S + static_cast<int32_t>(evicted % s->d.R)].kind = SA_SLOT_EMPTY;
+    }
+  }
+  s->t_next += s->d.F;
+  s->n_appends += 1;
+  s->staged_valid = false;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_string(sa_status st) {
+  switch (st) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARGUMENT: return "SA_ERR_INVALID_ARGUMENT";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_BAD_STATE: return "SA_ERR_BAD_STATE";
+    case SA_ERR_WORKSPACE_TOO_SMALL: return "SA_ERR_WORKSPACE_TOO_SMALL";
+    case SA_ERR_POSITION_RANGE: return "SA_ERR_POSITION_RANGE";
+    case SA_ERR_DEVICE: return "SA_ERR_DEVICE";
+  }
+  return "SA_ERR_UNKNOWN";
+}
+
+sa_status sa_config_check(const sa_config* cfg) {
+  Derived d;
+  return derive(cfg, &d);
+}
+
+size_t sa_workspace_bytes(const sa_config* cfg) {
+  Derived d;
+  if (derive(cfg, &d) != SA_OK) return 0;
+  return d.total;
+}
+
+sa_status sa_stream_create(const sa_config* cfg, void* d_workspace, size_t workspace_bytes, void* stream,
+                           sa_stream** out) {
+  if (out == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  Derived d;
+  sa_status st = derive(cfg, &d);
+  if (st != SA_OK) return st;
+  if (d_workspace != nullptr) {
+    if (workspace_bytes < d.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+    if ((reinterpret_cast<uintptr_t>(d_workspace) & (kAlign - 1)) != 0) return SA_ERR_INVALID_ARGUMENT;
+  }
+  sa_stream* s = new (std::nothrow) sa_stream();
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  s->d = d;
+  s->ws = static_cast<char*>(d_workspace);
+  s->slots.assign(d.n_slots, SlotMeta());
+  if (!s->planning()) {
+    // spatial tables: [Hf][d_h/2] then [Wf][d_w/2], host fp64 -> fp32
+    std::vector<float2> tab(static_cast<size_t>(d.Hf) * (d.dh / 2) + static_cast<size_t>(d.Wf) * (d.dw / 2));
+    size_t i = 0;
+    for (int y = 0; y < d.Hf; ++y)
+      for (int j = 0; j < d.dh / 2; ++j) {
+        const double a = y * freq(d, d.dh, j);
+        tab[i++] = make_float2(static_cast<float>(std::cos(a)), static_cast<float>(std::sin(a)));
+      }
+    for (int x = 0; x < d.Wf; ++x)
+      for (int j = 0; j < d.dw / 2; ++j) {
+        const double a = x * freq(d, d.dw, j);
+        tab[i++] = make_float2(static_cast<float>(std::cos(a)), static_cast<float>(std::sin(a)));
+      }
+    if (!tab.empty()) {
+      // synchronous copy: the host table dies with this call
+      hipStream_t hs = static_cast<hipStream_t>(stream);
+      if (hipMemcpyAsync(s->ws + d.tab_off, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice,
+                         hs) != hipSuccess ||
+          hipStreamSynchronize(hs) != hipSuccess) {
+        delete s;
+        return SA_ERR_DEVICE;
+      }
+    }
+  }
+  *out = s;
+  return SA_OK;
+}
+
+sa_status sa_stream_destroy(sa_stream* s) {
+  if (s == nullptr) return SA_OK;
+  for (auto& pr : s->prof) {
+    for (auto& e : pr.pending) {
+      (void)hipEventSynchronize(e.second);
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+    for (auto& e : pr.free_pairs) {
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+  }
+  delete s;
+  return SA_OK;
+}
+
+sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void* v, void* out, float* lse,
+                          void* stream) {
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  const Derived& d = s->d;
+  if (!s->planning()) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return SA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return SA_ERR_INVALID_ARGUMENT;
+  }
+  sa_status st = positions_ok(s, static_cast<int64_t>(s->t_next) + d.F);
+  if (st != SA_OK) return st;
+
+  const int32_t slot = s->staging_slot();
+  const int32_t n_keys = s->visible_chunks() * d.Nc;
+  const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
+  const int key_tiles = (n_keys + bn - 1) / bn;
+  const int splits = choose_splits(s, key_tiles);
+
+  if (!s->planning()) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    RopeWriteParams rp;
+    base_write_params(s, &rp);
+    rp.q = q; rp.k = k; rp.v = v;
+    rp.qrot = s->qscratch();
+    rp.row0 = slot * d.Nc;
+    fill_temporal(d, s->t_next, d.F, rp.t_cs);
+    st = timed(s, SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply(rp, d.dtype, hs); });
+    if (st != SA_OK) return st;
+
+    AttnParams ap;
+    std::memset(&ap, 0, sizeof(ap));
+    ap.q = s->qscratch();
+    ap.kcache = s->kcache();
+    ap.vtcache = s->vtcache();
+    ap.out = out;
+    ap.lse = lse;
+    ap.part_o = reinterpret_cast<float*>(s->ws + d.part_off);
+    ap.part_lse = ap.part_o + static_cast<size_t>(d.max_splits) * d.B * d.H * d.Nc * d.D;
+    ap.k_bh_stride = static_cast<int64_t>(d.n_slots) * d.Nc * d.D;
+    ap.vt_bh_stride = static_cast<int64_t>(d.D) * d.key_stride;
+    ap.key_stride = d.key_stride;
+    ap.n_keys = n_keys;
+    ap.Nc = d.Nc; ap.B = d.B; ap.H = d.H; ap.D = d.D;
+    ap.q_tiles = d.q_tiles;
+    ap.kv_splits = splits;
+    ap.key_tiles = key_tiles;
+    ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    st = timed(s, SA_K_CHUNK_ATTENTION, hs, [&] { return sa::launch_chunk_attention(ap, d.dtype, hs); });
+    if (st != SA_OK) return st;
+    if (splits > 1) {
+      CombineParams cp;
+      cp.part_o = ap.part_o;
+      cp.part_lse = ap.part_lse;
+      cp.out = out;
+      cp.lse = lse;
+      cp.Nc = d.Nc; cp.B = d.B; cp.H = d.H; cp.D = d.D; cp.kv_splits = splits;
+      st = timed(s, SA_K_ATTN_COMBINE, hs, [&] { return sa::launch_attn_combine(cp, d.dtype, hs); });
+      if (st != SA_OK) return st;
+    }
+  }
+  s->staged_valid = true;
+  s->staged_t = s->t_next;
+  s->staged_slot = slot;
+  s->last_q_tiles = d.q_tiles;
+  s->last_kv_splits = splits;
+  s->last_key_tiles = key_tiles;
+  return SA_OK;
+}
+
+sa_status sa_kv_append(sa_stream* s, const void* k, const void* v, void* stream) {
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  const Derived& d = s->d;
+  const bool commit_staged = (k == nullptr && v == nullptr);
+  if (!commit_staged && !s->planning()) {
+    if (k == nullptr || v == nullptr || !aligned16(k) || !aligned16(v)) return SA_ERR_INVALID_ARGUMENT;
+  }
+  sa_status st = positions_ok(s, static_cast<int64_t>(s->t_next) + d.F);
+  if (st != SA_OK) return st;
+  const int32_t slot = s->staging_slot();
+  if (commit_staged) {
+    if (!s->staged_valid || s->staged_t != s->t_next || s->staged_slot != slot) return SA_ERR_BAD_STATE;
+  } else if (!s->planning()) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    RopeWriteParams rp;
+    base_write_params(s, &rp);
+    rp.k = k; rp.v = v;
+    rp.row0 = slot * d.Nc;
+    fill_temporal(d, s->t_next, d.F, rp.t_cs);
+    st = timed(s, SA_K_KV_APPEND, hs, [&] { return sa::launch_kv_append(rp, d.dtype, hs); });
+    if (st != SA_OK) return st;
+  }
+  commit_meta(s);
+  return SA_OK;
+}
+
+sa_status sa_rope_refresh(sa_stream* s, int32_t new_base_t, uint32_t flags, void* stream, int32_t* delta_out) {
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  if ((flags & ~SA_REFRESH_SHIFT_SINK) != 0) return SA_ERR_INVALID_ARGUMENT;
+  if (new_base_t < -1) return SA_ERR_INVALID_ARGUMENT;
+  const Derived& d = s->d;
+  const int64_t base = new_base_t == -1 ? static_cast<int64_t>(d.S) * d.F : new_base_t;
+  const int32_t wv = s->window_valid();
+  std::vector<int32_t> win;                     // physical slots of visible window chunks, oldest first
+  for (int64_t c = s->ring_commits - wv; c < s->ring_commits; ++c)
+    win.push_back(d.S + static_cast<int32_t>(c % d.R));
+  const int64_t ref = win.empty() ? s->t_next : s->slots[win[0]].t0;
+  const int64_t delta = ref - base;
+  const int64_t new_t_next = s->t_next - delta;
+  if (new_t_next < 0 || new_t_next > kMaxPosition) return SA_ERR_POSITION_RANGE;
+  std::vector<int32_t> targets = win;
+  if (flags & SA_REFRESH_SHIFT_SINK) {
+    for (int32_t j = 0; j < s->sink_fill; ++j) {
+      const int64_t t = static_cast<int64_t>(s->slots[j].t0) - delta;
+      if (t < -kMaxPosition || t > kMaxPosition) return SA_ERR_POSITION_RANGE;
+      targets.push_back(j);
+    }
+  }
+  if (!s->planning() && delta != 0 && !targets.empty()) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    RefreshParams rp;
+    std::memset(&rp, 0, sizeof(rp));
+    rp.kcache = s->kcache();
+    rp.k_bh_stride = static_cast<int64_t>(d.n_slots) * d.Nc * d.D;
+    rp.BH = d.B * d.H; rp.D = d.D; rp.Nc = d.Nc; rp.dt = d.dt;
+    for (int j = 0; j < d.dt / 2; ++j) {
+      const double a = -static_cast<double>(delta) * freq(d, d.dt, j);
+      rp.cs[j] = make_float2(static_cast<float>(std::cos(a)), static_cast<float>(std::sin(a)));
+    }
+    for (size_t i0 = 0; i0 < targets.size(); i0 += sa::kMaxRefreshSlots) {
+      rp.n_slot = 0;
+      for (size_t i = i0; i < targets.size() && rp.n_slot < sa::kMaxRefreshSlots; ++i)
+        rp.slot_row0[rp.n_slot++] = targets[i] * d.Nc;
+      sa_status st = timed(s, SA_K_ROPE_REFRESH, hs, [&] { return sa::launch_rope_refresh(rp, d.dtype, hs); });
+      if (st != SA_OK) return st;
+    }
+  }
+  for (int32_t j : targets) s->slots[j].t0 = static_cast<int32_t>(s->slots[j].t0 - delta);
+  s->t_next = static_cast<int32_t>(new_t_next);
+  if (delta != 0) s->staged_valid = false;
+  s->last_delta = static_cast<int32_t>(delta);
+  if (delta_out != nullptr) *delta_out = static_cast<int32_t>(delta);
+  return SA_OK;
+}
+
+sa_status sa_sink_update(sa_stream* s, const void* k, const void* v, void* stream) {
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  const Derived& d = s->d;
+  if (d.S == 0) return SA_ERR_BAD_STATE;
+  if (!s->planning() && (k == nullptr || v == nullptr || !aligned16(k) || !aligned16(v)))
+    return SA_ERR_INVALID_ARGUMENT;
+  sa_status st = positions_ok(s, static_cast<int64_t>(d.S) * d.F);
+  if (st != SA_OK) return st;
+  if (!s->planning()) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    RopeWriteParams rp;
+    base_write_params(s, &rp);
+    rp.k = k; rp.v = v;
+    rp.in_tokens = d.S * d.Nc;
+    for (int32_t j = 0; j < d.S; ++j) {
+      rp.row0 = j * d.Nc;
+      rp.in_tok0 = j * d.Nc;
+      fill_temporal(d, static_cast<int64_t>(j) * d.F, d.F, rp.t_cs);
+      st = timed(s, SA_K_SINK_UPDATE, hs, [&] { return sa::launch_sink_update(rp, d.dtype, hs); });
+      if (st != SA_OK) return st;
+    }
+  }
+  for (int32_t j = 0; j < d.S; ++j) {
+    s->slots[j].kind = SA_SLOT_SINK;
+    s->slots[j].chunk_id = -1;
+    s->slots[j].t0 = j * d.F;
+  }
+  s->sink_fill = d.S;
+  s->staged_valid = false;
+  return SA_OK;
+}
+
+sa_status sa_stream_query(const sa_stream* s, sa_state* out) {
+  if (s == nullptr || out == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  sa_state st;
+  std::memset(&st, 0, sizeof(st));
+  st.n_appends = s->n_appends;
+  st.ring_commits = s->ring_commits;
+  st.t_next = s->t_next;
+  st.sink_fill = s->sink_fill;
+  st.window_valid = s->window_valid();
+  st.staging_slot = s->staging_slot();
+  st.n_slots = s->d.n_slots;
+  st.visible_chunks = s->visible_chunks();
+  st.visible_keys = st.visible_chunks * s->d.Nc;
+  st.staged_valid = s->staged_valid && s->staged_t == s->t_next && s->staged_slot == st.staging_slot;
+  st.last_q_tiles = s->last_q_tiles;
+  st.last_kv_splits = s->last_kv_splits;
+  st.last_key_tiles = s->last_key_tiles;
+  st.last_delta = s->last_delta;
+  *out = st;
+  return SA_OK;
+}
+
+sa_status sa_stream_slot(const sa_stream* s, int32_t slot, sa_slot_info* out) {
+  if (s == nullptr || out == nullptr || slot < 0 || slot >= s->d.n_slots) return SA_ERR_INVALID_ARGUMENT;
+  const SlotMeta& m = s->slots[slot];
+  sa_slot_info info;
+  info.kind = m.kind;
+  info.chunk_id = m.chunk_id;
+  info.t0 = m.t0;
+  if (slot == s->staging_slot() && m.kind != SA_SLOT_SINK) {
+    info.kind = SA_SLOT_STAGING;
+    info.chunk_id = s->n_appends;
+    info.t0 = s->t_next;
+  } else if (m.kind == SA_SLOT_EMPTY) {
+    info.chunk_id = -1;
+    info.t0 = 0;
+  }
+  *out = info;
+  return SA_OK;
+}
+
+sa_status sa_stream_layout(const sa_stream* s, sa_layout* out) {
+  if (s == nullptr || out == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  const Derived& d = s->d;
+  sa_layout L;
+  std::memset(&L, 0, sizeof(L));
+  L.k_offset = d.k_off;
+  L.k_bh_stride = static_cast<uint64_t>(d.n_slots) * d.Nc * d.D * d.elem;
+  L.vt_offset = d.vt_off;
+  L.vt_bh_stride = static_cast<uint64_t>(d.D) * d.key_stride * d.elem;
+  L.q_offset = d.q_off;
+  L.q_bh_stride = static_cast<uint64_t>(d.Nc) * d.D * d.elem;
+  L.partial_offset = d.part_off;
+  L.partial_bytes = d.part_bytes;
+  L.table_offset = d.tab_off;
+  L.table_bytes = d.tab_bytes;
+  L.key_stride = d.key_stride;
+  L.elem_bytes = d.elem;
+  L.max_kv_splits = d.max_splits;
+  *out = L;
+  return SA_OK;
+}
+
+sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value) {
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  switch (option) {
+    case SA_OPT_KV_SPLITS:
+      if (value < 0 || value > s->d.max_splits) return SA_ERR_INVALID_ARGUMENT;
+      s->kv_splits_opt = static_cast<int32_t>(value);
+      return SA_OK;
+    case SA_OPT_PROFILE:
+      if (value != 0 && value != 1) return SA_ERR_INVALID_ARGUMENT;
+      if (value == 1 && s->planning()) return SA_ERR_BAD_STATE;
+      s->profile = value == 1;
+      return SA_OK;
+    default:
+      return SA_ERR_INVALID_ARGUMENT;
+  }
+}
+
+sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int64_t* launches, int32_t reset) {
+  if (s == nullptr || kernel_id < 0 || kernel_id >= SA_K_COUNT) return SA_ERR_INVALID_ARGUMENT;
+  Prof& pr = s->prof[kernel_id];
+  for (auto& e : pr.pending) {
+    if (hipEventSynchronize(e.second) != hipSuccess) return SA_ERR_DEVICE;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e.first, e.second) != hipSuccess) return SA_ERR_DEVICE;
+    pr.total_ms += ms;
+    pr.launches += 1;
+    pr.free_pairs.push_back(e);
+  }
+  pr.pending.clear();
+  if (total_ms != nullptr) *total_ms = pr.total_ms;
+  if (launches != nullptr) *launches = pr.launches;
+  if (reset) {
+    pr.total_ms = 0.0;
+    pr.launches = 0;
+  }
+  return SA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal launch parameters shared by the host library (sa_host.cpp) and the
+// HIP kernels (rope_kernels.hip, attention_kernels.hip). Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kMaxTemporalPairs = 320;  // F * d_t / 2 per launch (table passed by value)
+constexpr int kMaxRefreshSlots = 64;    // slots re-rotated by one refresh launch
+constexpr int kMaxRefreshPairs = 64;    // d_t / 2 <= D / 2 <= 64
+
+// bf16 attention tiling (chunk_attention_bf16): 4 waves x 32 query rows, 64-key tiles.
+constexpr int kBf16BlockM = 128;
+constexpr int kBf16BlockN = 64;
+// fp32 attention tiling (chunk_attention_f32): 64 query rows, 32-key tiles.
+constexpr int kF32BlockM = 64;
+constexpr int kF32BlockN = 32;
+// Key-range splits per query tile (partials are merged by attn_combine).
+constexpr int kMaxKvSplits = 8;
+
+// Rotate-and-store of a chunk's K (and optionally Q) plus V into the cache:
+// rope_apply (Q -> scratch, K/V -> staging slot), kv_ring_append (K/V -> a slot),
+// and the sink update (one launch per sink chunk).
+struct RopeWriteParams {
+  const void* q;        // [B, in_tokens, H, D] or null (no Q)
+  const void* k;        // [B, in_tokens, H, D]
+  const void* v;        // [B, in_tokens, H, D]
+  void* qrot;           // [B*H][Nc][D] rotated Q scratch (when q != null)
+  void* kcache;         // [B*H][n_slots*Nc][D]
+  void* vtcache;        // [B*H][D][key_stride]
+  const float2* h_cs;   // [Hf][d_h/2] (cos, sin) of y * theta_h,j
+  const float2* w_cs;   // [Wf][d_w/2] (cos, sin) of x * theta_w,j
+  int64_t k_bh_stride;  // elements
+  int64_t vt_bh_stride; // elements
+  int32_t key_stride;   // elements per V^T channel row
+  int32_t row0;         // first cache row (key index) of the target slot
+  int32_t n_tokens;     // tokens written (Nc)
+  int32_t in_tokens;    // tokens per batch entry in the input tensors
+  int32_t in_tok0;      // first input token of this launch
+  int32_t B, H, D, Hf, Wf;
+  int32_t dt, dh, dw;
+  int32_t n_frames;     // frames covered by t_cs (F)
+  float2 t_cs[kMaxTemporalPairs];  // [frame][d_t/2]: (cos, sin) of (t0 + frame) * theta_t,j
+};
+
+// In-place re-rotation of the temporal pairs of whole cache slots by -Delta.
+struct RefreshParams {
+  void* kcache;         // [B*H][n_slots*Nc][D]
+  int64_t k_bh_stride;  // elements
+  int32_t BH, D, Nc, dt;
+  int32_t n_slot;
+  int32_t slot_row0[kMaxRefreshSlots];
+  float2 cs[kMaxRefreshPairs];     // (cos, sin) of -Delta * theta_t,j
+};
+
+// Attention of one chunk over the visible key prefix [0, n_keys) of every (b, h).
+struct AttnParams {
+  const void* q;        // [B*H][Nc][D] rotated queries
+  const void* kcache;   // [B*H][rows][D]
+  const void* vtcache;  // [B*H][D][key_stride]
+  void* out;            // [B][Nc][H][D]
+  float* lse;           // [B][H][Nc] natural log, or null
+  float* part_o;        // [splits][B*H][Nc][D] normalised partial outputs
+  float* part_lse;      // [splits][B*H][Nc] partial log2-sum-exp (log2 units)
+  int64_t k_bh_stride;  // elements
+  int64_t vt_bh_stride; // elements
+  int32_t key_stride;
+  int32_t n_keys;
+  int32_t Nc, B, H, D;
+  int32_t q_tiles;      // ceil(Nc / BlockM)
+  int32_t kv_splits;    // >= 1
+  int32_t key_tiles;    // ceil(n_keys / BlockN)
+  float scale_log2;     // softmax_scale * log2(e)
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  void* out;            // [B][Nc][H][D]
+  float* lse;           // or null
+  int32_t Nc, B, H, D, kv_splits;
+};
+
+// dtype: 0 = fp32, 1 = bf16 (sa_dtype)
+hipError_t launch_rope_apply(const RopeWriteParams& p, int dtype, hipStream_t st);
+hipError_t launch_kv_append(const RopeWriteParams& p, int dtype, hipStream_t st);
+hipError_t launch_sink_update(const RopeWriteParams& p, int dtype, hipStream_t st);
+hipError_t launch_rope_refresh(const RefreshParams& p, int dtype, hipStream_t st);
+hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st);
+hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,257 @@
+/*
+ * sa.h -- C ABI of the streaming chunk attention library (libsa.so, gfx950).
+ *
+ * What it computes. Video is generated chunk by chunk; each chunk holds F latent
+ * frames of Hf x Wf tokens (the B x T' x H x W input form of StreamDiffusionV2,
+ * "Sommario tecnico" 2.A.1). Every query token of the current chunk gets a 3D
+ * (t, h, w) rotary position embedding and attends with full softmax attention
+ * to (1) a persistent sink chunk, (2) a sliding window of the most recent
+ * committed chunks and (3) the current chunk itself (SANA-Streaming,
+ * "Transformer a diffusione ibrido": softmax blocks with a sliding local window
+ * and a persistent sink chunk). Keys are kept rotated in a bounded cache whose
+ * temporal RoPE offsets can be re-based at chunk boundaries so that long
+ * streams stay inside the trained position range, and the sink can be replaced
+ * (StreamDiffusionV2, "Sommario tecnico" 2.A.2: sink tokens updated during the
+ * stream, RoPE offsets reset periodically at block boundaries).
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *  - RoPE: head_dim D is split into contiguous segments [t | h | w] of even
+ *    lengths (default d_h = d_w = 2*floor(D/6), d_t = D - 2*d_h); pair j of a
+ *    segment of length d is channels (o+2j, o+2j+1) with frequency
+ *    theta^(-2j/d); the rotation of a pair is RoFormer's.
+ *  - Token n of a chunk sits at (t_next + n / (Hf*Wf), (n / Wf) % Hf, n % Wf).
+ *  - The first S committed chunks fill the sink; later commits enter the
+ *    window; W counts previous chunks (the current chunk is extra).
+ *  - Softmax scale defaults to 1/sqrt(D).
+ *
+ * Layouts. q, k, v and out are [B, Nc, H, D] contiguous (token-major, what a
+ * fused QKV projection writes), Nc = F*Hf*Wf, element type = config dtype.
+ * lse is [B, H, Nc] float32 (natural log). The workspace is opaque device
+ * memory sized by sa_workspace_bytes(); sa_stream_layout() describes it for
+ * inspection.
+ *
+ * Ownership. The caller owns every device buffer, including the workspace;
+ * the library never allocates device memory. It owns only the host handle
+ * (allocated by sa_stream_create, freed by sa_stream_destroy).
+ *
+ * Streams. `stream` arguments are hipStream_t values passed as void* (NULL =
+ * the default stream). All device work is enqueued asynchronously on that
+ * stream; calls on one handle must be ordered on one stream (the cache slot a
+ * commit overwrites may still be read by an earlier attend otherwise).
+ * Handles are not thread-safe; distinct handles are independent.
+ *
+ * Errors. Every entry point returns sa_status and never throws. Argument and
+ * state errors are detected on the host before any launch and leave the state
+ * unchanged; out-parameters are written only on SA_OK. A failed launch returns
+ * SA_ERR_DEVICE; asynchronous device faults surface at the caller's next
+ * synchronisation.
+ *
+ * Planning handles. A handle created with a NULL workspace runs all validation
+ * and bookkeeping but never touches the device (data pointers are ignored and
+ * may be NULL). It is what a scheduler (or a CPU-only test) uses to predict
+ * slot assignment, positions and launch plans.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARGUMENT = 1,   /* bad config, NULL pointer, bad flag or base      */
+  SA_ERR_UNSUPPORTED = 2,        /* shape/dtype without a kernel (see sa_config)     */
+  SA_ERR_BAD_STATE = 3,          /* call not valid in the current stream state       */
+  SA_ERR_WORKSPACE_TOO_SMALL = 4,
+  SA_ERR_POSITION_RANGE = 5,     /* a chunk would use t >= max_t (refresh cures it)  */
+  SA_ERR_DEVICE = 6              /* a HIP call failed                                */
+} sa_status;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* sa_rope_refresh flags */
+#define SA_REFRESH_SHIFT_SINK 1u
+
+/*
+ * Stream configuration (64 bytes, no padding holes).
+ *  batch            B >= 1 streams advancing in lockstep (same positions, own caches)
+ *  heads            H >= 1
+ *  head_dim         D: 64 or 128 (both dtypes)
+ *  frame_h, frame_w latent grid of one frame, >= 1
+ *  frames_per_chunk F >= 1 (one temporal RoPE unit per latent frame)
+ *  sink_chunks      S >= 0 persistent sink chunks
+ *  window_chunks    W >= 0 previous chunks kept in the sliding window
+ *  rope_dim_t/h/w   even, summing to D; all 0 selects the default split
+ *  max_t            0: unbounded; else every position used must be < max_t
+ *  rope_theta       RoPE base, 0 selects 10000
+ *  softmax_scale    0 selects 1/sqrt(D)
+ *  dtype            SA_F32 or SA_BF16 (element type of q, k, v, out and the cache)
+ * Limits: F * d_t / 2 <= SA_MAX_TEMPORAL_PAIRS; Nc = F*Hf*Wf <= 2^20;
+ *         (S + W + 1) * Nc <= 2^24 keys.
+ */
+typedef struct sa_config {
+  int32_t batch, heads, head_dim, frame_h, frame_w, frames_per_chunk;
+  int32_t sink_chunks, window_chunks;
+  int32_t rope_dim_t, rope_dim_h, rope_dim_w;
+  int32_t max_t;
+  double rope_theta;
+  float softmax_scale;
+  int32_t dtype;
+} sa_config;
+
+#define SA_MAX_TEMPORAL_PAIRS 320
+
+/* Host-side stream state (D3) and the plan of the last attend (D4). */
+typedef struct sa_state {
+  int64_t n_appends;        /* chunks committed so far; chunk ids are 0..n_appends-1     */
+  int64_t ring_commits;     /* commits that went to the window (after the sink filled)   */
+  int32_t t_next;           /* temporal position of the next chunk's first frame         */
+  int32_t sink_fill;        /* sink chunks holding data, 0..S                            */
+  int32_t window_valid;     /* visible window chunks, 0..W                               */
+  int32_t staging_slot;     /* physical slot the next chunk's own K/V are staged in      */
+  int32_t n_slots;          /* physical slots per (b, h): S + W + 1                      */
+  int32_t visible_chunks;   /* chunks the next attend sees, its own included             */
+  int32_t visible_keys;     /* keys the next attend sees: visible_chunks * Nc            */
+  int32_t staged_valid;     /* 1: the last attend's staged K/V may be committed by
+                               sa_kv_append(k = v = NULL)                                */
+  int32_t last_q_tiles;     /* attend launch plan: query tiles per (b, h) ...            */
+  int32_t last_kv_splits;   /* ... key-range splits per query tile (1 = no combine pass) */
+  int32_t last_key_tiles;   /* ... key tiles per query tile, summed over splits          */
+  int32_t last_delta;       /* Delta applied by the last sa_rope_refresh                 */
+} sa_state;
+
+/* What a physical cache slot holds. */
+typedef enum sa_slot_kind { SA_SLOT_EMPTY = 0, SA_SLOT_SINK = 1, SA_SLOT_WINDOW = 2,
+                            SA_SLOT_STAGING = 3 } sa_slot_kind;
+typedef struct sa_slot_info {
+  int64_t chunk_id;   /* committed chunk id; -1 for sink chunks written by sa_sink_update */
+  int32_t t0;         /* temporal position of the slot's first frame                      */
+  int32_t kind;       /* sa_slot_kind                                                     */
+} sa_slot_info;
+
+/* Byte offsets of the workspace regions (for inspection and tests). Per (b, h):
+ *  K cache:   [n_slots * Nc][D] rows, slot s at rows [s*Nc, (s+1)*Nc)
+ *  V cache:   transposed, [D][key_stride] (keys of all slots contiguous per channel)
+ *  Q scratch: [Nc][D] rotated queries of the last attend                           */
+typedef struct sa_layout {
+  uint64_t k_offset, k_bh_stride;      /* bytes; K row stride = D * elem_bytes          */
+  uint64_t vt_offset, vt_bh_stride;    /* bytes; channel stride = key_stride * elem     */
+  uint64_t q_offset, q_bh_stride;
+  uint64_t partial_offset, partial_bytes;
+  uint64_t table_offset, table_bytes;
+  int32_t key_stride;                  /* elements per V channel row (>= n_slots*Nc)    */
+  int32_t elem_bytes;
+  int32_t max_kv_splits;
+  int32_t reserved;
+} sa_layout;
+
+/* Kernels timed by the optional profiler. */
+typedef enum sa_kernel_id {
+  SA_K_ROPE_APPLY = 0, SA_K_CHUNK_ATTENTION = 1, SA_K_ATTN_COMBINE = 2,
+  SA_K_KV_APPEND = 3, SA_K_ROPE_REFRESH = 4, SA_K_SINK_UPDATE = 5, SA_K_COUNT = 6
+} sa_kernel_id;
+
+/* Options for sa_stream_set_option. */
+typedef enum sa_option {
+  SA_OPT_KV_SPLITS = 0,   /* 0: automatic; n >= 1: force n key-range splits per query tile */
+  SA_OPT_PROFILE = 1      /* 1: record HIP events around every launch (sa_profile_read)    */
+} sa_option;
+
+typedef struct sa_stream sa_stream;
+
+/* Human-readable name of a status code (static string). */
+const char* sa_status_string(sa_status s);
+
+/* Validate a config; SA_OK if a stream can be created from it. */
+sa_status sa_config_check(const sa_config* cfg);
+
+/* Workspace bytes a stream with this config needs (0 if the config is invalid). */
+size_t sa_workspace_bytes(const sa_config* cfg);
+
+/*
+ * Create a stream handle. d_workspace: caller-owned device memory of at least
+ * sa_workspace_bytes(cfg) bytes, 256-byte aligned, or NULL for a planning
+ * handle. The RoPE spatial cos/sin tables (host fp64, rounded to fp32) are
+ * uploaded into the workspace on `stream`. The stream starts empty: t_next 0,
+ * no sink, empty window. *out receives the handle.
+ */
+sa_status sa_stream_create(const sa_config* cfg, void* d_workspace, size_t workspace_bytes,
+                           void* stream, sa_stream** out);
+
+/* Free the host handle (never the workspace). NULL is accepted. */
+sa_status sa_stream_destroy(sa_stream* s);
+
+/*
+ * Attention of the current chunk (StreamDiffusionV2 2.A.1 chunked processing;
+ * SANA-Streaming sink + sliding window). q, k, v: [B, Nc, H, D] inputs of the
+ * current chunk; out: [B, Nc, H, D] output; lse: [B, H, Nc] float32 or NULL.
+ * Rotates q and k at positions (t_next + frame, y, x), stages the rotated k
+ * and v in the staging slot, then computes
+ *   out_i = sum_j softmax_j(scale * <q_i, k_j>) v_j
+ * over the sink, the window and the chunk itself (full, non-causal inside the
+ * chunk). The stream state does not change; the call may be repeated for one
+ * chunk (several denoising steps). SA_ERR_POSITION_RANGE if max_t > 0 and
+ * t_next + F > max_t.
+ */
+sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void* v,
+                          void* out, float* lse, void* stream);
+
+/*
+ * Commit one chunk: its k, v ([B, Nc, H, D]) are rotated at positions t_next..
+ * and stored into the next sink slot while the sink is not full, else into the
+ * window, evicting the oldest window chunk; then t_next += F. With k = v =
+ * NULL the K/V staged by the last sa_chunk_attend are committed without any
+ * device work (SA_ERR_BAD_STATE if no attend staged them since the last state
+ * change).
+ */
+sa_status sa_kv_append(sa_stream* s, const void* k, const void* v, void* stream);
+
+/*
+ * Re-base temporal RoPE offsets at a chunk boundary (StreamDiffusionV2 2.A.2).
+ * new_base_t: >= 0, or -1 for S*F (right after the pinned sink). Delta =
+ * (t0 of the oldest visible window chunk, or t_next if none) - new_base_t.
+ * Every visible window key is re-rotated by -Delta on the temporal pairs, the
+ * window t0s and t_next move by -Delta. The sink stays pinned unless flags has
+ * SA_REFRESH_SHIFT_SINK (then it moves too, and attention outputs are
+ * unchanged). delta_out (nullable) receives Delta.
+ */
+sa_status sa_rope_refresh(sa_stream* s, int32_t new_base_t, uint32_t flags, void* stream,
+                          int32_t* delta_out);
+
+/*
+ * Replace the sink (StreamDiffusionV2 2.A.2: sink tokens updated from recent
+ * context; which tokens to use is the caller's policy). k, v: [B, S*Nc, H, D];
+ * sink chunk j is rotated at t in [j*F, (j+1)*F). Afterwards the sink counts as
+ * full. SA_ERR_BAD_STATE if S = 0.
+ */
+sa_status sa_sink_update(sa_stream* s, const void* k, const void* v, void* stream);
+
+/* Current state and last launch plan. */
+sa_status sa_stream_query(const sa_stream* s, sa_state* out);
+
+/* What physical slot `slot` (0 <= slot < S + W + 1) holds; slots 0..S-1 are the sink. */
+sa_status sa_stream_slot(const sa_stream* s, int32_t slot, sa_slot_info* out);
+
+/* Workspace layout of this handle. */
+sa_status sa_stream_layout(const sa_stream* s, sa_layout* out);
+
+/* Set an sa_option. SA_ERR_INVALID_ARGUMENT for an unknown option or value. */
+sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value);
+
+/*
+ * Profiler (SA_OPT_PROFILE = 1): total device milliseconds and launch count of
+ * one kernel since the last reset, from HIP events recorded around each
+ * launch on the launch stream. Synchronises on the recorded events. reset != 0
+ * clears the counters after reading.
+ */
+sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int64_t* launches,
+                          int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SA_H_ */

@@ -11,8 +11,9 @@ StreamDiffusionV2, "Sommario tecnico", section 2.A.1), attending to a persistent
 sink chunk plus a sliding window of recent chunks (SANA-Streaming, "Transformer a
 diffusione ibrido").
 
-Inputs stand in for DiT Q/K/V activations: N(0, 1) draws in float32 from a
-PCG64 generator keyed by (20261203, config id, stream b, chunk, tensor id), then
+Inputs stand in for DiT Q/K/V activations: N(0, 1) draws in float32 from
+PCG64 generators keyed by (20261203, config id, stream b, chunk, tensor id,
+256-token block), then
 rounded to bfloat16 (round to nearest even) for the bf16 workloads. The
 outlier workload scales a per-head set of round(0.05 * D) channels of Q and K
 by 8 before rounding. No public dataset stands behind these inputs.
@@ -109,13 +110,14 @@ def to_bf16_exact(x: np.ndarray) -> np.ndarray:
     bfloat16, as a bf16 activation tensor would be.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    b = x.view(np.uint32)
+    r = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
+         & np.uint32(0xFFFF0000)).view(np.float32)
     nan = np.isnan(x)
-    out = rounded.astype(np.uint32).view(np.float32).copy()
-    out[nan] = np.float32(np.nan)
-    return out
+    if np.any(nan):
+        r = r.copy()
+        r[nan] = np.float32(np.nan)
+    return r
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -127,9 +129,23 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (b >> 16).astype(np.uint16)
 
 
-def _gen(cfg_id: int, b: int, chunk: int, tensor_id: int) -> np.random.Generator:
+def _gen(cfg_id: int, b: int, chunk: int, tensor_id: int, block: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(
-        [SEED_ROOT, cfg_id, b, chunk, tensor_id])))
+        [SEED_ROOT, cfg_id, b, chunk, tensor_id, block])))
+
+
+# tokens per independently seeded block (blocks are drawn in parallel threads)
+TOKEN_BLOCK = 256
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
 
 
 def outlier_channels(w: Workload) -> np.ndarray:
@@ -150,19 +166,31 @@ def source_id(c: int, distinct: Optional[frozenset]) -> int:
 
 
 def draw(w: Workload, src_chunk: int, tensor_id: int, n_tokens: Optional[int] = None) -> np.ndarray:
-    """One seeded tensor [B, n_tokens, H, D] in float32 (bf16-exact for bf16 workloads)."""
+    """One seeded tensor [B, n_tokens, H, D] in float32 (bf16-exact for bf16 workloads).
+
+    Token blocks of TOKEN_BLOCK tokens of each stream b have their own generator
+    keyed by (20261203, config id, b, chunk, tensor id, block), so the result
+    does not depend on how the blocks are scheduled.
+    """
     n = w.tokens_per_chunk if n_tokens is None else n_tokens
     out = np.empty((w.batch, n, w.heads, w.head_dim), dtype=np.float32)
     outl = outlier_channels(w)
-    for b in range(w.batch):
-        x = _gen(w.cfg_id, b, src_chunk, tensor_id).standard_normal(
-            (n, w.heads, w.head_dim), dtype=np.float32)
-        if outl.shape[1] and tensor_id in (T_Q, T_K, T_SINK_K):
+    scale_outliers = outl.shape[1] and tensor_id in (T_Q, T_K, T_SINK_K)
+
+    def fill(b, blk):
+        t0, t1 = blk * TOKEN_BLOCK, min(n, (blk + 1) * TOKEN_BLOCK)
+        x = _gen(w.cfg_id, b, src_chunk, tensor_id, blk).standard_normal(
+            (t1 - t0, w.heads, w.head_dim), dtype=np.float32)
+        if scale_outliers:
             for h in range(w.heads):
                 x[:, h, outl[h]] *= np.float32(w.outlier_scale)
-        out[b] = x
-    if w.dtype == "bf16":
-        out = to_bf16_exact(out)
+        if w.dtype == "bf16":
+            x = to_bf16_exact(x)
+        out[b, t0:t1] = x
+
+    jobs = [(b, blk) for b in range(w.batch) for blk in range((n + TOKEN_BLOCK - 1) // TOKEN_BLOCK)]
+    for f in [_pool().submit(fill, b, blk) for b, blk in jobs]:
+        f.result()
     return out
 
 

@@ -1,0 +1,248 @@
+"""CPU tests of the C-ABI library (no GPU, no kernel launches).
+
+* libsa.so loads and exports every function include/sa.h declares;
+* planning handles (created without a workspace) run the full bookkeeping:
+  their visible sets (chunk ids, positions), refresh deltas and positions are
+  compared bit-exactly with the oracle's stream semantics on seeded random
+  operation sequences; the physical slots seen by an attend must form the
+  prefix [0, visible_chunks) that the attention kernel reads;
+* error conventions: status codes, state unchanged after an error.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import causal_windowed_attention_amd as cwa
+from causal_windowed_attention_amd import _lib as L
+from oracle import HistoryOracle, SHIFT_SINK, StreamSpec
+from oracle.stream import StreamError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "sa.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    declared = set(re.findall(r"\b(sa_[a-z_]+)\s*\(", hdr))
+    assert len(declared) >= 14
+    lib = L.load()
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(L.SIGNATURES), declared ^ set(L.SIGNATURES)
+
+
+def test_struct_sizes_match_header():
+    import ctypes
+    assert ctypes.sizeof(L.sa_config) == 64
+    assert ctypes.sizeof(L.sa_state) == 16 + 12 * 4
+    assert ctypes.sizeof(L.sa_slot_info) == 16
+
+
+def _cfg(**kw):
+    base = dict(batch=1, heads=2, head_dim=64, frame_h=2, frame_w=3, frames_per_chunk=2,
+                sink_chunks=1, window_chunks=2, dtype="bf16")
+    base.update(kw)
+    return cwa.make_config(**base)
+
+
+def _spec(cfg):
+    return StreamSpec(batch=cfg.batch, heads=cfg.heads, head_dim=cfg.head_dim,
+                      frame_h=cfg.frame_h, frame_w=cfg.frame_w,
+                      frames_per_chunk=cfg.frames_per_chunk, sink_chunks=cfg.sink_chunks,
+                      window_chunks=cfg.window_chunks, max_t=cfg.max_t)
+
+
+def _lib_visible(s: cwa.Stream):
+    st = s.query()
+    seen = []
+    for slot in range(st["n_slots"]):
+        info = s.slot(slot)
+        if slot < st["visible_chunks"]:
+            assert info["kind"] != cwa.SA_SLOT_EMPTY, (slot, info)
+            kind = {cwa.SA_SLOT_SINK: "sink", cwa.SA_SLOT_WINDOW: "window",
+                    cwa.SA_SLOT_STAGING: "self"}[info["kind"]]
+            seen.append((kind, info["chunk_id"], info["t0"]))
+        else:
+            assert info["kind"] == cwa.SA_SLOT_EMPTY, (slot, info)
+    assert [k for k, _, _ in seen].count("self") == 1
+    assert seen.index([x for x in seen if x[0] == "self"][0]) == st["staging_slot"]
+    return st, sorted(seen, key=lambda x: (x[0] != "sink", x[2], x[1]))
+
+
+def _oracle_visible(orc):
+    return sorted(orc.visible(), key=lambda x: (x[0] != "sink", x[2], x[1]))
+
+
+def _dummy(spec, n_tokens=None):
+    n = spec.tokens_per_chunk if n_tokens is None else n_tokens
+    return np.zeros((spec.batch, n, spec.heads, spec.head_dim))
+
+
+@pytest.mark.parametrize("S,W,seed", [(1, 2, 0), (1, 6, 1), (2, 3, 2), (0, 2, 3), (1, 0, 4),
+                                      (0, 0, 5), (3, 1, 6), (1, 3, 7), (4, 4, 8)])
+def test_planning_bookkeeping_matches_oracle(S, W, seed):
+    cfg = _cfg(sink_chunks=S, window_chunks=W)
+    s = cwa.Stream(cfg, planning=True)
+    spec = _spec(cfg)
+    orc = HistoryOracle(spec)
+    g = np.random.default_rng(seed)
+    z = _dummy(spec)
+    for step in range(300):
+        st, vis = _lib_visible(s)
+        assert vis == _oracle_visible(orc), (step, vis, orc.visible())
+        assert st["t_next"] == orc.t_next and st["n_appends"] == orc.n_appends
+        assert st["sink_fill"] == orc.sink_fill and st["ring_commits"] == orc.ring_commits
+        assert st["visible_keys"] == len(orc.visible()) * (cfg.frames_per_chunk * 6)
+        r = g.random()
+        if r < 0.5:
+            zero_copy = g.random() < 0.5
+            if zero_copy:
+                s.chunk_attend(None, None, None)
+                s.kv_append(None, None)
+            else:
+                cwa.sa_kv_append(s.handle, 1, 1)       # explicit k, v (ignored by a planning handle)
+            orc.append(z, z)
+        elif r < 0.7:
+            base = int(g.choice([-1, 0, 2, 5, 11]))
+            flags = SHIFT_SINK if g.random() < 0.3 else 0
+            d_lib = s.rope_refresh(base, flags)
+            d_orc = orc.refresh(None if base == -1 else base, flags)
+            assert d_lib == d_orc
+            assert s.query()["last_delta"] == d_orc
+        elif r < 0.8:
+            if S > 0:
+                cwa.sa_sink_update(s.handle, 1, 1)
+                orc.sink_update(_dummy(spec, S * spec.tokens_per_chunk),
+                                _dummy(spec, S * spec.tokens_per_chunk))
+            else:
+                with pytest.raises(cwa.SaError) as e:
+                    cwa.sa_sink_update(s.handle, 1, 1)
+                assert e.value.status == L.SA_ERR_BAD_STATE
+        else:
+            s.chunk_attend(None, None, None)
+            st = s.query()
+            assert st["staged_valid"] == 1
+            assert st["last_key_tiles"] == -(-st["visible_keys"] // 64)
+    s.close()
+
+
+def test_zero_copy_commit_rules():
+    s = cwa.Stream(_cfg(), planning=True)
+    with pytest.raises(cwa.SaError) as e:          # nothing staged yet
+        s.kv_append(None, None)
+    assert e.value.status == L.SA_ERR_BAD_STATE
+    s.chunk_attend(None, None, None)
+    assert s.rope_refresh(0, 0) == 0                # Delta = 0 keeps the staged chunk valid
+    assert s.query()["staged_valid"] == 1
+    s.kv_append(None, None)
+    assert s.query()["n_appends"] == 1
+    with pytest.raises(cwa.SaError):                # consumed
+        s.kv_append(None, None)
+    for _ in range(4):
+        s.chunk_attend(None, None, None)
+        s.kv_append(None, None)
+    s.chunk_attend(None, None, None)
+    assert s.rope_refresh(-1, 0) != 0               # moving positions invalidates the staged K
+    with pytest.raises(cwa.SaError):
+        s.kv_append(None, None)
+    s.chunk_attend(None, None, None)
+    cwa.sa_sink_update(s.handle, 1, 1)              # so does a sink update
+    with pytest.raises(cwa.SaError):
+        s.kv_append(None, None)
+
+
+def test_position_range_and_state_unchanged():
+    cfg = _cfg(max_t=7, sink_chunks=1, window_chunks=1)
+    s = cwa.Stream(cfg, planning=True)
+    for _ in range(3):                               # chunks at t = 0, 2, 4 (F = 2)
+        s.chunk_attend(None, None, None)
+        s.kv_append(None, None)
+    before = s.query()
+    with pytest.raises(cwa.SaError) as e:            # t = 6..7 would reach max_t
+        s.chunk_attend(None, None, None)
+    assert e.value.status == L.SA_ERR_POSITION_RANGE
+    with pytest.raises(cwa.SaError) as e:
+        cwa.sa_kv_append(s.handle, 1, 1)
+    assert e.value.status == L.SA_ERR_POSITION_RANGE
+    assert s.query() == before
+    assert s.rope_refresh(-1, 0) == 2                # oldest window chunk t0 = 4 -> base 2
+    s.chunk_attend(None, None, None)                 # now at t = 4..5
+
+
+def test_error_codes():
+    lib = L.load()
+    assert cwa.sa_status_string(0) == "SA_OK"
+    assert cwa.sa_status_string(5) == "SA_ERR_POSITION_RANGE"
+    bad = [
+        (dict(batch=0), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(head_dim=63), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(head_dim=96), L.SA_ERR_UNSUPPORTED),
+        (dict(sink_chunks=-1), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(rope_dims=(30, 20, 20)), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(rope_dims=(25, 20, 19)), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(frames_per_chunk=40, head_dim=128), L.SA_ERR_UNSUPPORTED),
+        (dict(dtype=7), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(rope_theta=0.5), L.SA_ERR_INVALID_ARGUMENT),
+        (dict(max_t=1), L.SA_ERR_POSITION_RANGE),
+    ]
+    for kw, code in bad:
+        cfg = _cfg(**kw)
+        assert cwa.sa_config_check(cfg) == code, kw
+        assert cwa.sa_workspace_bytes(cfg) == 0
+        with pytest.raises(cwa.SaError) as e:
+            cwa.sa_stream_create(cfg, None)
+        assert e.value.status == code
+    cfg = _cfg(rope_dims=(24, 20, 20))
+    assert cwa.sa_config_check(cfg) == 0
+    s = cwa.Stream(cfg, planning=True)
+    with pytest.raises(cwa.SaError) as e:
+        s.rope_refresh(-5, 0)
+    assert e.value.status == L.SA_ERR_INVALID_ARGUMENT
+    with pytest.raises(cwa.SaError) as e:
+        s.rope_refresh(-1, 4)
+    assert e.value.status == L.SA_ERR_INVALID_ARGUMENT
+    with pytest.raises(cwa.SaError):
+        s.set_option(cwa.SA_OPT_KV_SPLITS, 99)
+    with pytest.raises(cwa.SaError):
+        s.set_option(cwa.SA_OPT_PROFILE, 1)          # a planning handle has no device work
+    with pytest.raises(cwa.SaError):
+        s.set_option(42, 0)
+    with pytest.raises(cwa.SaError):
+        s.slot(-1)
+    with pytest.raises(cwa.SaError):
+        s.slot(s.query()["n_slots"])
+    assert lib.sa_stream_destroy(None) == 0
+    assert lib.sa_chunk_attend(None, None, None, None, None, None, None) == L.SA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_layout_and_plans():
+    import synth
+    for name in ["wan1.3b", "wan14b_b4", "hybrid1280x704", "long512p", "tiny_f32"]:
+        w = synth.WORKLOADS[name]
+        cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w,
+                              w.frames_per_chunk, w.sink_chunks, w.window_chunks, dtype=w.dtype)
+        s = cwa.Stream(cfg, planning=True)
+        lay = s.layout()
+        nc, bh, d = w.tokens_per_chunk, w.batch * w.heads, w.head_dim
+        slots = w.sink_chunks + w.window_chunks + 1
+        elem = 2 if w.dtype == "bf16" else 4
+        assert lay["k_bh_stride"] == slots * nc * d * elem
+        assert lay["key_stride"] % 64 == 0 and lay["key_stride"] >= slots * nc
+        assert lay["vt_offset"] >= lay["k_offset"] + bh * lay["k_bh_stride"]
+        assert lay["q_offset"] >= lay["vt_offset"] + bh * lay["vt_bh_stride"]
+        for off in ("k_offset", "vt_offset", "q_offset", "partial_offset", "table_offset"):
+            assert lay[off] % 256 == 0
+        assert cwa.sa_workspace_bytes(cfg) >= lay["table_offset"] + lay["table_bytes"]
+        for c in range(slots + 2):
+            s.chunk_attend(None, None, None)
+            st = s.query()
+            assert st["visible_chunks"] == min(c, slots - 1) + 1
+            bm = 128 if w.dtype == "bf16" else 64
+            bn = 64 if w.dtype == "bf16" else 32
+            assert st["last_q_tiles"] == -(-nc // bm)
+            assert st["last_key_tiles"] == -(-st["visible_keys"] // bn)
+            assert 1 <= st["last_kv_splits"] <= lay["max_kv_splits"]
+            s.kv_append(None, None)
+        assert s.query()["visible_keys"] == slots * nc

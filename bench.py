@@ -184,8 +184,9 @@ def main():
             kern[name] = ms / n
     st = s.query()
     # refresh and sink update (not in this workload's schedule): timed separately
-    for _ in range(3):
-        s.rope_refresh(-1, 0)
+    base = w.sink_chunks * w.frames_per_chunk
+    for i in range(4):
+        s.rope_refresh(base + (i % 2) * w.frames_per_chunk, 0)   # alternate bases: Delta != 0 each time
         s.sink_update(*[torch.cat([pool[0][j]] * w.sink_chunks, dim=1) for j in (1, 2)])
     for name, k_id in (("rope_refresh", cwa.SA_K_ROPE_REFRESH), ("sink_update", cwa.SA_K_SINK_UPDATE)):
         ms, n = s.profile_read(k_id, reset=True)

@@ -48,7 +48,23 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget for the oracle baseline sample")
     ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 4 times (scales the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 4 x (read 1 GiB + write 1 GiB)."""
+    import torch
+    torch.cuda.set_device(0)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
 
 
 def kernel_source_hash():
@@ -117,6 +133,9 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(a stream's caches live on one GPU; see DESIGN.md for how it would shard)",
@@ -233,7 +252,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
-            "kernel": "chunk_attention_bf16<128>",
+            "kernel": "chunk_attention_bf16_d128",
             "flops_per_launch": flops,
             "mean_ms": attn_ms,
             "kernel_source_hash": src_hash,

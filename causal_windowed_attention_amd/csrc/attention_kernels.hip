@@ -35,6 +35,8 @@
 // and log2-sum-exp L_s, O = sum_s 2^(L_s - L) O_s with L = log2 sum_s 2^L_s.
 #include "sa_internal.h"
 
+#include <type_traits>
+
 namespace sa {
 namespace {
 
@@ -59,27 +61,46 @@ __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// bf16 tile geometry. A stage holds one K tile (64 keys x D, row-major) and
+// one V^T tile (D x 64 keys) in LDS without padding; 16-byte chunks are placed
+// with an XOR swizzle (chunk c of row r sits at c ^ (r & 7)) so the MFMA
+// operand reads of 8 consecutive rows hit distinct banks. Tiles are copied
+// global -> LDS directly (global_load_lds_dwordx4: lane i of a wave writes the
+// 16 bytes at LDS base + 16 i), choosing each lane's source so that the chunk
+// lands at its swizzled place; no VGPR staging, no LDS write instructions.
 template <int D>
-struct AttnSmem {
-  __bf16 k[2][kBf16BlockN * D];
-  __bf16 vt[2][D * kBf16BlockN];
+struct Bf16Geom {
+  static constexpr int BN = kBf16BlockN;
+  static constexpr int KROW = D * 2;          // bytes per K row
+  static constexpr int VROW = BN * 2;         // bytes per V^T row
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int BUF = KBYTES + VBYTES; // one stage (K + V^T)
+  static constexpr int KC = D / 8;            // 16-byte chunks per K row
+  static constexpr int VC = BN / 8;           // 16-byte chunks per V^T row
+  static constexpr int KCOPIES = KBYTES / 1024 / 4;   // 1 KB wave copies per wave per tile
+  static constexpr int VCOPIES = VBYTES / 1024 / 4;
 };
 
+// Rescale threshold (log2 units): the running maximum used to exponentiate a
+// row is only raised when a tile's maximum exceeds it by more than this, so
+// un-normalised weights stay below 2^8 and the O rescale runs rarely.
+constexpr float kRescaleThreshold = 8.0f;
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16(AttnParams p) {
-  constexpr int BN = kBf16BlockN;
-  constexpr int KC = D / 8;                      // 16-byte chunks per K row
-  constexpr int VC = BN / 8;                     // 16-byte chunks per V^T row
-  constexpr int KLOADS = BN * KC / kThreads;     // K chunks per thread per tile
-  constexpr int VLOADS = D * VC / kThreads;      // V^T chunks per thread per tile
+__device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
+  using G = Bf16Geom<D>;
+  constexpr int BN = G::BN;
   constexpr int KSTEPS = D / 16;                 // MFMA k-steps of QK^T
   constexpr int MT = BN / 32;                    // 32-key score tiles per key tile
   constexpr int DT = D / 32;                     // 32-channel output tiles
   constexpr int PSTEPS = BN / 16;                // MFMA k-steps of PV
-  __shared__ AttnSmem<D> sm;
+  static_assert(2 * G::BUF <= 65536, "LDS offsets must fit the 16-bit immediate");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   const int n_work = p.B * p.H * p.q_tiles * p.kv_splits;
@@ -90,10 +111,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16(AttnParams p
   const int bh = rest / p.kv_splits;
   const int t_begin = static_cast<int>((static_cast<int64_t>(split) * p.key_tiles) / p.kv_splits);
   const int t_end = static_cast<int>((static_cast<int64_t>(split + 1) * p.key_tiles) / p.kv_splits);
-
-  const __bf16* kbase = static_cast<const __bf16*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride;
-  const __bf16* vbase = static_cast<const __bf16*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride;
   const int n_keys = p.n_keys;
+  const int t_tail = (n_keys % BN) ? p.key_tiles - 1 : p.key_tiles;   // index of a ragged last tile
+
+  const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
+  const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
 
   // ---- Q rows of this wave as MFMA B operands --------------------------------
   const int q = qt * kBf16BlockM + wave * 32 + l32;
@@ -103,129 +125,127 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16(AttnParams p
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
 
-  // ---- tile staging: global -> registers -> LDS ------------------------------
-  uint4 kreg[KLOADS], vreg[VLOADS];
-  auto load_tile = [&](int t) {
+  // ---- tile copies: lane sources for the swizzled LDS image ------------------
+  // copy i of wave w fills LDS chunks P = (i * 4 + w) * 64 + lane of the region
+  int k_row[G::KCOPIES], k_src[G::KCOPIES], v_src[G::VCOPIES];
+#pragma unroll
+  for (int i = 0; i < G::KCOPIES; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane;
+    const int r = P / G::KC, c = (P % G::KC) ^ (r & 7);
+    k_row[i] = swap_bits23(r);                   // key (tile-local) held by LDS row r
+    k_src[i] = c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < G::VCOPIES; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane;
+    const int d = P / G::VC, c = (P % G::VC) ^ (d & 7);
+    v_src[i] = d * p.key_stride * 2 + c * 16;
+  }
+  auto issue_tile = [&](int t, int buf) {
     const int key0 = t * BN;
+    char* dst = smem + buf * G::BUF;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = id / KC, c = id % KC;
-      const int key = key0 + r;
-      kreg[i] = key < n_keys ? *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(key) * D + 8 * c)
-                             : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < G::KCOPIES; ++i) {
+      const int key = min(key0 + k_row[i], n_keys - 1);   // rows past the range: any finite row
+      __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key) * G::KROW + k_src[i],
+                                       dst + (i * 4 + wave) * 1024, 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int id = tid + i * kThreads;
-      const int d = id / VC, c = id % VC;
-      const int k8 = key0 + 8 * c;
-      uint4 v = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(d) * p.key_stride + k8);
-      if (k8 + 8 > n_keys) {                     // ragged tail: zero keys >= n_keys
-        unsigned w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k8 + e >= n_keys) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        v = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      vreg[i] = v;
-    }
+    for (int i = 0; i < G::VCOPIES; ++i)
+      __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src[i],
+                                       dst + G::KBYTES + (i * 4 + wave) * 1024, 16, 0, 0);
   };
-  auto store_tile = [&](int buf) {
+
+  // ---- MFMA operand read addresses (per lane; k-steps differ by XOR) ---------
+  const int x = l32 & 7;
+  int ka[4], va[4];
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = swap_bits23(id / KC), c = id % KC;
-      *reinterpret_cast<uint4*>(&sm.k[buf][r * D + ((c ^ (r & 7)) * 8)]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int id = tid + i * kThreads;
-      const int d = id / VC, c = id % VC;
-      *reinterpret_cast<uint4*>(&sm.vt[buf][d * BN + ((c ^ (d & 7)) * 8)]) = vreg[i];
-    }
-  };
+  for (int j = 0; j < 4; ++j) {
+    ka[j] = l32 * G::KROW + (((2 * j + g) ^ x) * 16);
+    va[j] = G::KBYTES + l32 * G::VROW + (((2 * j + g) ^ x) * 16);
+  }
 
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x16{};
-  float m = -__builtin_inff();   // running max of scaled scores (log2 units)
-  float l = 0.f;                 // per-lane partial row sum
+  float m = -__builtin_inff();   // exponent reference of this row (log2 units)
+  float l = 0.f;                 // per-lane partial row sum relative to m
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_tile(t + 1);
-    const __bf16* Ks = sm.k[buf];
-    const __bf16* Vs = sm.vt[buf];
-    const int key0 = t * BN;
-
+  auto compute_tile = [&](int t, int buf, auto tail) {
+    const char* stage = smem + buf * G::BUF;
     // S^T = K Q^T  (32 keys x 32 queries per accumulator)
     f32x16 sacc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      sacc[mt] = f32x16{};
-      const int r = 32 * mt + l32;
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int c = 2 * s + g;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + r * D + ((c ^ (r & 7)) * 8));
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + ka[s & 3] + (s >> 2) * 128 +
+                                                          mt * 32 * G::KROW);
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
       }
-    }
-    // accumulator j of tile mt holds key key0 + 32*mt + 16*(j/8) + 8*g + j%8
-    if (key0 + BN > n_keys) {
+    // accumulator j of tile mt holds key t*BN + 32*mt + 16*(j/8) + 8*g + j%8
+    if constexpr (decltype(tail)::value) {
+      const int key0 = t * BN;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys) sacc[mt][j] = -__builtin_inff();
     }
-
-    // online softmax (base 2)
-    float mx = -__builtin_inff();
+    float mx = sacc[0][0];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mt][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * p.scale_log2);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {      // wave-uniform: raise the reference max
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+    }
     float rs = 0.f;
     bf16x8 pb[PSTEPS];
 #pragma unroll
     for (int s = 0; s < PSTEPS; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m_new));
+        const float pv = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m));
         rs += pv;
         pb[s][e] = static_cast<__bf16>(pv);
       }
     }
-    l = fmaf(l, alpha, rs);
-#pragma unroll
-    for (int i = 0; i < DT; ++i) o[i] *= alpha;
-
+    l += rs;
     // O^T += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + l32;
+    for (int s = 0; s < PSTEPS; ++s)
 #pragma unroll
-      for (int s = 0; s < PSTEPS; ++s) {
-        const int c = 2 * s + g;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + d * BN + ((c ^ (d & 7)) * 8));
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + va[s] + dt * 32 * G::VROW);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
       }
-    }
+  };
 
-    if (t + 1 < t_end) store_tile(buf ^ 1);
+  // one barrier per tile: it publishes tile t (all waves' copies landed) and
+  // retires tile t-1 (all waves done reading the buffer tile t+1 goes to)
+  const int t_stop = min(t_end, t_tail);         // full tiles [t_begin, t_stop)
+  if (t_begin < t_end) issue_tile(t_begin, 0);
+  int t = t_begin;
+  for (; t < t_stop; ++t) {
+    const int buf = (t - t_begin) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (t + 1 < t_end) issue_tile(t + 1, buf ^ 1);
+    compute_tile(t, buf, std::false_type{});
+  }
+  if (t < t_end) {                               // the ragged last tile
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    compute_tile(t, (t - t_begin) & 1, std::true_type{});
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -259,6 +279,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16(AttnParams p
                         o[dt][4 * jj + 3] * inv);
     if (g == 0) p.part_lse[row] = lse2;
   }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d128(AttnParams p) {
+  chunk_attention_bf16_body<128>(p);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d64(AttnParams p) {
+  chunk_attention_bf16_body<64>(p);
 }
 
 // fp32: one query row per lane, 64 rows per block, 32-key tiles through LDS.
@@ -373,8 +401,8 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
   const int64_t n_work = static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
   if (n_work <= 0) return hipSuccess;
   if (dtype == 1) {
-    if (p.D == 128) hipLaunchKernelGGL(chunk_attention_bf16<128>, dim3(n_work), dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL(chunk_attention_bf16<64>, dim3(n_work), dim3(kThreads), 0, st, p);
+    if (p.D == 128) hipLaunchKernelGGL(chunk_attention_bf16_d128, dim3(n_work), dim3(kThreads), 0, st, p);
+    else hipLaunchKernelGGL(chunk_attention_bf16_d64, dim3(n_work), dim3(kThreads), 0, st, p);
   } else {
     if (p.D == 128) hipLaunchKernelGGL(chunk_attention_f32<128>, dim3(n_work), dim3(64), 0, st, p);
     else hipLaunchKernelGGL(chunk_attention_f32<64>, dim3(n_work), dim3(64), 0, st, p);

@@ -320,15 +320,23 @@ sa_status sa_stream_create(const sa_config* cfg, void* d_workspace, size_t works
         const double a = x * freq(d, d.dw, j);
         tab[i++] = make_float2(static_cast<float>(std::cos(a)), static_cast<float>(std::sin(a)));
       }
-    if (!tab.empty()) {
-      // synchronous copy: the host table dies with this call
-      hipStream_t hs = static_cast<hipStream_t>(stream);
-      if (hipMemcpyAsync(s->ws + d.tab_off, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice,
-                         hs) != hipSuccess ||
-          hipStreamSynchronize(hs) != hipSuccess) {
-        delete s;
-        return SA_ERR_DEVICE;
-      }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    // The attention kernel's ragged last key tile reads a few V^T entries past
+    // the visible keys (with weight 0); zeroing the V^T cache once keeps them finite.
+    if (hipMemsetAsync(s->ws + d.vt_off, 0, d.vt_bytes, hs) != hipSuccess) {
+      delete s;
+      return SA_ERR_DEVICE;
+    }
+    if (!tab.empty() &&
+        hipMemcpyAsync(s->ws + d.tab_off, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice,
+                       hs) != hipSuccess) {
+      delete s;
+      return SA_ERR_DEVICE;
+    }
+    // synchronous: the host table dies with this call
+    if (hipStreamSynchronize(hs) != hipSuccess) {
+      delete s;
+      return SA_ERR_DEVICE;
     }
   }
   *out = s;

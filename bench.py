@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget for the oracle baseline sample")
     ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--variant", type=int, default=0,
+                    help="bf16 attention kernel variant (0 automatic, 1 = 32 rows/wave, 2 = 64 rows/wave)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 4 times (scales the HBM byte counters)")
     return ap.parse_args()
@@ -155,6 +157,7 @@ def main():
     cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
                           w.sink_chunks, w.window_chunks, dtype="bf16")
     s = cwa.Stream(cfg, device=dev)
+    s.set_option(cwa.SA_OPT_ATTN_VARIANT, args.variant)
     nc = w.tokens_per_chunk
     steady = w.sink_chunks + w.window_chunks
     pool = []
@@ -244,6 +247,7 @@ def main():
             "visible_keys": nk, "step": "one steady-state chunk: attend (rope_apply + chunk_attention"
             + (" + attn_combine" if st["last_kv_splits"] > 1 else "") + ") + append (kv_ring_append)",
             "kv_splits": st["last_kv_splits"], "q_tiles": st["last_q_tiles"],
+            "attn_variant": args.variant,
         },
         "roofline": {
             "bound": "mfma",

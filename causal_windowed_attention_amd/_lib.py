@@ -27,7 +27,7 @@ SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_WINDOW, SA_SLOT_STAGING = 0, 1, 2, 3
 SA_K_ROPE_APPLY, SA_K_CHUNK_ATTENTION, SA_K_ATTN_COMBINE = 0, 1, 2
 SA_K_KV_APPEND, SA_K_ROPE_REFRESH, SA_K_SINK_UPDATE, SA_K_COUNT = 3, 4, 5, 6
 # sa_option
-SA_OPT_KV_SPLITS, SA_OPT_PROFILE = 0, 1
+SA_OPT_KV_SPLITS, SA_OPT_PROFILE, SA_OPT_ATTN_VARIANT = 0, 1, 2
 
 
 class sa_config(ctypes.Structure):

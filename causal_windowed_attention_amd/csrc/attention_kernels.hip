@@ -87,10 +87,14 @@ struct Bf16Geom {
 // un-normalised weights stay below 2^8 and the O rescale runs rarely.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D>
+// QB = 32-row query blocks per wave: 1 -> 128 rows per workgroup (2
+// workgroups per CU), 2 -> 256 rows per workgroup (each K/V operand read from
+// LDS feeds two MFMAs, halving LDS traffic per FLOP; one workgroup per CU).
+template <int D, int QB>
 __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
   using G = Bf16Geom<D>;
   constexpr int BN = G::BN;
+  constexpr int BM = 4 * 32 * QB;                // query rows per workgroup
   constexpr int KSTEPS = D / 16;                 // MFMA k-steps of QK^T
   constexpr int MT = BN / 32;                    // 32-key score tiles per key tile
   constexpr int DT = D / 32;                     // 32-channel output tiles
@@ -118,12 +122,15 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
   const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
 
   // ---- Q rows of this wave as MFMA B operands --------------------------------
-  const int q = qt * kBf16BlockM + wave * 32 + l32;
-  const int qrow = min(q, p.Nc - 1);
-  const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
-  bf16x8 bq[KSTEPS];
+  const int q0 = qt * BM + wave * 32 * QB + l32;  // query of block qb: q0 + 32 * qb
+  bf16x8 bq[QB][KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = min(q0 + 32 * qb, p.Nc - 1);
+    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[qb][s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
+  }
 
   // ---- tile copies: lane sources for the swizzled LDS image ------------------
   // copy i of wave w fills LDS chunks P = (i * 4 + w) * 64 + lane of the region
@@ -165,25 +172,33 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
     va[j] = G::KBYTES + l32 * G::VROW + (((2 * j + g) ^ x) * 16);
   }
 
-  f32x16 o[DT];
+  f32x16 o[QB][DT];
+  float m[QB], l[QB];            // exponent reference (log2 units), per-lane partial row sum
 #pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
-  float m = -__builtin_inff();   // exponent reference of this row (log2 units)
-  float l = 0.f;                 // per-lane partial row sum relative to m
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[qb][i] = f32x16{};
+    m[qb] = -__builtin_inff();
+    l[qb] = 0.f;
+  }
 
   auto compute_tile = [&](int t, int buf, auto tail) {
     const char* stage = smem + buf * G::BUF;
     // S^T = K Q^T  (32 keys x 32 queries per accumulator)
-    f32x16 sacc[MT];
+    f32x16 sacc[QB][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) sacc[qb][mt] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + ka[s & 3] + (s >> 2) * 128 +
                                                           mt * 32 * G::KROW);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[qb][s], sacc[qb][mt], 0, 0, 0);
       }
     // accumulator j of tile mt holds key t*BN + 32*mt + 16*(j/8) + 8*g + j%8
     if constexpr (decltype(tail)::value) {
@@ -192,41 +207,48 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys) sacc[mt][j] = -__builtin_inff();
+          if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[qb][mt][j] = -__builtin_inff();
     }
-    float mx = sacc[0][0];
+    bf16x8 pb[QB][PSTEPS];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = sacc[qb][0][0];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mt][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
-    if (__any(mx > m + kRescaleThreshold)) {      // wave-uniform: raise the reference max
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      l *= alpha;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < DT; ++i) o[i] *= alpha;
-    }
-    float rs = 0.f;
-    bf16x8 pb[PSTEPS];
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[qb][mt][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+      if (__any(mx > m[qb] + kRescaleThreshold)) {   // wave-uniform: raise the reference max
+        const float m_new = fmaxf(m[qb], mx);
+        const float alpha = fast_exp2(m[qb] - m_new);
+        m[qb] = m_new;
+        l[qb] *= alpha;
 #pragma unroll
-    for (int s = 0; s < PSTEPS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m));
-        rs += pv;
-        pb[s][e] = static_cast<__bf16>(pv);
+        for (int i = 0; i < DT; ++i) o[qb][i] *= alpha;
       }
+      float rs = 0.f;
+#pragma unroll
+      for (int s = 0; s < PSTEPS; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = fast_exp2(fmaf(sacc[qb][s >> 1][8 * (s & 1) + e], p.scale_log2, -m[qb]));
+          rs += pv;
+          pb[qb][s][e] = static_cast<__bf16>(pv);
+        }
+      }
+      l[qb] += rs;
     }
-    l += rs;
     // O^T += V^T P^T
 #pragma unroll
     for (int s = 0; s < PSTEPS; ++s)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + va[s] + dt * 32 * G::VROW);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][s], o[qb][dt], 0, 0, 0);
       }
   };
 
@@ -249,44 +271,56 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l_tot = l + __shfl_xor(l, 32);
-  if (q >= p.Nc) return;
-  const float inv = 1.f / l_tot;
-  const float lse2 = m + __log2f(l_tot);
   const int b = bh / p.H, h = bh - b * p.H;
-  if (p.kv_splits == 1) {
-    __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l[qb] + __shfl_xor(l[qb], 32);
+    const int q = q0 + 32 * qb;
+    if (q >= p.Nc) continue;
+    const float inv = 1.f / l_tot;
+    const float lse2 = m[qb] + __log2f(l_tot);
+    if (p.kv_splits == 1) {
+      __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 v;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[dt][4 * jj + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
-      }
-    if (p.lse != nullptr && g == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
-  } else {
-    const size_t row = (static_cast<size_t>(split) * p.B * p.H + bh) * p.Nc + q;
-    float* dst = p.part_o + row * D;
+        for (int jj = 0; jj < 4; ++jj) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 v;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[qb][dt][4 * jj + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
+        }
+      if (p.lse != nullptr && g == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
+    } else {
+      const size_t row = (static_cast<size_t>(split) * p.B * p.H + bh) * p.Nc + q;
+      float* dst = p.part_o + row * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
-            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
-                        o[dt][4 * jj + 3] * inv);
-    if (g == 0) p.part_lse[row] = lse2;
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
+              make_float4(o[qb][dt][4 * jj] * inv, o[qb][dt][4 * jj + 1] * inv,
+                          o[qb][dt][4 * jj + 2] * inv, o[qb][dt][4 * jj + 3] * inv);
+      if (g == 0) p.part_lse[row] = lse2;
+    }
   }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d128(AttnParams p) {
-  chunk_attention_bf16_body<128>(p);
+  chunk_attention_bf16_body<128, 1>(p);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d64(AttnParams p) {
-  chunk_attention_bf16_body<64>(p);
+  chunk_attention_bf16_body<64, 1>(p);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void chunk_attention_bf16_d128_q64(AttnParams p) {
+  chunk_attention_bf16_body<128, 2>(p);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void chunk_attention_bf16_d64_q64(AttnParams p) {
+  chunk_attention_bf16_body<64, 2>(p);
 }
 
 // fp32: one query row per lane, 64 rows per block, 32-key tiles through LDS.
@@ -401,8 +435,9 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
   const int64_t n_work = static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
   if (n_work <= 0) return hipSuccess;
   if (dtype == 1) {
-    if (p.D == 128) hipLaunchKernelGGL(chunk_attention_bf16_d128, dim3(n_work), dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL(chunk_attention_bf16_d64, dim3(n_work), dim3(kThreads), 0, st, p);
+    auto k = p.q_rows_per_block == 256 ? (p.D == 128 ? chunk_attention_bf16_d128_q64 : chunk_attention_bf16_d64_q64)
+                                       : (p.D == 128 ? chunk_attention_bf16_d128 : chunk_attention_bf16_d64);
+    hipLaunchKernelGGL(k, dim3(n_work), dim3(kThreads), 0, st, p);
   } else {
     if (p.D == 128) hipLaunchKernelGGL(chunk_attention_f32<128>, dim3(n_work), dim3(64), 0, st, p);
     else hipLaunchKernelGGL(chunk_attention_f32<64>, dim3(n_work), dim3(64), 0, st, p);

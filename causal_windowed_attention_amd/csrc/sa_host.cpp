@@ -139,6 +139,7 @@ struct sa_stream {
   // last plan (D4)
   int32_t last_q_tiles = 0, last_kv_splits = 0, last_key_tiles = 0, last_delta = 0;
   int32_t kv_splits_opt = 0;
+  int32_t variant_opt = 0;
   bool profile = false;
   Prof prof[SA_K_COUNT];
 
@@ -223,14 +224,20 @@ sa_status timed(sa_stream* s, int kid, hipStream_t st, F&& launch) {
   return SA_OK;
 }
 
-int choose_splits(const sa_stream* s, int key_tiles) {
+// Query rows per workgroup of the attention kernel used for this stream.
+int attn_block_m(const sa_stream* s) {
+  if (s->d.dtype != SA_BF16) return sa::kF32BlockM;
+  return s->variant_opt == 2 ? sa::kBf16BlockMWide : sa::kBf16BlockM;
+}
+
+int choose_splits(const sa_stream* s, int key_tiles, int q_tiles) {
   const Derived& d = s->d;
   int splits = s->kv_splits_opt;
   if (splits <= 0) {
-    // Fill the chip: 256 CUs x 2 resident workgroups. Split the key range only
+    // Fill the chip: 256 CUs x resident workgroups. Split the key range only
     // when the (b, h, q-tile) grid leaves more than a quarter of the slots idle.
-    const int64_t blocks = static_cast<int64_t>(d.B) * d.H * d.q_tiles;
-    const int64_t slots = 512;
+    const int64_t blocks = static_cast<int64_t>(d.B) * d.H * q_tiles;
+    const int64_t slots = attn_block_m(s) == sa::kBf16BlockMWide ? 256 : 512;
     splits = 1;
     if (blocks * 4 < slots * 3) {
       splits = static_cast<int>((slots + blocks - 1) / blocks);
@@ -377,7 +384,9 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
   const int32_t n_keys = s->visible_chunks() * d.Nc;
   const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
   const int key_tiles = (n_keys + bn - 1) / bn;
-  const int splits = choose_splits(s, key_tiles);
+  const int bm = attn_block_m(s);
+  const int q_tiles = (d.Nc + bm - 1) / bm;
+  const int splits = choose_splits(s, key_tiles, q_tiles);
 
   if (!s->planning()) {
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -404,7 +413,8 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
     ap.key_stride = d.key_stride;
     ap.n_keys = n_keys;
     ap.Nc = d.Nc; ap.B = d.B; ap.H = d.H; ap.D = d.D;
-    ap.q_tiles = d.q_tiles;
+    ap.q_rows_per_block = bm;
+    ap.q_tiles = q_tiles;
     ap.kv_splits = splits;
     ap.key_tiles = key_tiles;
     ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
@@ -424,7 +434,7 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
   s->staged_valid = true;
   s->staged_t = s->t_next;
   s->staged_slot = slot;
-  s->last_q_tiles = d.q_tiles;
+  s->last_q_tiles = q_tiles;
   s->last_kv_splits = splits;
   s->last_key_tiles = key_tiles;
   return SA_OK;
@@ -606,6 +616,10 @@ sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value) {
     case SA_OPT_KV_SPLITS:
       if (value < 0 || value > s->d.max_splits) return SA_ERR_INVALID_ARGUMENT;
       s->kv_splits_opt = static_cast<int32_t>(value);
+      return SA_OK;
+    case SA_OPT_ATTN_VARIANT:
+      if (value < 0 || value > 2) return SA_ERR_INVALID_ARGUMENT;
+      s->variant_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_PROFILE:
       if (value != 0 && value != 1) return SA_ERR_INVALID_ARGUMENT;

@@ -157,8 +157,10 @@ typedef enum sa_kernel_id {
 
 /* Options for sa_stream_set_option. */
 typedef enum sa_option {
-  SA_OPT_KV_SPLITS = 0,   /* 0: automatic; n >= 1: force n key-range splits per query tile */
-  SA_OPT_PROFILE = 1      /* 1: record HIP events around every launch (sa_profile_read)    */
+  SA_OPT_KV_SPLITS = 0,     /* 0: automatic; n >= 1: force n key-range splits per query tile */
+  SA_OPT_PROFILE = 1,       /* 1: record HIP events around every launch (sa_profile_read)    */
+  SA_OPT_ATTN_VARIANT = 2   /* bf16 attention kernel: 0 automatic, 1 = 32 query rows per
+                               wave (128 per workgroup), 2 = 64 rows per wave (256)          */
 } sa_option;
 
 typedef struct sa_stream sa_stream;

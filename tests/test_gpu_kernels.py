@@ -56,10 +56,12 @@ def _check_storage(s, ring: RingOracle, w, max_ulp):
             assert np.array_equal(host(v), ring.stored_v(cid))
 
 
-def _run_sequence(w, ops, check_storage=True):
+def _run_sequence(w, ops, check_storage=True, variant=0):
     """Drive the GPU stream and both oracles through ops; check every attend."""
-    say("sequence", w.name, w.dtype, "B", w.batch, "H", w.heads, "D", w.head_dim, "Nc", w.tokens_per_chunk)
+    say("sequence", w.name, w.dtype, "B", w.batch, "H", w.heads, "D", w.head_dim, "Nc", w.tokens_per_chunk,
+        "variant", variant)
     s = cwa.Stream(config_for(w))
+    s.set_option(cwa.SA_OPT_ATTN_VARIANT, variant)
     spec = spec_for(w)
     hist = HistoryOracle(spec)
     ring = RingOracle(spec, storage=w.dtype)
@@ -130,14 +132,16 @@ OPS = ["attend", "append", "attend", "append0", "attend", "append", "attend", "a
        "attend", "append", "attend"]
 
 
-def test_stream_bf16_d128_storage_and_outputs():
-    _run_sequence(SMALL, OPS)
+@pytest.mark.parametrize("variant", [1, 2])
+def test_stream_bf16_d128_storage_and_outputs(variant):
+    _run_sequence(SMALL, OPS, variant=variant)
 
 
-def test_stream_bf16_d64():
+@pytest.mark.parametrize("variant", [1, 2])
+def test_stream_bf16_d64(variant):
     w = synth.small_variant(SMALL, name="small_d64", head_dim=64, frame_h=4, frame_w=8,
                             frames_per_chunk=2, window_chunks=3)
-    _run_sequence(w, OPS)
+    _run_sequence(w, OPS, variant=variant)
 
 
 def test_stream_f32_tiny_config():
@@ -157,12 +161,12 @@ def test_stream_f32_d128_with_sink_update():
     _run_sequence(w, OPS)
 
 
-@pytest.mark.parametrize("S,W,B", [(0, 2, 1), (1, 0, 2), (0, 0, 1), (2, 1, 2)])
-def test_edge_shapes(S, W, B):
+@pytest.mark.parametrize("S,W,B,variant", [(0, 2, 1, 1), (1, 0, 2, 2), (0, 0, 1, 1), (2, 1, 2, 2)])
+def test_edge_shapes(S, W, B, variant):
     w = synth.small_variant(SMALL, name=f"edge_S{S}W{W}", sink_chunks=S, window_chunks=W, batch=B,
                             heads=2)
     _run_sequence(w, ["attend", "append", "attend", "append0", "attend", "append", "refresh",
-                      "attend", "append", "attend"])
+                      "attend", "append", "attend"], variant=variant)
 
 
 def test_one_token_chunks():
@@ -182,12 +186,13 @@ def _steady_stream(w, n_commit):
     return s, hist
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_forced_kv_splits_and_repeat(dtype):
+@pytest.mark.parametrize("dtype,variant", [("bf16", 1), ("bf16", 2), ("f32", 0)])
+def test_forced_kv_splits_and_repeat(dtype, variant):
     w = synth.small_variant(SMALL, name="splits", dtype=dtype, frame_h=10, frame_w=10,
                             frames_per_chunk=3, batch=1, heads=2, window_chunks=3)
-    say("splits", dtype, "Nc", w.tokens_per_chunk)
+    say("splits", dtype, "Nc", w.tokens_per_chunk, "variant", variant)
     s, hist = _steady_stream(w, 5)
+    s.set_option(cwa.SA_OPT_ATTN_VARIANT, variant)
     q, k, v = synth.chunk_qkv(w, 5)
     want, want_lse = hist.attend(q, k, v)
     qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)

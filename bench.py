@@ -256,7 +256,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
-            "kernel": "chunk_attention_bf16_d128",
+            "kernel": {1: "chunk_attention_bf16_d128", 2: "chunk_attention_bf16_d128_q64",
+                       3: "chunk_attention_bf16_d128_pp"}[args.variant or 3],
             "flops_per_launch": flops,
             "mean_ms": attn_ms,
             "kernel_source_hash": src_hash,

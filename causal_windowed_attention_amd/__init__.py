@@ -239,13 +239,12 @@ class Stream:
 
     # -- read-only views of the cache inside the workspace (inspection, tests) ---
     def k_cache_view(self):
-        """[B*H, n_slots*Nc, D] rotated keys."""
+        """[B*H, key_stride, D] rotated keys (slot s at rows [s*Nc, (s+1)*Nc))."""
         lay = self.layout()
-        st = self.query()
         bh = self.cfg.batch * self.cfg.heads
-        n = bh * st["n_slots"] * self.Nc * self.cfg.head_dim
+        n = bh * lay["key_stride"] * self.cfg.head_dim
         raw = self.workspace[lay["k_offset"]:lay["k_offset"] + n * lay["elem_bytes"]]
-        return raw.view(self._torch_dtype()).view(bh, st["n_slots"] * self.Nc, self.cfg.head_dim)
+        return raw.view(self._torch_dtype()).view(bh, lay["key_stride"], self.cfg.head_dim)
 
     def vt_cache_view(self):
         """[B*H, D, key_stride] transposed values."""

@@ -11,9 +11,9 @@
 // (b, h) and one key-range split:
 //  * each wave owns 32 query rows; its rotated Q rows sit in VGPRs as the B
 //    operand of v_mfma_f32_32x32x16_bf16;
-//  * K tiles (64 keys x D) and V^T tiles (D x 64 keys) are staged in LDS,
-//    double-buffered, with an XOR swizzle of the 16-byte chunks so the MFMA
-//    operand reads of 8 consecutive rows hit distinct banks;
+//  * K tiles (64 keys x D) and V^T tiles (D x 64 keys) are copied into LDS
+//    through a multi-stage pipeline, with an XOR swizzle of the 16-byte chunks
+//    so the MFMA operand reads are free of bank conflicts;
 //  * scores are computed transposed, S^T = K Q^T: lane l holds query l % 32, so
 //    the online-softmax rescale of the O^T accumulators is one scalar per lane
 //    and the fp32 scores convert in registers into the B operand of
@@ -56,18 +56,33 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return xcd * base + min(xcd, extra) + idx;
 }
 
+// s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt/lgkmcnt free.
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
+}
+
+// Swizzled position of 16-byte chunk c in LDS row r of a tile whose rows hold
+// `chunks` chunks (8 or 16); an involution in c for fixed r.
+__device__ __forceinline__ int swz(int c, int r, int chunks) {
+  return chunks >= 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
 // Swap bits 2 and 3 of a tile row index (an involution).
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
 // bf16 tile geometry. A stage holds one K tile (64 keys x D, row-major) and
-// one V^T tile (D x 64 keys) in LDS without padding; 16-byte chunks are placed
-// with an XOR swizzle (chunk c of row r sits at c ^ (r & 7)) so the MFMA
-// operand reads of 8 consecutive rows hit distinct banks. Tiles are copied
-// global -> LDS directly (global_load_lds_dwordx4: lane i of a wave writes the
-// 16 bytes at LDS base + 16 i), choosing each lane's source so that the chunk
-// lands at its swizzled place; no VGPR staging, no LDS write instructions.
+// one V^T tile (D x 64 keys) in LDS without padding. gfx950 serves a
+// ds_read_b128 16 lanes (256 bytes, all 64 banks) at a time, and the MFMA
+// operand reads of those 16 lanes hit 16 consecutive rows at the same logical
+// 16-byte chunk; the chunks are therefore XOR-swizzled so the 16 rows land on
+// 16 distinct bank groups: chunk c of a 256-byte row r sits at c ^ (r & 15),
+// chunk c of a 128-byte row r (two rows per 256-byte bank window) at
+// c ^ ((r >> 1) & 7). Tiles are copied global -> LDS directly
+// (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at LDS base +
+// 16 i), choosing each lane's source so that the chunk lands at its swizzled
+// place; no VGPR staging, no LDS write instructions.
 template <int D>
 struct Bf16Geom {
   static constexpr int BN = kBf16BlockN;
@@ -87,20 +102,26 @@ struct Bf16Geom {
 // un-normalised weights stay below 2^8 and the O rescale runs rarely.
 constexpr float kRescaleThreshold = 8.0f;
 
-// QB = 32-row query blocks per wave: 1 -> 128 rows per workgroup (2
-// workgroups per CU), 2 -> 256 rows per workgroup (each K/V operand read from
-// LDS feeds two MFMAs, halving LDS traffic per FLOP; one workgroup per CU).
-template <int D, int QB>
+// Kernel shape parameters:
+//  NW     waves per workgroup (4 or 8); each wave owns 32 * QB query rows
+//  QB     32-row query blocks per wave (2: each K/V operand read feeds two MFMAs)
+//  STAGES LDS stages of the tile copy pipeline: copies for tile t + STAGES - 1
+//         are issued while tile t is computed, so a copy has STAGES - 1 tiles of
+//         compute to land (misses to the last-level cache take microseconds)
+template <int D, int NW, int QB, int STAGES>
 __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
   using G = Bf16Geom<D>;
   constexpr int BN = G::BN;
-  constexpr int BM = 4 * 32 * QB;                // query rows per workgroup
+  constexpr int BM = NW * 32 * QB;               // query rows per workgroup
   constexpr int KSTEPS = D / 16;                 // MFMA k-steps of QK^T
   constexpr int MT = BN / 32;                    // 32-key score tiles per key tile
   constexpr int DT = D / 32;                     // 32-channel output tiles
   constexpr int PSTEPS = BN / 16;                // MFMA k-steps of PV
-  static_assert(2 * G::BUF <= 65536, "LDS offsets must fit the 16-bit immediate");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::BUF];
+  constexpr int KCOPIES = G::KBYTES / 1024 / NW; // 1 KB copies per wave per tile
+  constexpr int VCOPIES = G::VBYTES / 1024 / NW;
+  static_assert(KCOPIES * NW * 1024 == G::KBYTES && VCOPIES * NW * 1024 == G::VBYTES, "copy split");
+  static_assert(STAGES >= 2 && (STAGES - 2) * (KCOPIES + VCOPIES) <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * G::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,44 +154,43 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
   }
 
   // ---- tile copies: lane sources for the swizzled LDS image ------------------
-  // copy i of wave w fills LDS chunks P = (i * 4 + w) * 64 + lane of the region
-  int k_row[G::KCOPIES], k_src[G::KCOPIES], v_src[G::VCOPIES];
+  // copy i of wave w fills LDS chunks P = (i * NW + w) * 64 + lane of the region
+  int k_row[KCOPIES], k_src[KCOPIES], v_src[VCOPIES];
 #pragma unroll
-  for (int i = 0; i < G::KCOPIES; ++i) {
-    const int P = (i * 4 + wave) * 64 + lane;
-    const int r = P / G::KC, c = (P % G::KC) ^ (r & 7);
+  for (int i = 0; i < KCOPIES; ++i) {
+    const int P = (i * NW + wave) * 64 + lane;
+    const int r = P / G::KC, c = swz(P % G::KC, r, G::KC);
     k_row[i] = swap_bits23(r);                   // key (tile-local) held by LDS row r
     k_src[i] = c * 16;
   }
 #pragma unroll
-  for (int i = 0; i < G::VCOPIES; ++i) {
-    const int P = (i * 4 + wave) * 64 + lane;
-    const int d = P / G::VC, c = (P % G::VC) ^ (d & 7);
+  for (int i = 0; i < VCOPIES; ++i) {
+    const int P = (i * NW + wave) * 64 + lane;
+    const int d = P / G::VC, c = swz(P % G::VC, d, G::VC);
     v_src[i] = d * p.key_stride * 2 + c * 16;
   }
   auto issue_tile = [&](int t, int buf) {
     const int key0 = t * BN;
     char* dst = smem + buf * G::BUF;
 #pragma unroll
-    for (int i = 0; i < G::KCOPIES; ++i) {
+    for (int i = 0; i < KCOPIES; ++i) {
       const int key = min(key0 + k_row[i], n_keys - 1);   // rows past the range: any finite row
       __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key) * G::KROW + k_src[i],
-                                       dst + (i * 4 + wave) * 1024, 16, 0, 0);
+                                       dst + (i * NW + wave) * 1024, 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < G::VCOPIES; ++i)
+    for (int i = 0; i < VCOPIES; ++i)
       __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src[i],
-                                       dst + G::KBYTES + (i * 4 + wave) * 1024, 16, 0, 0);
+                                       dst + G::KBYTES + (i * NW + wave) * 1024, 16, 0, 0);
   };
 
-  // ---- MFMA operand read addresses (per lane; k-steps differ by XOR) ---------
-  const int x = l32 & 7;
-  int ka[4], va[4];
+  // ---- MFMA operand read addresses -----------------------------------------
+  // lane reads LDS row l32 (+ 32 per 32-row tile), logical chunk 2s + g (k-step s)
+  int ka[KSTEPS], va[PSTEPS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ka[j] = l32 * G::KROW + (((2 * j + g) ^ x) * 16);
-    va[j] = G::KBYTES + l32 * G::VROW + (((2 * j + g) ^ x) * 16);
-  }
+  for (int s = 0; s < KSTEPS; ++s) ka[s] = l32 * G::KROW + swz(2 * s + g, l32, G::KC) * 16;
+#pragma unroll
+  for (int s = 0; s < PSTEPS; ++s) va[s] = G::KBYTES + l32 * G::VROW + swz(2 * s + g, l32, G::VC) * 16;
 
   f32x16 o[QB][DT];
   float m[QB], l[QB];            // exponent reference (log2 units), per-lane partial row sum
@@ -194,8 +214,7 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + ka[s & 3] + (s >> 2) * 128 +
-                                                          mt * 32 * G::KROW);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + ka[s] + mt * 32 * G::KROW);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sacc[qb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[qb][s], sacc[qb][mt], 0, 0, 0);
@@ -252,22 +271,35 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
       }
   };
 
-  // one barrier per tile: it publishes tile t (all waves' copies landed) and
-  // retires tile t-1 (all waves done reading the buffer tile t+1 goes to)
+  // Copy pipeline: tiles t .. t + STAGES - 2 are in flight when tile t is
+  // computed. One barrier per tile publishes tile t (every wave's copies for it
+  // have landed: each wave first waits until at most its copies for the
+  // STAGES - 2 later tiles are outstanding) and retires tile t - 1, whose
+  // buffer then receives tile t + STAGES - 1.
+  constexpr int PER_TILE = KCOPIES + VCOPIES;
   const int t_stop = min(t_end, t_tail);         // full tiles [t_begin, t_stop)
-  if (t_begin < t_end) issue_tile(t_begin, 0);
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i)
+    if (t_begin + i < t_end) issue_tile(t_begin + i, i);
+  auto wait_tile = [&](int t) {
+    const int ahead = min(t_end - 1 - t, STAGES - 2);   // later tiles already issued
+    if (ahead >= STAGES - 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * PER_TILE));
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+  };
   int t = t_begin;
   for (; t < t_stop; ++t) {
-    const int buf = (t - t_begin) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < t_end) issue_tile(t + 1, buf ^ 1);
+    const int buf = (t - t_begin) % STAGES;
+    wait_tile(t);
+    if (t + STAGES - 1 < t_end) issue_tile(t + STAGES - 1, (t - t_begin + STAGES - 1) % STAGES);
     compute_tile(t, buf, std::false_type{});
   }
   if (t < t_end) {                               // the ragged last tile
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    compute_tile(t, (t - t_begin) & 1, std::true_type{});
+    wait_tile(t);
+    compute_tile(t, (t - t_begin) % STAGES, std::true_type{});
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -307,20 +339,276 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
   }
 }
 
+// Value of x held by lane (l ^ 32): v_permlane32_swap exchanges the two wave halves in
+// the VALU, no LDS round trip.
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Ping-pong schedule, 8 waves x 32 query rows (BM = 256), 4 LDS stages.
+// Each wave runs a sequence of blocks separated by workgroup barriers:
+//   M(0) = QK(0);  V(0) = softmax(0);  M(i) = QK(i) + PV(i-1);  V(i);  ...;  M(n) = PV(n-1)
+// so an M block is only MFMAs (and their LDS operand reads) and a V block only
+// VALU work. Waves 4-7 run one barrier behind waves 0-3, so on every SIMD (one
+// wave of each group) one wave's MFMA block overlaps the other's softmax block.
+// Tile copies: tile i+2 is issued at the start of M(i); before the barrier
+// that opens global slot 2i, every wave waits for its copies of tile i. A
+// stage is reused 4 tiles later, after the lagging group's last PV read of it.
+template <int D>
+__device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p) {
+  using G = Bf16Geom<D>;
+  constexpr int NW = 8, STAGES = 4;
+  constexpr int BN = G::BN;
+  constexpr int BM = NW * 32;
+  constexpr int KSTEPS = D / 16, MT = BN / 32, DT = D / 32, PSTEPS = BN / 16;
+  constexpr int KCOPIES = G::KBYTES / 1024 / NW;
+  constexpr int VCOPIES = G::VBYTES / 1024 / NW;
+  constexpr int PER_TILE = KCOPIES + VCOPIES;
+  static_assert(KCOPIES * NW * 1024 == G::KBYTES && VCOPIES * NW * 1024 == G::VBYTES, "copy split");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * G::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lag = wave >= 4 ? 1 : 0;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int n_work = p.B * p.H * p.q_tiles * p.kv_splits;
+  const int work = xcd_remap(blockIdx.x, n_work);
+  const int qt = work % p.q_tiles;
+  const int rest = work / p.q_tiles;
+  const int split = rest % p.kv_splits;
+  const int bh = rest / p.kv_splits;
+  const int t_begin = static_cast<int>((static_cast<int64_t>(split) * p.key_tiles) / p.kv_splits);
+  const int t_end = static_cast<int>((static_cast<int64_t>(split + 1) * p.key_tiles) / p.kv_splits);
+  const int n = t_end - t_begin;                 // tiles of this work item (>= 1)
+  const int n_keys = p.n_keys;
+
+  const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
+  const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
+
+  const int q = qt * BM + wave * 32 + l32;
+  bf16x8 bq[KSTEPS];
+  {
+    const int qrow = min(q, p.Nc - 1);
+    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
+  }
+
+  // Copy sources (byte offsets) of copy c of this wave; K rows of every (b, h)
+  // are padded to key_stride, so a tile never reads past the allocation.
+  // Recomputed per copy (a few VALU ops) to keep registers for the pipeline.
+  auto k_src = [&](int c) {
+    const int P = (c * NW + wave) * 64 + lane;
+    const int r = P / G::KC;
+    return swap_bits23(r) * G::KROW + swz(P % G::KC, r, G::KC) * 16;
+  };
+  auto v_src = [&](int c) {
+    const int P = (c * NW + wave) * 64 + lane;
+    const int d = P / G::VC;
+    return d * p.key_stride * 2 + swz(P % G::VC, d, G::VC) * 16;
+  };
+  auto issue_tile = [&](int i) {                 // tile t_begin + i into stage i % STAGES
+    const int key0 = (t_begin + i) * BN;
+    char* dst = smem + (i % STAGES) * G::BUF;
+#pragma unroll
+    for (int c = 0; c < KCOPIES; ++c)
+      __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key0) * G::KROW + k_src(c),
+                                       dst + (c * NW + wave) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int c = 0; c < VCOPIES; ++c)
+      __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src(c),
+                                       dst + G::KBYTES + (c * NW + wave) * 1024, 16, 0, 0);
+  };
+
+  // K operand address of k-step s: row l32, swizzled chunk of logical chunk 2s + g,
+  // recomputed per read (two VALU ops) rather than held in 8 registers
+  const int ka_row = l32 * G::KROW;
+  auto ka = [&](int s) { return ka_row + swz(2 * s + g, l32, G::KC) * 16; };
+  auto va = [&](int s) { return G::KBYTES + l32 * G::VROW + swz(2 * s + g, l32, G::VC) * 16; };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
+  f32x16 sacc[MT];
+  bf16x8 pb[PSTEPS];
+  float m = -__builtin_inff(), l = 0.f;
+
+  auto qk = [&](int i) {
+    const char* stage = smem + (i % STAGES) * G::BUF;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + ka(s) + mt * 32 * G::KROW);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
+      }
+  };
+  auto pv = [&](int i) {
+    const char* stage = smem + (i % STAGES) * G::BUF;
+#pragma unroll
+    for (int s = 0; s < PSTEPS; ++s)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + va(s) + dt * 32 * G::VROW);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
+      }
+  };
+  auto softmax = [&](int i) {
+    const int key0 = (t_begin + i) * BN;
+    if (key0 + BN > n_keys) {                     // ragged last tile (wave-uniform branch)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys) sacc[mt][j] = -__builtin_inff();
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mt][j]);
+    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int s = 0; s < PSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pvl = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m));
+        rs += pvl;
+        pb[s][e] = static_cast<__bf16>(pvl);
+      }
+    l += rs;
+  };
+
+  // QK(i) and PV(i-1) interleaved: step k issues the K operand read and the QK
+  // MFMA of (s = k / MT, mt = k % MT) and the V operand read and the PV MFMA of
+  // (s = k / DT, dt = k % DT); the scheduling barriers keep two LDS reads ahead
+  // of two MFMAs so the operand registers in flight stay bounded.
+  static_assert(KSTEPS * MT == PSTEPS * DT, "QK and PV have the same MFMA count");
+  auto qk_pv = [&](int i) {
+    const char* ks = smem + (i % STAGES) * G::BUF;
+    const char* vs = smem + ((i - 1) % STAGES) * G::BUF;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KSTEPS * MT; ++k) {
+      const int s = k / MT, mt = k % MT;
+      const int sv = k / DT, dt = k % DT;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ka(s) + mt * 32 * G::KROW);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(vs + va(sv) + dt * 32 * G::VROW);
+      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pb[sv], o[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // operands of step 0
+#pragma unroll
+    for (int k = 0; k < KSTEPS * MT; ++k) {
+      if (k + 1 < KSTEPS * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // step k+1 reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // step k MFMAs
+    }
+  };
+  // Both groups run the same block sequence; waves 4-7 pass one extra barrier
+  // first (and waves 0-3 one at the end), which offsets them by one block.
+  // Before the barrier that opens global slot 2i every wave has waited for
+  // its copies of tile i: for the leading group that barrier precedes M(i),
+  // for the lagging group it precedes V(i-1).
+  auto wait_tile = [&](int i) {                  // tile i complete; tile i + 1 may be in flight
+    if (i + 1 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_TILE));
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  issue_tile(0);
+  if (n > 1) issue_tile(1);
+  if (lag) {
+    wait_tile(0);
+    __syncthreads();
+  }
+  if (!lag) wait_tile(0);
+  __syncthreads();
+  if (n > 2) issue_tile(2);
+  qk(0);                                         // M(0)
+  if (lag && n > 1) wait_tile(1);
+  __syncthreads();
+  softmax(0);                                    // V(0)
+  for (int i = 1; i < n; ++i) {
+    if (!lag) wait_tile(i);
+    __syncthreads();
+    if (i + 2 < n) issue_tile(i + 2);
+    qk_pv(i);                                    // M(i)
+    if (lag && i + 1 < n) wait_tile(i + 1);
+    __syncthreads();
+    softmax(i);                                  // V(i)
+  }
+  __syncthreads();
+  pv(n - 1);                                     // M(n)
+  if (!lag) __syncthreads();
+
+  // ---- epilogue ---------------------------------------------------------------
+  const float l_tot = l + xor32(l);
+  if (q >= p.Nc) return;
+  const float inv = 1.f / l_tot;
+  const float lse2 = m + __log2f(l_tot);
+  const int b = bh / p.H, h = bh - b * p.H;
+  if (p.kv_splits == 1) {
+    __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[dt][4 * jj + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
+      }
+    if (p.lse != nullptr && g == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
+  } else {
+    const size_t row = (static_cast<size_t>(split) * p.B * p.H + bh) * p.Nc + q;
+    float* dst = p.part_o + row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
+            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                        o[dt][4 * jj + 3] * inv);
+    if (g == 0) p.part_lse[row] = lse2;
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d128(AttnParams p) {
-  chunk_attention_bf16_body<128, 1>(p);
+  chunk_attention_bf16_body<128, 4, 1, 2>(p);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d64(AttnParams p) {
-  chunk_attention_bf16_body<64, 1>(p);
+  chunk_attention_bf16_body<64, 4, 1, 2>(p);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_bf16_d128_q64(AttnParams p) {
-  chunk_attention_bf16_body<128, 2>(p);
+  chunk_attention_bf16_body<128, 4, 2, 2>(p);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_bf16_d64_q64(AttnParams p) {
-  chunk_attention_bf16_body<64, 2>(p);
+  chunk_attention_bf16_body<64, 4, 2, 2>(p);
+}
+
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_pp(AttnParams p) {
+  chunk_attention_bf16_pp_body<128>(p);
+}
+
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d64_pp(AttnParams p) {
+  chunk_attention_bf16_pp_body<64>(p);
 }
 
 // fp32: one query row per lane, 64 rows per block, 32-key tiles through LDS.
@@ -435,9 +723,14 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
   const int64_t n_work = static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
   if (n_work <= 0) return hipSuccess;
   if (dtype == 1) {
-    auto k = p.q_rows_per_block == 256 ? (p.D == 128 ? chunk_attention_bf16_d128_q64 : chunk_attention_bf16_d64_q64)
-                                       : (p.D == 128 ? chunk_attention_bf16_d128 : chunk_attention_bf16_d64);
-    hipLaunchKernelGGL(k, dim3(n_work), dim3(kThreads), 0, st, p);
+    if (p.variant == 3) {
+      hipLaunchKernelGGL(p.D == 128 ? chunk_attention_bf16_d128_pp : chunk_attention_bf16_d64_pp, dim3(n_work),
+                         dim3(2 * kThreads), 0, st, p);
+    } else {
+      auto k = p.variant == 2 ? (p.D == 128 ? chunk_attention_bf16_d128_q64 : chunk_attention_bf16_d64_q64)
+                              : (p.D == 128 ? chunk_attention_bf16_d128 : chunk_attention_bf16_d64);
+      hipLaunchKernelGGL(k, dim3(n_work), dim3(kThreads), 0, st, p);
+    }
   } else {
     if (p.D == 128) hipLaunchKernelGGL(chunk_attention_f32<128>, dim3(n_work), dim3(64), 0, st, p);
     else hipLaunchKernelGGL(chunk_attention_f32<64>, dim3(n_work), dim3(64), 0, st, p);

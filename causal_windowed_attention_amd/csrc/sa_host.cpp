@@ -95,7 +95,8 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->max_splits = static_cast<int32_t>(ms < 1 ? 1 : (ms > sa::kMaxKvSplits ? sa::kMaxKvSplits : ms));
 
   const size_t bh = static_cast<size_t>(d->B) * d->H;
-  d->k_bytes = bh * static_cast<size_t>(keys) * d->D * d->elem;
+  // K rows padded to key_stride per (b, h): a key tile never leaves the allocation
+  d->k_bytes = bh * static_cast<size_t>(d->key_stride) * d->D * d->elem;
   d->vt_bytes = bh * static_cast<size_t>(d->D) * d->key_stride * d->elem;
   d->q_bytes = bh * static_cast<size_t>(d->Nc) * d->D * d->elem;
   d->part_bytes = d->max_splits > 1
@@ -189,7 +190,7 @@ void base_write_params(const sa_stream* s, RopeWriteParams* p) {
   p->vtcache = s->vtcache();
   p->h_cs = s->h_cs();
   p->w_cs = s->w_cs();
-  p->k_bh_stride = static_cast<int64_t>(d.n_slots) * d.Nc * d.D;
+  p->k_bh_stride = static_cast<int64_t>(d.key_stride) * d.D;
   p->vt_bh_stride = static_cast<int64_t>(d.D) * d.key_stride;
   p->key_stride = d.key_stride;
   p->n_tokens = d.Nc;
@@ -224,10 +225,17 @@ sa_status timed(sa_stream* s, int kid, hipStream_t st, F&& launch) {
   return SA_OK;
 }
 
+// bf16 attention kernel variant used for this stream (automatic: the
+// ping-pong kernel, variant 3).
+int attn_variant(const sa_stream* s) {
+  if (s->d.dtype != SA_BF16) return 0;
+  return s->variant_opt == 0 ? 3 : s->variant_opt;
+}
+
 // Query rows per workgroup of the attention kernel used for this stream.
 int attn_block_m(const sa_stream* s) {
   if (s->d.dtype != SA_BF16) return sa::kF32BlockM;
-  return s->variant_opt == 2 ? sa::kBf16BlockMWide : sa::kBf16BlockM;
+  return attn_variant(s) == 1 ? sa::kBf16BlockM : sa::kBf16BlockMWide;
 }
 
 int choose_splits(const sa_stream* s, int key_tiles, int q_tiles) {
@@ -237,7 +245,7 @@ int choose_splits(const sa_stream* s, int key_tiles, int q_tiles) {
     // Fill the chip: 256 CUs x resident workgroups. Split the key range only
     // when the (b, h, q-tile) grid leaves more than a quarter of the slots idle.
     const int64_t blocks = static_cast<int64_t>(d.B) * d.H * q_tiles;
-    const int64_t slots = attn_block_m(s) == sa::kBf16BlockMWide ? 256 : 512;
+    const int64_t slots = attn_block_m(s) == sa::kBf16BlockMWide ? 256 : 512;   // resident workgroups
     splits = 1;
     if (blocks * 4 < slots * 3) {
       splits = static_cast<int>((slots + blocks - 1) / blocks);
@@ -328,9 +336,10 @@ sa_status sa_stream_create(const sa_config* cfg, void* d_workspace, size_t works
         tab[i++] = make_float2(static_cast<float>(std::cos(a)), static_cast<float>(std::sin(a)));
       }
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    // The attention kernel's ragged last key tile reads a few V^T entries past
-    // the visible keys (with weight 0); zeroing the V^T cache once keeps them finite.
-    if (hipMemsetAsync(s->ws + d.vt_off, 0, d.vt_bytes, hs) != hipSuccess) {
+    // The attention kernel's ragged last key tile reads a few K rows and V^T
+    // entries past the visible keys (masked, weight 0); zeroing the caches once
+    // keeps them finite.
+    if (hipMemsetAsync(s->ws + d.k_off, 0, d.vt_off - d.k_off + d.vt_bytes, hs) != hipSuccess) {
       delete s;
       return SA_ERR_DEVICE;
     }
@@ -408,11 +417,12 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
     ap.lse = lse;
     ap.part_o = reinterpret_cast<float*>(s->ws + d.part_off);
     ap.part_lse = ap.part_o + static_cast<size_t>(d.max_splits) * d.B * d.H * d.Nc * d.D;
-    ap.k_bh_stride = static_cast<int64_t>(d.n_slots) * d.Nc * d.D;
+    ap.k_bh_stride = static_cast<int64_t>(d.key_stride) * d.D;
     ap.vt_bh_stride = static_cast<int64_t>(d.D) * d.key_stride;
     ap.key_stride = d.key_stride;
     ap.n_keys = n_keys;
     ap.Nc = d.Nc; ap.B = d.B; ap.H = d.H; ap.D = d.D;
+    ap.variant = attn_variant(s);
     ap.q_rows_per_block = bm;
     ap.q_tiles = q_tiles;
     ap.kv_splits = splits;
@@ -493,7 +503,7 @@ sa_status sa_rope_refresh(sa_stream* s, int32_t new_base_t, uint32_t flags, void
     RefreshParams rp;
     std::memset(&rp, 0, sizeof(rp));
     rp.kcache = s->kcache();
-    rp.k_bh_stride = static_cast<int64_t>(d.n_slots) * d.Nc * d.D;
+    rp.k_bh_stride = static_cast<int64_t>(d.key_stride) * d.D;
     rp.BH = d.B * d.H; rp.D = d.D; rp.Nc = d.Nc; rp.dt = d.dt;
     for (int j = 0; j < d.dt / 2; ++j) {
       const double a = -static_cast<double>(delta) * freq(d, d.dt, j);
@@ -594,7 +604,7 @@ sa_status sa_stream_layout(const sa_stream* s, sa_layout* out) {
   sa_layout L;
   std::memset(&L, 0, sizeof(L));
   L.k_offset = d.k_off;
-  L.k_bh_stride = static_cast<uint64_t>(d.n_slots) * d.Nc * d.D * d.elem;
+  L.k_bh_stride = static_cast<uint64_t>(d.key_stride) * d.D * d.elem;
   L.vt_offset = d.vt_off;
   L.vt_bh_stride = static_cast<uint64_t>(d.D) * d.key_stride * d.elem;
   L.q_offset = d.q_off;
@@ -618,7 +628,7 @@ sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value) {
       s->kv_splits_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_ATTN_VARIANT:
-      if (value < 0 || value > 2) return SA_ERR_INVALID_ARGUMENT;
+      if (value < 0 || value > 3) return SA_ERR_INVALID_ARGUMENT;
       s->variant_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_PROFILE:

@@ -14,7 +14,7 @@ constexpr int kMaxRefreshPairs = 64;    // d_t / 2 <= D / 2 <= 64
 // bf16 attention tiling (chunk_attention_bf16*): 4 waves x 32 or 64 query rows,
 // 64-key tiles.
 constexpr int kBf16BlockM = 128;      // variant 1: 32 query rows per wave
-constexpr int kBf16BlockMWide = 256;  // variant 2: 64 query rows per wave
+constexpr int kBf16BlockMWide = 256;  // variant 2: 64 query rows per wave; variant 3: 8 waves x 32
 constexpr int kBf16BlockN = 64;
 // fp32 attention tiling (chunk_attention_f32): 64 query rows, 32-key tiles.
 constexpr int kF32BlockM = 64;
@@ -71,6 +71,7 @@ struct AttnParams {
   int32_t key_stride;
   int32_t n_keys;
   int32_t Nc, B, H, D;
+  int32_t variant;      // bf16 kernel: 1 (4 waves x 32 rows), 2 (4 x 64), 3 (ping-pong 8 x 32)
   int32_t q_rows_per_block;  // BlockM of the kernel variant
   int32_t q_tiles;      // ceil(Nc / BlockM)
   int32_t kv_splits;    // >= 1

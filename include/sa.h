@@ -134,7 +134,7 @@ typedef struct sa_slot_info {
 } sa_slot_info;
 
 /* Byte offsets of the workspace regions (for inspection and tests). Per (b, h):
- *  K cache:   [n_slots * Nc][D] rows, slot s at rows [s*Nc, (s+1)*Nc)
+ *  K cache:   [key_stride][D] rows, slot s at rows [s*Nc, (s+1)*Nc)
  *  V cache:   transposed, [D][key_stride] (keys of all slots contiguous per channel)
  *  Q scratch: [Nc][D] rotated queries of the last attend                           */
 typedef struct sa_layout {
@@ -159,8 +159,9 @@ typedef enum sa_kernel_id {
 typedef enum sa_option {
   SA_OPT_KV_SPLITS = 0,     /* 0: automatic; n >= 1: force n key-range splits per query tile */
   SA_OPT_PROFILE = 1,       /* 1: record HIP events around every launch (sa_profile_read)    */
-  SA_OPT_ATTN_VARIANT = 2   /* bf16 attention kernel: 0 automatic, 1 = 32 query rows per
-                               wave (128 per workgroup), 2 = 64 rows per wave (256)          */
+  SA_OPT_ATTN_VARIANT = 2   /* bf16 attention kernel: 0 automatic (3), 1 = 4 waves x 32
+                               query rows, 2 = 4 waves x 64 rows, 3 = 8 waves x 32 rows with
+                               a ping-pong MFMA/softmax schedule                             */
 } sa_option;
 
 typedef struct sa_stream sa_stream;

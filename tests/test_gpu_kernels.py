@@ -132,12 +132,12 @@ OPS = ["attend", "append", "attend", "append0", "attend", "append", "attend", "a
        "attend", "append", "attend"]
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 def test_stream_bf16_d128_storage_and_outputs(variant):
     _run_sequence(SMALL, OPS, variant=variant)
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 def test_stream_bf16_d64(variant):
     w = synth.small_variant(SMALL, name="small_d64", head_dim=64, frame_h=4, frame_w=8,
                             frames_per_chunk=2, window_chunks=3)
@@ -161,7 +161,7 @@ def test_stream_f32_d128_with_sink_update():
     _run_sequence(w, OPS)
 
 
-@pytest.mark.parametrize("S,W,B,variant", [(0, 2, 1, 1), (1, 0, 2, 2), (0, 0, 1, 1), (2, 1, 2, 2)])
+@pytest.mark.parametrize("S,W,B,variant", [(0, 2, 1, 1), (1, 0, 2, 2), (0, 0, 1, 3), (2, 1, 2, 3)])
 def test_edge_shapes(S, W, B, variant):
     w = synth.small_variant(SMALL, name=f"edge_S{S}W{W}", sink_chunks=S, window_chunks=W, batch=B,
                             heads=2)
@@ -186,7 +186,7 @@ def _steady_stream(w, n_commit):
     return s, hist
 
 
-@pytest.mark.parametrize("dtype,variant", [("bf16", 1), ("bf16", 2), ("f32", 0)])
+@pytest.mark.parametrize("dtype,variant", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("f32", 0)])
 def test_forced_kv_splits_and_repeat(dtype, variant):
     w = synth.small_variant(SMALL, name="splits", dtype=dtype, frame_h=10, frame_w=10,
                             frames_per_chunk=3, batch=1, heads=2, window_chunks=3)

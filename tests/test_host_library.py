@@ -228,7 +228,7 @@ def test_workspace_layout_and_plans():
         nc, bh, d = w.tokens_per_chunk, w.batch * w.heads, w.head_dim
         slots = w.sink_chunks + w.window_chunks + 1
         elem = 2 if w.dtype == "bf16" else 4
-        assert lay["k_bh_stride"] == slots * nc * d * elem
+        assert lay["k_bh_stride"] == lay["key_stride"] * d * elem
         assert lay["key_stride"] % 64 == 0 and lay["key_stride"] >= slots * nc
         assert lay["vt_offset"] >= lay["k_offset"] + bh * lay["k_bh_stride"]
         assert lay["q_offset"] >= lay["vt_offset"] + bh * lay["vt_bh_stride"]
@@ -239,7 +239,7 @@ def test_workspace_layout_and_plans():
             s.chunk_attend(None, None, None)
             st = s.query()
             assert st["visible_chunks"] == min(c, slots - 1) + 1
-            bm = 128 if w.dtype == "bf16" else 64
+            bm = 256 if w.dtype == "bf16" else 64
             bn = 64 if w.dtype == "bf16" else 32
             assert st["last_q_tiles"] == -(-nc // bm)
             assert st["last_key_tiles"] == -(-st["visible_keys"] // bn)

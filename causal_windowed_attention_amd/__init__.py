@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 from . import _lib as L
 from ._lib import (SA_BF16, SA_F32, SA_K_ATTN_COMBINE, SA_K_CHUNK_ATTENTION, SA_K_COUNT,
                    SA_K_KV_APPEND, SA_K_ROPE_APPLY, SA_K_ROPE_REFRESH, SA_K_SINK_UPDATE,
-                   SA_OK, SA_OPT_ATTN_VARIANT, SA_OPT_KV_SPLITS, SA_OPT_PROFILE, SA_REFRESH_SHIFT_SINK,
+                   SA_OK, SA_OPT_ATTN_VARIANT, SA_OPT_KV_SPLITS, SA_OPT_SCHEDULE, SA_OPT_PROFILE, SA_REFRESH_SHIFT_SINK,
                    SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_STAGING, SA_SLOT_WINDOW, sa_config)
 
 __all__ = [
@@ -27,7 +27,7 @@ __all__ = [
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
     "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "Stream",
     "SA_F32", "SA_BF16", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
-    "SA_OPT_ATTN_VARIANT",
+    "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
     "SA_K_ROPE_APPLY", "SA_K_CHUNK_ATTENTION", "SA_K_ATTN_COMBINE", "SA_K_KV_APPEND",
     "SA_K_ROPE_REFRESH", "SA_K_SINK_UPDATE", "SA_K_COUNT",
     "SA_SLOT_EMPTY", "SA_SLOT_SINK", "SA_SLOT_WINDOW", "SA_SLOT_STAGING",

@@ -27,7 +27,7 @@ SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_WINDOW, SA_SLOT_STAGING = 0, 1, 2, 3
 SA_K_ROPE_APPLY, SA_K_CHUNK_ATTENTION, SA_K_ATTN_COMBINE = 0, 1, 2
 SA_K_KV_APPEND, SA_K_ROPE_REFRESH, SA_K_SINK_UPDATE, SA_K_COUNT = 3, 4, 5, 6
 # sa_option
-SA_OPT_KV_SPLITS, SA_OPT_PROFILE, SA_OPT_ATTN_VARIANT = 0, 1, 2
+SA_OPT_KV_SPLITS, SA_OPT_PROFILE, SA_OPT_ATTN_VARIANT, SA_OPT_SCHEDULE = 0, 1, 2, 3
 
 
 class sa_config(ctypes.Structure):
@@ -47,7 +47,8 @@ class sa_state(ctypes.Structure):
                 ("n_slots", ctypes.c_int32), ("visible_chunks", ctypes.c_int32),
                 ("visible_keys", ctypes.c_int32), ("staged_valid", ctypes.c_int32),
                 ("last_q_tiles", ctypes.c_int32), ("last_kv_splits", ctypes.c_int32),
-                ("last_key_tiles", ctypes.c_int32), ("last_delta", ctypes.c_int32)]
+                ("last_key_tiles", ctypes.c_int32), ("last_delta", ctypes.c_int32),
+                ("last_sk_groups", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class sa_slot_info(ctypes.Structure):

@@ -62,9 +62,10 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
 }
 
 // Swizzled position of 16-byte chunk c in LDS row r of a tile whose rows hold
-// `chunks` chunks (8 or 16); an involution in c for fixed r.
+// `chunks` chunks (4, 8 or 16; 4 rows of 64 bytes, 2 of 128 or 1 of 256 share a
+// 256-byte bank window); an involution in c for fixed r.
 __device__ __forceinline__ int swz(int c, int r, int chunks) {
-  return chunks >= 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+  return chunks >= 16 ? (c ^ (r & 15)) : chunks == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
 // Swap bits 2 and 3 of a tile row index (an involution).
@@ -83,9 +84,9 @@ __device__ __forceinline__ int swap_bits23(int r) {
 // (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at LDS base +
 // 16 i), choosing each lane's source so that the chunk lands at its swizzled
 // place; no VGPR staging, no LDS write instructions.
-template <int D>
+template <int D, int BN_ = kBf16BlockN>
 struct Bf16Geom {
-  static constexpr int BN = kBf16BlockN;
+  static constexpr int BN = BN_;
   static constexpr int KROW = D * 2;          // bytes per K row
   static constexpr int VROW = BN * 2;         // bytes per V^T row
   static constexpr int KBYTES = BN * KROW;
@@ -101,6 +102,10 @@ struct Bf16Geom {
 // row is only raised when a tile's maximum exceeds it by more than this, so
 // un-normalised weights stay below 2^8 and the O rescale runs rarely.
 constexpr float kRescaleThreshold = 8.0f;
+
+#ifndef PP_READ_AHEAD
+#define PP_READ_AHEAD 1
+#endif
 
 // Kernel shape parameters:
 //  NW     waves per workgroup (4 or 8); each wave owns 32 * QB query rows
@@ -355,10 +360,23 @@ __device__ __forceinline__ float xor32(float x) {
 // Tile copies: tile i+2 is issued at the start of M(i); before the barrier
 // that opens global slot 2i, every wave waits for its copies of tile i. A
 // stage is reused 4 tiles later, after the lagging group's last PV read of it.
+// Output of one ping-pong segment: the final rows, a key-range split partial,
+// or a stream-K partial slot.
+enum PpOut { kPpFinal = 0, kPpSplit = 1, kPpStreamK = 2 };
+constexpr int kPpStages = 4;
+
 template <int D>
-__device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p) {
+struct PpSmem {
+  static constexpr int BYTES = kPpStages * Bf16Geom<D>::BUF;
+};
+
+// One ping-pong work segment: query tile qt of (b, h) = bh against key tiles
+// [t_begin, t_end).
+template <int D>
+__device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int bh, int qt, int t_begin,
+                                           int t_end, int mode, int slot) {
   using G = Bf16Geom<D>;
-  constexpr int NW = 8, STAGES = 4;
+  constexpr int NW = 8, STAGES = kPpStages;
   constexpr int BN = G::BN;
   constexpr int BM = NW * 32;
   constexpr int KSTEPS = D / 16, MT = BN / 32, DT = D / 32, PSTEPS = BN / 16;
@@ -366,23 +384,13 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
   constexpr int VCOPIES = G::VBYTES / 1024 / NW;
   constexpr int PER_TILE = KCOPIES + VCOPIES;
   static_assert(KCOPIES * NW * 1024 == G::KBYTES && VCOPIES * NW * 1024 == G::VBYTES, "copy split");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * G::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lag = wave >= 4 ? 1 : 0;
   const int l32 = lane & 31, g = lane >> 5;
-
-  const int n_work = p.B * p.H * p.q_tiles * p.kv_splits;
-  const int work = xcd_remap(blockIdx.x, n_work);
-  const int qt = work % p.q_tiles;
-  const int rest = work / p.q_tiles;
-  const int split = rest % p.kv_splits;
-  const int bh = rest / p.kv_splits;
-  const int t_begin = static_cast<int>((static_cast<int64_t>(split) * p.key_tiles) / p.kv_splits);
-  const int t_end = static_cast<int>((static_cast<int64_t>(split + 1) * p.key_tiles) / p.kv_splits);
-  const int n = t_end - t_begin;                 // tiles of this work item (>= 1)
+  const int n = t_end - t_begin;                 // tiles of this segment (>= 1)
   const int n_keys = p.n_keys;
 
   const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
@@ -512,10 +520,11 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
       sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pb[sv], o[dt], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // operands of step 0
+    constexpr int AHEAD = PP_READ_AHEAD;                   // steps of operand reads in flight
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);   // operands of steps 0 .. AHEAD-1
 #pragma unroll
     for (int k = 0; k < KSTEPS * MT; ++k) {
-      if (k + 1 < KSTEPS * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // step k+1 reads
+      if (k + AHEAD < KSTEPS * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // step k+AHEAD reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // step k MFMAs
     }
   };
@@ -553,6 +562,295 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
   __syncthreads();
   pv(n - 1);                                     // M(n)
   if (!lag) __syncthreads();
+
+  // ---- epilogue ---------------------------------------------------------------
+  const float l_tot = l + xor32(l);
+  const float inv = 1.f / l_tot;
+  const float lse2 = m + __log2f(l_tot);
+  if (mode == kPpStreamK) {                      // partial rows of this q-tile, all BM of them
+    const size_t row = static_cast<size_t>(slot) * BM + wave * 32 + l32;
+    float* dst = p.sk_part_o + row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
+            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                        o[dt][4 * jj + 3] * inv);
+    if (g == 0) p.sk_part_lse[row] = lse2;
+    return;
+  }
+  if (q >= p.Nc) return;
+  const int b = bh / p.H, h = bh - b * p.H;
+  if (mode == kPpFinal) {
+    __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[dt][4 * jj + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
+      }
+    if (p.lse != nullptr && g == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
+  } else {
+    const size_t row = (static_cast<size_t>(slot) * p.B * p.H + bh) * p.Nc + q;
+    float* dst = p.part_o + row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
+            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                        o[dt][4 * jj + 3] * inv);
+    if (g == 0) p.part_lse[row] = lse2;
+  }
+}
+
+// First iteration of stream-K workgroup w: ranges [start(w), start(w + 1)) split
+// the L = q-tiles * key-tiles iterations evenly.
+__device__ __forceinline__ int64_t sk_start(int w, int64_t L, int G) { return (static_cast<int64_t>(w) * L) / G; }
+
+// Ping-pong kernel driver. Grid mode: one workgroup per (b*h, split, q-tile).
+// Stream-K mode (sk_groups > 0): sk_groups persistent workgroups, each running
+// its range as segments; a segment that covers a whole q-tile writes the final
+// rows, a partial one writes slot 2w (the range's first segment) or 2w + 1 (its
+// last), merged afterwards by attn_sk_combine.
+template <int D>
+__device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p) {
+  __shared__ __attribute__((aligned(1024))) char smem[PpSmem<D>::BYTES];
+  const bool sk = p.sk_groups > 0;
+  const int T = p.key_tiles;
+  // grid mode: one segment, the work item's (q-tile, split); stream-K: the range of w
+  const int G = sk ? p.sk_groups : p.B * p.H * p.q_tiles * p.kv_splits;
+  const int w = xcd_remap(blockIdx.x, G);
+  const int64_t L = static_cast<int64_t>(p.B) * p.H * p.q_tiles * T;
+  const int64_t r0 = sk ? sk_start(w, L, G) : 0, r1 = sk ? sk_start(w + 1, L, G) : 1;
+  for (int64_t it = r0; it < r1;) {
+    int bh, qt, t0, t1, mode, slot;
+    if (sk) {
+      const int64_t u = it / T;                  // q-tile index: bh * q_tiles + qt
+      bh = static_cast<int>(u / p.q_tiles);
+      qt = static_cast<int>(u % p.q_tiles);
+      t0 = static_cast<int>(it - u * T);
+      t1 = static_cast<int>(min(static_cast<int64_t>(T), r1 - u * T));
+      mode = (t0 == 0 && t1 == T) ? kPpFinal : kPpStreamK;
+      slot = 2 * w + (it == r0 ? 0 : 1);
+      it = u * T + t1;
+    } else {
+      qt = w % p.q_tiles;
+      const int rest = w / p.q_tiles;
+      const int split = rest % p.kv_splits;
+      bh = rest / p.kv_splits;
+      t0 = static_cast<int>((static_cast<int64_t>(split) * T) / p.kv_splits);
+      t1 = static_cast<int>((static_cast<int64_t>(split + 1) * T) / p.kv_splits);
+      mode = p.kv_splits == 1 ? kPpFinal : kPpSplit;
+      slot = split;
+      it = r1;
+    }
+    pp_segment<D>(p, smem, bh, qt, t0, t1, mode, slot);
+    if (it < r1) __syncthreads();                // the next segment reuses every LDS stage
+  }
+}
+
+// Software-pipelined schedule, 8 waves x 32 query rows (BM = 256), two waves
+// per SIMD. Block X(i) of every wave holds three independent streams:
+//   QK(i+1) MFMAs -> S_next,  PV(i-1) MFMAs <- P_prev,  softmax(i) VALU: S_cur -> P_cur,
+// interleaved by scheduling barriers so each wave keeps the matrix pipe fed
+// while its softmax runs; S and P are double-buffered (the loop is unrolled by
+// two so the buffers swap roles without copies). A block needs K of tile i+1
+// and V of tile i-1, so a tile occupies its LDS stage for three blocks; copies
+// for tile i+STAGES-2 are issued at the start of X(i). The O rescale (rare,
+// when a row maximum grows by more than 2^8) runs after the block's PV MFMAs,
+// and then recomputes P(i) with the new reference.
+template <int D, int STAGES, int BNT>
+__device__ __forceinline__ void chunk_attention_bf16_pl_body(const AttnParams& p) {
+  using G = Bf16Geom<D, BNT>;
+  constexpr int NW = 8;
+  constexpr int BN = G::BN;
+  constexpr int BM = NW * 32;
+  constexpr int KSTEPS = D / 16, MT = BN / 32, DT = D / 32, PSTEPS = BN / 16;
+  constexpr int KCOPIES = G::KBYTES / 1024 / NW;
+  constexpr int VCOPIES = G::VBYTES / 1024 / NW;
+  constexpr int PER_TILE = KCOPIES + VCOPIES;
+  constexpr int LEAD = STAGES - 2;               // tiles copied ahead of the block that first reads them
+  static_assert(KCOPIES * NW * 1024 == G::KBYTES && VCOPIES * NW * 1024 == G::VBYTES, "copy split");
+  static_assert(STAGES >= 3 && (LEAD - 1) * PER_TILE <= 63, "pipeline depth");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * G::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int n_work = p.B * p.H * p.q_tiles * p.kv_splits;
+  const int work = xcd_remap(blockIdx.x, n_work);
+  const int qt = work % p.q_tiles;
+  const int rest = work / p.q_tiles;
+  const int split = rest % p.kv_splits;
+  const int bh = rest / p.kv_splits;
+  const int t_begin = static_cast<int>((static_cast<int64_t>(split) * p.key_tiles) / p.kv_splits);
+  const int t_end = static_cast<int>((static_cast<int64_t>(split + 1) * p.key_tiles) / p.kv_splits);
+  const int n = t_end - t_begin;
+  const int n_keys = p.n_keys;
+
+  const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
+  const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
+
+  const int q = qt * BM + wave * 32 + l32;
+  bf16x8 bq[KSTEPS];
+  {
+    const int qrow = min(q, p.Nc - 1);
+    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
+  }
+
+  auto k_src = [&](int c) {
+    const int P = (c * NW + wave) * 64 + lane;
+    const int r = P / G::KC;
+    return swap_bits23(r) * G::KROW + swz(P % G::KC, r, G::KC) * 16;
+  };
+  auto v_src = [&](int c) {
+    const int P = (c * NW + wave) * 64 + lane;
+    const int d = P / G::VC;
+    return d * p.key_stride * 2 + swz(P % G::VC, d, G::VC) * 16;
+  };
+  auto issue_tile = [&](int i) {
+    const int key0 = (t_begin + i) * BN;
+    char* dst = smem + (i % STAGES) * G::BUF;
+#pragma unroll
+    for (int c = 0; c < KCOPIES; ++c)
+      __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key0) * G::KROW + k_src(c),
+                                       dst + (c * NW + wave) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int c = 0; c < VCOPIES; ++c)
+      __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src(c),
+                                       dst + G::KBYTES + (c * NW + wave) * 1024, 16, 0, 0);
+  };
+  const int ka_row = l32 * G::KROW;
+  auto ka = [&](int s) { return ka_row + swz(2 * s + g, l32, G::KC) * 16; };
+  auto va = [&](int s) { return G::KBYTES + l32 * G::VROW + swz(2 * s + g, l32, G::VC) * 16; };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
+  float m = -__builtin_inff(), l = 0.f;
+  f32x16 sa[MT], sb[MT];
+  bf16x8 pa[PSTEPS], pb[PSTEPS];
+
+  // scores of tile i into acc (zeroed here)
+  auto qk = [&](int i, f32x16 (&acc)[MT]) {
+    const char* ks = smem + (i % STAGES) * G::BUF;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ka(s) + mt * 32 * G::KROW);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc[mt], 0, 0, 0);
+      }
+  };
+  auto pv = [&](int i, const bf16x8 (&pp)[PSTEPS]) {
+    const char* vs = smem + (i % STAGES) * G::BUF;
+#pragma unroll
+    for (int s = 0; s < PSTEPS; ++s)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + va(s) + dt * 32 * G::VROW);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[s], o[dt], 0, 0, 0);
+      }
+  };
+  // exponentiate tile i's scores against reference mr; returns the row-sum partial
+  auto expo = [&](const f32x16 (&sc)[MT], bf16x8 (&pp)[PSTEPS], float mr) {
+    float rs = 0.f;
+#pragma unroll
+    for (int s = 0; s < PSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + e], p.scale_log2, -mr));
+        rs += v;
+        pp[s][e] = static_cast<__bf16>(v);
+      }
+    return rs;
+  };
+  auto mask_tail = [&](int i, f32x16 (&sc)[MT]) {
+    const int key0 = (t_begin + i) * BN;
+    if (key0 + BN > n_keys) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys) sc[mt][j] = -__builtin_inff();
+    }
+  };
+  auto rowmax = [&](const f32x16 (&sc)[MT]) {
+    float mx = sc[0][0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[mt][j]);
+    return fmaxf(mx, xor32(mx)) * p.scale_log2;
+  };
+
+  auto wait_and_sync = [&](int i) {              // copies of tile i have landed in every wave
+    if (i + 1 < n && LEAD > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((LEAD - 1) * PER_TILE));
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // Block X(i): QK(i+1) -> snext, PV(i-1) <- pprev, softmax(i): scur -> pcur.
+  auto block = [&](int i, f32x16 (&scur)[MT], f32x16 (&snext)[MT], bf16x8 (&pprev)[PSTEPS],
+                   bf16x8 (&pcur)[PSTEPS]) {
+    if (i + 1 < n) wait_and_sync(i + 1);         // K of tile i+1 is read below
+    else __syncthreads();
+    if (i + LEAD + 1 < n) issue_tile(i + LEAD + 1);
+    mask_tail(i, scur);
+    const float mx = rowmax(scur);
+    const bool grow = mx > m + kRescaleThreshold;
+    const float rs = expo(scur, pcur, m);        // fast path against the current reference
+    if (i + 1 < n) qk(i + 1, snext);
+    if (i >= 1) pv(i - 1, pprev);
+#pragma unroll
+    for (int k = 0; k < KSTEPS * MT; ++k) {      // MFMA : VALU : LDS-read interleave
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+    if (__any(grow)) {                           // rare: raise the reference, rescale O, redo P(i)
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l = l * alpha + expo(scur, pcur, m);
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] *= alpha;
+    } else {
+      l += rs;
+    }
+  };
+
+  for (int i = 0; i <= LEAD && i < n; ++i) issue_tile(i);
+  wait_and_sync(0);
+  qk(0, sa);                                     // X(-1)
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    block(i, sa, sb, pb, pa);
+    block(i + 1, sb, sa, pa, pb);
+  }
+  if (i < n) {                                   // odd n: last block, scores in sa
+    block(i, sa, sb, pb, pa);
+    __syncthreads();
+    pv(i, pa);                                   // X(n)
+  } else {
+    __syncthreads();
+    pv(n - 1, pb);
+  }
 
   // ---- epilogue ---------------------------------------------------------------
   const float l_tot = l + xor32(l);
@@ -717,10 +1015,56 @@ __global__ __launch_bounds__(kThreads) void attn_combine(CombineParams p) {
   if (p.lse != nullptr && g4 == 0) p.lse[rq] = (mx + __log2f(wsum)) * kLn2;
 }
 
+// Merge the stream-K partials of one q-tile (block u): slots of the workgroups
+// whose ranges cut it; unsplit q-tiles were written directly and are skipped.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_sk_combine(AttnParams p) {
+  const int u = blockIdx.x;
+  const int G = p.sk_groups, T_ = p.key_tiles, BM = p.q_rows_per_block;
+  const int64_t L = static_cast<int64_t>(p.B) * p.H * p.q_tiles * T_;
+  const int64_t first = static_cast<int64_t>(u) * T_, last = first + T_ - 1;
+  const int w0 = static_cast<int>(((first + 1) * G + L - 1) / L - 1);   // workgroup holding iteration first
+  const int w1 = static_cast<int>(((last + 1) * G + L - 1) / L - 1);
+  if (w0 == w1) return;
+  const int bh = u / p.q_tiles, qt = u % p.q_tiles;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int groups = p.D / 4;
+  for (int idx = threadIdx.x; idx < BM * groups; idx += kThreads) {
+    const int r = idx / groups, c4 = idx - r * groups;
+    const int q = qt * BM + r;
+    if (q >= p.Nc) break;                        // rows are visited in increasing order
+    float mx = -__builtin_inff();
+    for (int w = w0; w <= w1; ++w) {
+      const int slot = 2 * w + (sk_start(w, L, G) < first ? 1 : 0);
+      mx = fmaxf(mx, p.sk_part_lse[static_cast<size_t>(slot) * BM + r]);
+    }
+    float wsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int w = w0; w <= w1; ++w) {
+      const size_t row = static_cast<size_t>(2 * w + (sk_start(w, L, G) < first ? 1 : 0)) * BM + r;
+      const float wt = fast_exp2(p.sk_part_lse[row] - mx);
+      const float4 v = *reinterpret_cast<const float4*>(p.sk_part_o + row * p.D + 4 * c4);
+      wsum += wt;
+      acc.x = fmaf(wt, v.x, acc.x);
+      acc.y = fmaf(wt, v.y, acc.y);
+      acc.z = fmaf(wt, v.z, acc.z);
+      acc.w = fmaf(wt, v.w, acc.w);
+    }
+    const float inv = 1.f / wsum;
+    T* dst = static_cast<T*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * p.D + 4 * c4;
+    dst[0] = static_cast<T>(acc.x * inv);
+    dst[1] = static_cast<T>(acc.y * inv);
+    dst[2] = static_cast<T>(acc.z * inv);
+    dst[3] = static_cast<T>(acc.w * inv);
+    if (p.lse != nullptr && c4 == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = (mx + __log2f(wsum)) * kLn2;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st) {
-  const int64_t n_work = static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
+  const int64_t n_work =
+      p.sk_groups > 0 ? p.sk_groups : static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
   if (n_work <= 0) return hipSuccess;
   if (dtype == 1) {
     if (p.variant == 3) {
@@ -735,6 +1079,13 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
     if (p.D == 128) hipLaunchKernelGGL(chunk_attention_f32<128>, dim3(n_work), dim3(64), 0, st, p);
     else hipLaunchKernelGGL(chunk_attention_f32<64>, dim3(n_work), dim3(64), 0, st, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st) {
+  const int n_qt = p.B * p.H * p.q_tiles;
+  if (n_qt <= 0 || p.sk_groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_sk_combine<__bf16>, dim3(n_qt), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

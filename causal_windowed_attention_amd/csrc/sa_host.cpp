@@ -35,6 +35,7 @@ using sa::RopeWriteParams;
 
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxPosition = 1 << 30;   // guard against int32 overflow when max_t == 0
+constexpr int kSkGroups = 256;              // persistent workgroups of the stream-K schedule (one per CU)
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -43,8 +44,8 @@ struct Derived {
   int32_t key_stride, q_tiles, max_splits;
   double theta;
   float scale;
-  size_t k_off, k_bytes, vt_off, vt_bytes, q_off, q_bytes, part_off, part_bytes, tab_off, tab_bytes,
-      total;
+  size_t k_off, k_bytes, vt_off, vt_bytes, q_off, q_bytes, part_off, part_bytes, sk_off, sk_bytes, tab_off,
+      tab_bytes, total;
 };
 
 sa_status derive(const sa_config* c, Derived* d) {
@@ -102,12 +103,17 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->part_bytes = d->max_splits > 1
                       ? static_cast<size_t>(d->max_splits) * bh * d->Nc * (static_cast<size_t>(d->D) + 1) * 4
                       : 0;
+  // stream-K partials: 2 slots per persistent workgroup, BlockM rows of D + 1 floats
+  d->sk_bytes = d->dtype == SA_BF16
+                    ? static_cast<size_t>(2 * kSkGroups) * sa::kBf16BlockMWide * (static_cast<size_t>(d->D) + 1) * 4
+                    : 0;
   d->tab_bytes = (static_cast<size_t>(d->Hf) * (d->dh / 2) + static_cast<size_t>(d->Wf) * (d->dw / 2)) * 8;
   size_t off = 0;
   d->k_off = off; off = align_up(off + d->k_bytes, kAlign);
   d->vt_off = off; off = align_up(off + d->vt_bytes, kAlign);
   d->q_off = off; off = align_up(off + d->q_bytes, kAlign);
   d->part_off = off; off = align_up(off + d->part_bytes, kAlign);
+  d->sk_off = off; off = align_up(off + d->sk_bytes, kAlign);
   d->tab_off = off; off = align_up(off + d->tab_bytes, kAlign);
   d->total = off;
   return SA_OK;
@@ -141,6 +147,8 @@ struct sa_stream {
   int32_t last_q_tiles = 0, last_kv_splits = 0, last_key_tiles = 0, last_delta = 0;
   int32_t kv_splits_opt = 0;
   int32_t variant_opt = 0;
+  int32_t schedule_opt = 0;
+  int32_t last_sk_groups = 0;
   bool profile = false;
   Prof prof[SA_K_COUNT];
 
@@ -255,6 +263,19 @@ int choose_splits(const sa_stream* s, int key_tiles, int q_tiles) {
   if (splits > key_tiles) splits = key_tiles;
   if (splits < 1) splits = 1;
   return splits;
+}
+
+// Stream-K (ping-pong kernel only): persistent workgroups sharing the
+// (q-tile, key-tile) iterations evenly, when one workgroup per q-tile would
+// leave part of the chip idle in the last round. 0 = grid schedule.
+int choose_stream_k(const sa_stream* s, int key_tiles, int q_tiles) {
+  const Derived& d = s->d;
+  if (attn_variant(s) != 3 || s->kv_splits_opt > 0 || s->schedule_opt == 1) return 0;
+  const int64_t n_qt = static_cast<int64_t>(d.B) * d.H * q_tiles;
+  const int64_t L = n_qt * key_tiles;
+  if (L < 2 * kSkGroups) return 0;               // too little work to share
+  if (s->schedule_opt == 2) return kSkGroups;
+  return (n_qt % kSkGroups) != 0 ? kSkGroups : 0;
 }
 
 void commit_meta(sa_stream* s) {
@@ -395,7 +416,8 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
   const int key_tiles = (n_keys + bn - 1) / bn;
   const int bm = attn_block_m(s);
   const int q_tiles = (d.Nc + bm - 1) / bm;
-  const int splits = choose_splits(s, key_tiles, q_tiles);
+  const int sk_groups = choose_stream_k(s, key_tiles, q_tiles);
+  const int splits = sk_groups > 0 ? 1 : choose_splits(s, key_tiles, q_tiles);
 
   if (!s->planning()) {
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -428,8 +450,15 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
     ap.kv_splits = splits;
     ap.key_tiles = key_tiles;
     ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    ap.sk_groups = sk_groups;
+    ap.sk_part_o = reinterpret_cast<float*>(s->ws + d.sk_off);
+    ap.sk_part_lse = ap.sk_part_o + static_cast<size_t>(2 * kSkGroups) * sa::kBf16BlockMWide * d.D;
     st = timed(s, SA_K_CHUNK_ATTENTION, hs, [&] { return sa::launch_chunk_attention(ap, d.dtype, hs); });
     if (st != SA_OK) return st;
+    if (sk_groups > 0) {
+      st = timed(s, SA_K_ATTN_COMBINE, hs, [&] { return sa::launch_attn_sk_combine(ap, hs); });
+      if (st != SA_OK) return st;
+    }
     if (splits > 1) {
       CombineParams cp;
       cp.part_o = ap.part_o;
@@ -445,6 +474,7 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
   s->staged_t = s->t_next;
   s->staged_slot = slot;
   s->last_q_tiles = q_tiles;
+  s->last_sk_groups = sk_groups;
   s->last_kv_splits = splits;
   s->last_key_tiles = key_tiles;
   return SA_OK;
@@ -575,6 +605,7 @@ sa_status sa_stream_query(const sa_stream* s, sa_state* out) {
   st.last_kv_splits = s->last_kv_splits;
   st.last_key_tiles = s->last_key_tiles;
   st.last_delta = s->last_delta;
+  st.last_sk_groups = s->last_sk_groups;
   *out = st;
   return SA_OK;
 }
@@ -630,6 +661,10 @@ sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value) {
     case SA_OPT_ATTN_VARIANT:
       if (value < 0 || value > 3) return SA_ERR_INVALID_ARGUMENT;
       s->variant_opt = static_cast<int32_t>(value);
+      return SA_OK;
+    case SA_OPT_SCHEDULE:
+      if (value < 0 || value > 2) return SA_ERR_INVALID_ARGUMENT;
+      s->schedule_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_PROFILE:
       if (value != 0 && value != 1) return SA_ERR_INVALID_ARGUMENT;

@@ -77,7 +77,12 @@ struct AttnParams {
   int32_t kv_splits;    // >= 1
   int32_t key_tiles;    // ceil(n_keys / BlockN)
   float scale_log2;     // softmax_scale * log2(e)
+  int32_t sk_groups;    // > 0: stream-K schedule with this many persistent workgroups (variant 3)
+  float* sk_part_o;     // [2 * sk_groups][BlockM][D] stream-K partial outputs
+  float* sk_part_lse;   // [2 * sk_groups][BlockM] stream-K partial log2-sum-exp
 };
+
+constexpr int kMaxSkGroups = 512;
 
 struct CombineParams {
   const float* part_o;
@@ -94,5 +99,6 @@ hipError_t launch_sink_update(const RopeWriteParams& p, int dtype, hipStream_t s
 hipError_t launch_rope_refresh(const RefreshParams& p, int dtype, hipStream_t st);
 hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st);
 hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st);
+hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st);
 
 }  // namespace sa

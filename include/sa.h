@@ -122,6 +122,8 @@ typedef struct sa_state {
   int32_t last_kv_splits;   /* ... key-range splits per query tile (1 = no combine pass) */
   int32_t last_key_tiles;   /* ... key tiles per query tile, summed over splits          */
   int32_t last_delta;       /* Delta applied by the last sa_rope_refresh                 */
+  int32_t last_sk_groups;   /* attend launch plan: persistent stream-K workgroups (0: grid) */
+  int32_t reserved;
 } sa_state;
 
 /* What a physical cache slot holds. */
@@ -159,9 +161,13 @@ typedef enum sa_kernel_id {
 typedef enum sa_option {
   SA_OPT_KV_SPLITS = 0,     /* 0: automatic; n >= 1: force n key-range splits per query tile */
   SA_OPT_PROFILE = 1,       /* 1: record HIP events around every launch (sa_profile_read)    */
-  SA_OPT_ATTN_VARIANT = 2   /* bf16 attention kernel: 0 automatic (3), 1 = 4 waves x 32
+  SA_OPT_ATTN_VARIANT = 2,  /* bf16 attention kernel: 0 automatic (3), 1 = 4 waves x 32
                                query rows, 2 = 4 waves x 64 rows, 3 = 8 waves x 32 rows with
                                a ping-pong MFMA/softmax schedule                             */
+  SA_OPT_SCHEDULE = 3       /* variant 3 work distribution: 0 automatic, 1 = one workgroup per
+                               (b, h, q-tile, split), 2 = stream-K (persistent workgroups
+                               sharing the q-tile x key-tile iterations evenly, partial tiles
+                               merged by a combine pass)                                     */
 } sa_option;
 
 typedef struct sa_stream sa_stream;

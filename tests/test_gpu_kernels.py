@@ -267,3 +267,34 @@ def test_profiler_counts_launches():
     assert n == 3
     assert s.profile_read(cwa.SA_K_KV_APPEND) == (0.0, 0)
     s.close()
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_stream_k_schedule(D):
+    """Stream-K: 256 persistent workgroups share the q-tile x key-tile iterations;
+    here every q-tile is cut across several workgroups, so the partial merge runs
+    for all of them. Compared with the oracle and with the grid schedule."""
+    w = synth.small_variant(SMALL, name=f"streamk{D}", head_dim=D, frame_h=10, frame_w=10,
+                            frames_per_chunk=3, batch=2, heads=8, window_chunks=3)
+    say("stream-K", D, "Nc", w.tokens_per_chunk)
+    s, hist = _steady_stream(w, 5)
+    q, k, v = synth.chunk_qkv(w, 5)
+    want, want_lse = hist.attend(q, k, v)
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    outs = {}
+    for sched in (1, 2):
+        s.set_option(cwa.SA_OPT_ATTN_VARIANT, 3)
+        s.set_option(cwa.SA_OPT_SCHEDULE, sched)
+        lse = torch.empty((w.batch, w.heads, w.tokens_per_chunk), dtype=torch.float32, device="cuda")
+        out = s.chunk_attend(qd, kd, vd, lse=lse)
+        torch.cuda.synchronize()
+        st = s.query()
+        assert (st["last_sk_groups"] > 0) == (sched == 2), st
+        a, r = err(host(out), want)
+        la, _ = err(host(lse), want_lse)
+        say(f"  schedule {sched}: sk_groups {st['last_sk_groups']} max {a:.2e} rel {r:.2e} lse {la:.2e}")
+        assert a <= BF16_ABS and r <= BF16_REL and la <= BF16_ABS
+        outs[sched] = host(out)
+    a, _ = err(outs[2], outs[1])
+    assert a <= 1e-2, a
+    s.close()

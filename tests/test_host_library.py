@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 def test_struct_sizes_match_header():
     import ctypes
     assert ctypes.sizeof(L.sa_config) == 64
-    assert ctypes.sizeof(L.sa_state) == 16 + 12 * 4
+    assert ctypes.sizeof(L.sa_state) == 16 + 14 * 4
     assert ctypes.sizeof(L.sa_slot_info) == 16
 
 

@@ -68,6 +68,21 @@ __device__ __forceinline__ int swz(int c, int r, int chunks) {
   return chunks >= 16 ? (c ^ (r & 15)) : chunks == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
+// Raw buffer resource over the `bytes` bytes at `base` (gfx9 word 3: untyped
+// dwords); a lane whose offset lies past the end reads zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voffset into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds). The MUBUF form matters: with the FLAT-encoded
+// global_load_lds in flight the compiler can only wait for lgkmcnt(0) before
+// any LDS read result, which serialises the MFMA operand reads behind the
+// newest one; buffer loads count in vmcnt alone.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, int voffset, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
 // Swap bits 2 and 3 of a tile row index (an involution).
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -81,7 +96,7 @@ __device__ __forceinline__ int swap_bits23(int r) {
 // 16 distinct bank groups: chunk c of a 256-byte row r sits at c ^ (r & 15),
 // chunk c of a 128-byte row r (two rows per 256-byte bank window) at
 // c ^ ((r >> 1) & 7). Tiles are copied global -> LDS directly
-// (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at LDS base +
+// (buffer_load_dwordx4 ... lds: lane i of a wave writes the 16 bytes at LDS base +
 // 16 i), choosing each lane's source so that the chunk lands at its swizzled
 // place; no VGPR staging, no LDS write instructions.
 template <int D, int BN_ = kBf16BlockN>
@@ -104,7 +119,7 @@ struct Bf16Geom {
 constexpr float kRescaleThreshold = 8.0f;
 
 #ifndef PP_READ_AHEAD
-#define PP_READ_AHEAD 1
+#define PP_READ_AHEAD 2
 #endif
 
 // Kernel shape parameters:
@@ -174,19 +189,19 @@ __device__ __forceinline__ void chunk_attention_bf16_body(const AttnParams& p) {
     const int d = P / G::VC, c = swz(P % G::VC, d, G::VC);
     v_src[i] = d * p.key_stride * 2 + c * 16;
   }
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, p.k_bh_stride * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, p.vt_bh_stride * 2);
   auto issue_tile = [&](int t, int buf) {
     const int key0 = t * BN;
     char* dst = smem + buf * G::BUF;
 #pragma unroll
     for (int i = 0; i < KCOPIES; ++i) {
       const int key = min(key0 + k_row[i], n_keys - 1);   // rows past the range: any finite row
-      __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key) * G::KROW + k_src[i],
-                                       dst + (i * NW + wave) * 1024, 16, 0, 0);
+      lds_copy16(krs, key * G::KROW + k_src[i], dst + (i * NW + wave) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < VCOPIES; ++i)
-      __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src[i],
-                                       dst + G::KBYTES + (i * NW + wave) * 1024, 16, 0, 0);
+      lds_copy16(vrs, key0 * 2 + v_src[i], dst + G::KBYTES + (i * NW + wave) * 1024);
   };
 
   // ---- MFMA operand read addresses -----------------------------------------
@@ -418,17 +433,15 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
     const int d = P / G::VC;
     return d * p.key_stride * 2 + swz(P % G::VC, d, G::VC) * 16;
   };
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, p.k_bh_stride * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, p.vt_bh_stride * 2);
   auto issue_tile = [&](int i) {                 // tile t_begin + i into stage i % STAGES
     const int key0 = (t_begin + i) * BN;
     char* dst = smem + (i % STAGES) * G::BUF;
 #pragma unroll
-    for (int c = 0; c < KCOPIES; ++c)
-      __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key0) * G::KROW + k_src(c),
-                                       dst + (c * NW + wave) * 1024, 16, 0, 0);
+    for (int c = 0; c < KCOPIES; ++c) lds_copy16(krs, key0 * G::KROW + k_src(c), dst + (c * NW + wave) * 1024);
 #pragma unroll
-    for (int c = 0; c < VCOPIES; ++c)
-      __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src(c),
-                                       dst + G::KBYTES + (c * NW + wave) * 1024, 16, 0, 0);
+    for (int c = 0; c < VCOPIES; ++c) lds_copy16(vrs, key0 * 2 + v_src(c), dst + G::KBYTES + (c * NW + wave) * 1024);
   };
 
   // K operand address of k-step s: row l32, swizzled chunk of logical chunk 2s + g,
@@ -655,236 +668,6 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
   }
 }
 
-// Software-pipelined schedule, 8 waves x 32 query rows (BM = 256), two waves
-// per SIMD. Block X(i) of every wave holds three independent streams:
-//   QK(i+1) MFMAs -> S_next,  PV(i-1) MFMAs <- P_prev,  softmax(i) VALU: S_cur -> P_cur,
-// interleaved by scheduling barriers so each wave keeps the matrix pipe fed
-// while its softmax runs; S and P are double-buffered (the loop is unrolled by
-// two so the buffers swap roles without copies). A block needs K of tile i+1
-// and V of tile i-1, so a tile occupies its LDS stage for three blocks; copies
-// for tile i+STAGES-2 are issued at the start of X(i). The O rescale (rare,
-// when a row maximum grows by more than 2^8) runs after the block's PV MFMAs,
-// and then recomputes P(i) with the new reference.
-template <int D, int STAGES, int BNT>
-__device__ __forceinline__ void chunk_attention_bf16_pl_body(const AttnParams& p) {
-  using G = Bf16Geom<D, BNT>;
-  constexpr int NW = 8;
-  constexpr int BN = G::BN;
-  constexpr int BM = NW * 32;
-  constexpr int KSTEPS = D / 16, MT = BN / 32, DT = D / 32, PSTEPS = BN / 16;
-  constexpr int KCOPIES = G::KBYTES / 1024 / NW;
-  constexpr int VCOPIES = G::VBYTES / 1024 / NW;
-  constexpr int PER_TILE = KCOPIES + VCOPIES;
-  constexpr int LEAD = STAGES - 2;               // tiles copied ahead of the block that first reads them
-  static_assert(KCOPIES * NW * 1024 == G::KBYTES && VCOPIES * NW * 1024 == G::VBYTES, "copy split");
-  static_assert(STAGES >= 3 && (LEAD - 1) * PER_TILE <= 63, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * G::BUF];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g = lane >> 5;
-
-  const int n_work = p.B * p.H * p.q_tiles * p.kv_splits;
-  const int work = xcd_remap(blockIdx.x, n_work);
-  const int qt = work % p.q_tiles;
-  const int rest = work / p.q_tiles;
-  const int split = rest % p.kv_splits;
-  const int bh = rest / p.kv_splits;
-  const int t_begin = static_cast<int>((static_cast<int64_t>(split) * p.key_tiles) / p.kv_splits);
-  const int t_end = static_cast<int>((static_cast<int64_t>(split + 1) * p.key_tiles) / p.kv_splits);
-  const int n = t_end - t_begin;
-  const int n_keys = p.n_keys;
-
-  const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
-  const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
-
-  const int q = qt * BM + wave * 32 + l32;
-  bf16x8 bq[KSTEPS];
-  {
-    const int qrow = min(q, p.Nc - 1);
-    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
-  }
-
-  auto k_src = [&](int c) {
-    const int P = (c * NW + wave) * 64 + lane;
-    const int r = P / G::KC;
-    return swap_bits23(r) * G::KROW + swz(P % G::KC, r, G::KC) * 16;
-  };
-  auto v_src = [&](int c) {
-    const int P = (c * NW + wave) * 64 + lane;
-    const int d = P / G::VC;
-    return d * p.key_stride * 2 + swz(P % G::VC, d, G::VC) * 16;
-  };
-  auto issue_tile = [&](int i) {
-    const int key0 = (t_begin + i) * BN;
-    char* dst = smem + (i % STAGES) * G::BUF;
-#pragma unroll
-    for (int c = 0; c < KCOPIES; ++c)
-      __builtin_amdgcn_global_load_lds(kbase + static_cast<size_t>(key0) * G::KROW + k_src(c),
-                                       dst + (c * NW + wave) * 1024, 16, 0, 0);
-#pragma unroll
-    for (int c = 0; c < VCOPIES; ++c)
-      __builtin_amdgcn_global_load_lds(vbase + static_cast<size_t>(key0) * 2 + v_src(c),
-                                       dst + G::KBYTES + (c * NW + wave) * 1024, 16, 0, 0);
-  };
-  const int ka_row = l32 * G::KROW;
-  auto ka = [&](int s) { return ka_row + swz(2 * s + g, l32, G::KC) * 16; };
-  auto va = [&](int s) { return G::KBYTES + l32 * G::VROW + swz(2 * s + g, l32, G::VC) * 16; };
-
-  f32x16 o[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
-  float m = -__builtin_inff(), l = 0.f;
-  f32x16 sa[MT], sb[MT];
-  bf16x8 pa[PSTEPS], pb[PSTEPS];
-
-  // scores of tile i into acc (zeroed here)
-  auto qk = [&](int i, f32x16 (&acc)[MT]) {
-    const char* ks = smem + (i % STAGES) * G::BUF;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ka(s) + mt * 32 * G::KROW);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc[mt], 0, 0, 0);
-      }
-  };
-  auto pv = [&](int i, const bf16x8 (&pp)[PSTEPS]) {
-    const char* vs = smem + (i % STAGES) * G::BUF;
-#pragma unroll
-    for (int s = 0; s < PSTEPS; ++s)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + va(s) + dt * 32 * G::VROW);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[s], o[dt], 0, 0, 0);
-      }
-  };
-  // exponentiate tile i's scores against reference mr; returns the row-sum partial
-  auto expo = [&](const f32x16 (&sc)[MT], bf16x8 (&pp)[PSTEPS], float mr) {
-    float rs = 0.f;
-#pragma unroll
-    for (int s = 0; s < PSTEPS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + e], p.scale_log2, -mr));
-        rs += v;
-        pp[s][e] = static_cast<__bf16>(v);
-      }
-    return rs;
-  };
-  auto mask_tail = [&](int i, f32x16 (&sc)[MT]) {
-    const int key0 = (t_begin + i) * BN;
-    if (key0 + BN > n_keys) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys) sc[mt][j] = -__builtin_inff();
-    }
-  };
-  auto rowmax = [&](const f32x16 (&sc)[MT]) {
-    float mx = sc[0][0];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[mt][j]);
-    return fmaxf(mx, xor32(mx)) * p.scale_log2;
-  };
-
-  auto wait_and_sync = [&](int i) {              // copies of tile i have landed in every wave
-    if (i + 1 < n && LEAD > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((LEAD - 1) * PER_TILE));
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
-  // Block X(i): QK(i+1) -> snext, PV(i-1) <- pprev, softmax(i): scur -> pcur.
-  auto block = [&](int i, f32x16 (&scur)[MT], f32x16 (&snext)[MT], bf16x8 (&pprev)[PSTEPS],
-                   bf16x8 (&pcur)[PSTEPS]) {
-    if (i + 1 < n) wait_and_sync(i + 1);         // K of tile i+1 is read below
-    else __syncthreads();
-    if (i + LEAD + 1 < n) issue_tile(i + LEAD + 1);
-    mask_tail(i, scur);
-    const float mx = rowmax(scur);
-    const bool grow = mx > m + kRescaleThreshold;
-    const float rs = expo(scur, pcur, m);        // fast path against the current reference
-    if (i + 1 < n) qk(i + 1, snext);
-    if (i >= 1) pv(i - 1, pprev);
-#pragma unroll
-    for (int k = 0; k < KSTEPS * MT; ++k) {      // MFMA : VALU : LDS-read interleave
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-    }
-    if (__any(grow)) {                           // rare: raise the reference, rescale O, redo P(i)
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      l = l * alpha + expo(scur, pcur, m);
-#pragma unroll
-      for (int d = 0; d < DT; ++d) o[d] *= alpha;
-    } else {
-      l += rs;
-    }
-  };
-
-  for (int i = 0; i <= LEAD && i < n; ++i) issue_tile(i);
-  wait_and_sync(0);
-  qk(0, sa);                                     // X(-1)
-  int i = 0;
-  for (; i + 1 < n; i += 2) {
-    block(i, sa, sb, pb, pa);
-    block(i + 1, sb, sa, pa, pb);
-  }
-  if (i < n) {                                   // odd n: last block, scores in sa
-    block(i, sa, sb, pb, pa);
-    __syncthreads();
-    pv(i, pa);                                   // X(n)
-  } else {
-    __syncthreads();
-    pv(n - 1, pb);
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
-  const float l_tot = l + xor32(l);
-  if (q >= p.Nc) return;
-  const float inv = 1.f / l_tot;
-  const float lse2 = m + __log2f(l_tot);
-  const int b = bh / p.H, h = bh - b * p.H;
-  if (p.kv_splits == 1) {
-    __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[dt][4 * jj + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
-      }
-    if (p.lse != nullptr && g == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
-  } else {
-    const size_t row = (static_cast<size_t>(split) * p.B * p.H + bh) * p.Nc + q;
-    float* dst = p.part_o + row * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
-            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
-                        o[dt][4 * jj + 3] * inv);
-    if (g == 0) p.part_lse[row] = lse2;
-  }
-}
-
 __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d128(AttnParams p) {
   chunk_attention_bf16_body<128, 4, 1, 2>(p);
 }
@@ -1019,29 +802,37 @@ __global__ __launch_bounds__(kThreads) void attn_combine(CombineParams p) {
 // whose ranges cut it; unsplit q-tiles were written directly and are skipped.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attn_sk_combine(AttnParams p) {
+  constexpr int kMaxParts = 16;                  // workgroups cutting one q-tile (checked on the host)
+  __shared__ int s_slot[kMaxParts];
+  __shared__ int s_n;
   const int u = blockIdx.x;
   const int G = p.sk_groups, T_ = p.key_tiles, BM = p.q_rows_per_block;
-  const int64_t L = static_cast<int64_t>(p.B) * p.H * p.q_tiles * T_;
-  const int64_t first = static_cast<int64_t>(u) * T_, last = first + T_ - 1;
-  const int w0 = static_cast<int>(((first + 1) * G + L - 1) / L - 1);   // workgroup holding iteration first
-  const int w1 = static_cast<int>(((last + 1) * G + L - 1) / L - 1);
-  if (w0 == w1) return;
+  if (threadIdx.x == 0) {
+    const int64_t L = static_cast<int64_t>(p.B) * p.H * p.q_tiles * T_;
+    const int64_t first = static_cast<int64_t>(u) * T_, last = first + T_ - 1;
+    const int w0 = static_cast<int>(((first + 1) * G + L - 1) / L - 1);   // workgroup holding iteration first
+    const int w1 = static_cast<int>(((last + 1) * G + L - 1) / L - 1);
+    int n = 0;
+    if (w0 != w1)
+      for (int w = w0; w <= w1 && n < kMaxParts; ++w) s_slot[n++] = 2 * w + (sk_start(w, L, G) < first ? 1 : 0);
+    s_n = n;
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (n == 0) return;                            // unsplit: written by the attention kernel
   const int bh = u / p.q_tiles, qt = u % p.q_tiles;
   const int b = bh / p.H, h = bh - b * p.H;
   const int groups = p.D / 4;
-  for (int idx = threadIdx.x; idx < BM * groups; idx += kThreads) {
+  const int rows = min(BM, p.Nc - qt * BM);
+  for (int idx = threadIdx.x; idx < rows * groups; idx += kThreads) {
     const int r = idx / groups, c4 = idx - r * groups;
     const int q = qt * BM + r;
-    if (q >= p.Nc) break;                        // rows are visited in increasing order
     float mx = -__builtin_inff();
-    for (int w = w0; w <= w1; ++w) {
-      const int slot = 2 * w + (sk_start(w, L, G) < first ? 1 : 0);
-      mx = fmaxf(mx, p.sk_part_lse[static_cast<size_t>(slot) * BM + r]);
-    }
+    for (int j = 0; j < n; ++j) mx = fmaxf(mx, p.sk_part_lse[static_cast<size_t>(s_slot[j]) * BM + r]);
     float wsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int w = w0; w <= w1; ++w) {
-      const size_t row = static_cast<size_t>(2 * w + (sk_start(w, L, G) < first ? 1 : 0)) * BM + r;
+    for (int j = 0; j < n; ++j) {
+      const size_t row = static_cast<size_t>(s_slot[j]) * BM + r;
       const float wt = fast_exp2(p.sk_part_lse[row] - mx);
       const float4 v = *reinterpret_cast<const float4*>(p.sk_part_o + row * p.D + 4 * c4);
       wsum += wt;

@@ -88,6 +88,8 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->scale = c->softmax_scale == 0.f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->D)))
                                      : c->softmax_scale;
   d->key_stride = static_cast<int32_t>(align_up(static_cast<size_t>(keys), 64));
+  // bf16 tile copies address one (b, h) region through a buffer resource (32-bit offsets)
+  if (static_cast<int64_t>(d->key_stride) * d->D * d->elem >= (int64_t{1} << 31)) return SA_ERR_UNSUPPORTED;
   const int bm = d->dtype == SA_BF16 ? sa::kBf16BlockM : sa::kF32BlockM;
   d->q_tiles = (d->Nc + bm - 1) / bm;
   // partial buffers only where splitting can help filling the chip
@@ -274,8 +276,12 @@ int choose_stream_k(const sa_stream* s, int key_tiles, int q_tiles) {
   const int64_t n_qt = static_cast<int64_t>(d.B) * d.H * q_tiles;
   const int64_t L = n_qt * key_tiles;
   if (L < 2 * kSkGroups) return 0;               // too little work to share
-  if (s->schedule_opt == 2) return kSkGroups;
-  return (n_qt % kSkGroups) != 0 ? kSkGroups : 0;
+  // at most 16 workgroups may cut one q-tile (the combine pass's limit)
+  if (static_cast<int64_t>(key_tiles) * kSkGroups > 14 * L) return 0;
+  // Only on request: measured on a power-limited part, filling the idle CUs of a ragged
+  // last wave lowers the clock by about as much as it cuts cycles, and the combine pass
+  // then makes the whole slower.
+  return s->schedule_opt == 2 ? kSkGroups : 0;
 }
 
 void commit_meta(sa_stream* s) {

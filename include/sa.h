@@ -91,7 +91,9 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *  softmax_scale    0 selects 1/sqrt(D)
  *  dtype            SA_F32 or SA_BF16 (element type of q, k, v, out and the cache)
  * Limits: F * d_t / 2 <= SA_MAX_TEMPORAL_PAIRS; Nc = F*Hf*Wf <= 2^20;
- *         (S + W + 1) * Nc <= 2^24 keys.
+ *         (S + W + 1) * Nc <= 2^24 keys, and the cache of one (b, h) (keys
+ *         rounded up to 64, times D times the element size) below 2^31 bytes.
+ *         A config over a limit is SA_ERR_UNSUPPORTED.
  */
 typedef struct sa_config {
   int32_t batch, heads, head_dim, frame_h, frame_w, frames_per_chunk;
@@ -164,7 +166,7 @@ typedef enum sa_option {
   SA_OPT_ATTN_VARIANT = 2,  /* bf16 attention kernel: 0 automatic (3), 1 = 4 waves x 32
                                query rows, 2 = 4 waves x 64 rows, 3 = 8 waves x 32 rows with
                                a ping-pong MFMA/softmax schedule                             */
-  SA_OPT_SCHEDULE = 3       /* variant 3 work distribution: 0 automatic, 1 = one workgroup per
+  SA_OPT_SCHEDULE = 3       /* variant 3 work distribution: 0 automatic (1), 1 = one workgroup per
                                (b, h, q-tile, split), 2 = stream-K (persistent workgroups
                                sharing the q-tile x key-tile iterations evenly, partial tiles
                                merged by a combine pass)                                     */

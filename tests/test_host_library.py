@@ -183,6 +183,9 @@ def test_error_codes():
         (dict(rope_dims=(30, 20, 20)), L.SA_ERR_INVALID_ARGUMENT),
         (dict(rope_dims=(25, 20, 19)), L.SA_ERR_INVALID_ARGUMENT),
         (dict(frames_per_chunk=40, head_dim=128), L.SA_ERR_UNSUPPORTED),
+        # 9 slots x 2^20 keys x 128 x 2 bytes per (b, h) >= 2^31: past the 32-bit buffer range
+        (dict(frame_h=1024, frame_w=1024, frames_per_chunk=1, window_chunks=7, head_dim=128),
+         L.SA_ERR_UNSUPPORTED),
         (dict(dtype=7), L.SA_ERR_INVALID_ARGUMENT),
         (dict(rope_theta=0.5), L.SA_ERR_INVALID_ARGUMENT),
         (dict(max_t=1), L.SA_ERR_POSITION_RANGE),

@@ -56,69 +56,132 @@ __device__ __forceinline__ Vec16<T> rotate(const Vec16<T>& in, const float2 (&cs
   return out;
 }
 
+// Transpose of a VN x VN block held as VN 16-byte vectors: in[t] = token t's VN
+// channels, out[c] = channel c's VN tokens. bf16: each output dword packs the
+// same-parity halves of two input dwords (v_perm_b32); fp32: register renaming.
+template <typename T>
+__device__ __forceinline__ void transpose_block(const uint4 (&in)[16 / sizeof(T)], uint4 (&out)[16 / sizeof(T)]) {
+  constexpr int VN = 16 / sizeof(T);
+  auto dw = [](const uint4& v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; };
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                // channels 2k, 2k+1
+      unsigned lo[4], hi[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {           // tokens 2jj, 2jj+1
+        lo[jj] = __builtin_amdgcn_perm(dw(in[2 * jj + 1], k), dw(in[2 * jj], k), 0x05040100u);
+        hi[jj] = __builtin_amdgcn_perm(dw(in[2 * jj + 1], k), dw(in[2 * jj], k), 0x07060302u);
+      }
+      out[2 * k] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      out[2 * k + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < VN; ++c) out[c] = make_uint4(dw(in[0], c), dw(in[1], c), dw(in[2], c), dw(in[3], c));
+  }
+}
+
 // One block: 64 tokens of head blockIdx.y of stream blockIdx.z.
+//  * K (and Q): thread (tid % vpt) owns one 16-byte channel vector of tokens
+//    tid / vpt + j * (256 / vpt); all its loads are issued before any store.
+//  * V: thread owns a VN x VN (tokens x channels) block, transposes it in
+//    registers and stores VN 16-byte rows of V^T; lanes with consecutive token
+//    groups of one channel group write 128 contiguous bytes per channel row.
 template <typename T, bool HAS_Q>
 __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
   constexpr int VN = 16 / sizeof(T);             // elements per 16-byte vector
-  constexpr int LDS_STRIDE = kTileTokens + VN;   // padded row of the V^T tile
+  constexpr int MAXJ = 32 / VN;                  // K/Q vectors per thread (D <= 128)
   __shared__ float2 s_tcs[kMaxTemporalPairs];
-  __shared__ Vec16<T> s_vraw[128 * LDS_STRIDE / VN];
-  T* s_v = reinterpret_cast<T*>(s_vraw);
+  __shared__ int s_fyx[kTileTokens][3];          // (frame, y, x) of the tile's tokens
 
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * kTileTokens;
   const int h = blockIdx.y, b = blockIdx.z;
   const int ntab = p.n_frames * (p.dt >> 1);
   for (int i = tid; i < ntab; i += kThreads) s_tcs[i] = p.t_cs[i];
-  __syncthreads();
-
-  const int vpt = p.D / VN;                      // vectors per token row of one head
-  const int nvec = kTileTokens * vpt;
-  const int hw = p.Hf * p.Wf;
-  const size_t bh = static_cast<size_t>(b) * p.H + h;
-  const T* kin = static_cast<const T*>(p.k);
-  const T* vin = static_cast<const T*>(p.v);
-  T* kc = static_cast<T*>(p.kcache) + bh * p.k_bh_stride;
-
-  for (int i = tid; i < nvec; i += kThreads) {
-    const int tl = i / vpt;
-    const int c0 = (i - tl * vpt) * VN;
-    const int n = n0 + tl;
-    if (n >= p.n_tokens) continue;
-    const size_t in_off =
-        ((static_cast<size_t>(b) * p.in_tokens + p.in_tok0 + n) * p.H + h) * p.D + c0;
-    const int f = n / hw, rem = n - f * hw, y = rem / p.Wf, x = rem - y * p.Wf;
-    float2 cs[VN / 2];
-#pragma unroll
-    for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, p, c0 + 2 * e, f, y, x);
-
-    const Vec16<T> kv = *reinterpret_cast<const Vec16<T>*>(kin + in_off);
-    *reinterpret_cast<Vec16<T>*>(kc + static_cast<size_t>(p.row0 + n) * p.D + c0) = rotate<T>(kv, cs);
-    if constexpr (HAS_Q) {
-      const Vec16<T> qv = *reinterpret_cast<const Vec16<T>*>(static_cast<const T*>(p.q) + in_off);
-      T* qo = static_cast<T*>(p.qrot) + (bh * p.n_tokens + n) * p.D + c0;
-      *reinterpret_cast<Vec16<T>*>(qo) = rotate<T>(qv, cs);
-    }
-    const Vec16<T> vv = *reinterpret_cast<const Vec16<T>*>(vin + in_off);
-#pragma unroll
-    for (int e = 0; e < VN; ++e) s_v[(c0 + e) * LDS_STRIDE + tl] = vv.e[e];
+  if (tid < kTileTokens) {
+    const int n = min(n0 + tid, p.n_tokens - 1);
+    const int hw = p.Hf * p.Wf;
+    const int f = n / hw, rem = n - f * hw, y = rem / p.Wf;
+    s_fyx[tid][0] = f;
+    s_fyx[tid][1] = y;
+    s_fyx[tid][2] = rem - y * p.Wf;
   }
   __syncthreads();
 
-  // V^T rows: channel d holds this tile's tokens contiguously at keys row0 + n0 ...
+  const size_t bh = static_cast<size_t>(b) * p.H + h;
+  const T* __restrict__ kin = static_cast<const T*>(p.k);
+  const T* __restrict__ qin = static_cast<const T*>(p.q);
+  const T* __restrict__ vin = static_cast<const T*>(p.v);
+  T* __restrict__ kc = static_cast<T*>(p.kcache) + bh * p.k_bh_stride;
+  T* __restrict__ qo = static_cast<T*>(p.qrot) + bh * p.n_tokens * p.D;
+  T* __restrict__ vt = static_cast<T*>(p.vtcache) + bh * p.vt_bh_stride + p.row0 + n0;
+  auto in_off = [&](int n, int c) {
+    return ((static_cast<size_t>(b) * p.in_tokens + p.in_tok0 + n) * p.H + h) * p.D + c;
+  };
+
+  // ---- issue every load first: V blocks, then K (and Q) vectors ---------------
+  constexpr int TG = kTileTokens / VN;           // token groups per tile
+  constexpr int MAXB = (TG * 128 / VN + kThreads - 1) / kThreads;   // V blocks per thread (D <= 128)
+  const int nblk = TG * (p.D / VN);
   const int ntok = min(kTileTokens, p.n_tokens - n0);
-  T* vt = static_cast<T*>(p.vtcache) + bh * p.vt_bh_stride + p.row0 + n0;
-  if (ntok == kTileTokens && ((p.row0 + n0) % VN) == 0) {
-    constexpr int VPR = kTileTokens / VN;        // vectors per channel row
-    for (int i = tid; i < p.D * VPR; i += kThreads) {
-      const int d = i / VPR, c = i - d * VPR;
-      *reinterpret_cast<Vec16<T>*>(vt + static_cast<size_t>(d) * p.key_stride + c * VN) =
-          *reinterpret_cast<const Vec16<T>*>(s_v + d * LDS_STRIDE + c * VN);
+  uint4 vin_r[MAXB][VN];
+#pragma unroll
+  for (int r = 0; r < MAXB; ++r) {
+    const int blk = tid + r * kThreads;
+    const int t0 = (blk % TG) * VN, cb = (blk / TG) * VN;
+#pragma unroll
+    for (int t = 0; t < VN; ++t)
+      vin_r[r][t] = blk < nblk && t0 + t < ntok ? *reinterpret_cast<const uint4*>(vin + in_off(n0 + t0 + t, cb))
+                                                : make_uint4(0, 0, 0, 0);
+  }
+  const int vpt = p.D / VN;
+  const int tpp = kThreads / vpt;                // tokens per pass
+  const int passes = kTileTokens / tpp;          // <= MAXJ
+  const int c0 = (tid % vpt) * VN;
+  const int tl0 = tid / vpt;
+  Vec16<T> kv[MAXJ], qv[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int n = n0 + tl0 + j * tpp;
+    if (j < passes && n < p.n_tokens) {
+      kv[j] = *reinterpret_cast<const Vec16<T>*>(kin + in_off(n, c0));
+      if constexpr (HAS_Q) qv[j] = *reinterpret_cast<const Vec16<T>*>(qin + in_off(n, c0));
     }
-  } else {
-    for (int i = tid; i < p.D * ntok; i += kThreads) {
-      const int d = i / ntok, t = i - d * ntok;
-      vt[static_cast<size_t>(d) * p.key_stride + t] = s_v[d * LDS_STRIDE + t];
+  }
+
+  // ---- K (and Q): rotate 16-byte channel vectors ----------------------------
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int tl = tl0 + j * tpp, n = n0 + tl;
+    if (j < passes && n < p.n_tokens) {
+      float2 cs[VN / 2];
+#pragma unroll
+      for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, p, c0 + 2 * e, s_fyx[tl][0], s_fyx[tl][1], s_fyx[tl][2]);
+      *reinterpret_cast<Vec16<T>*>(kc + static_cast<size_t>(p.row0 + n) * p.D + c0) = rotate<T>(kv[j], cs);
+      if constexpr (HAS_Q) *reinterpret_cast<Vec16<T>*>(qo + static_cast<size_t>(n) * p.D + c0) = rotate<T>(qv[j], cs);
+    }
+  }
+
+  // ---- V: VN x VN register transposes straight into V^T ---------------------
+  const bool vec_ok = (p.row0 % VN) == 0;        // 16-byte aligned V^T rows
+#pragma unroll
+  for (int r = 0; r < MAXB; ++r) {
+    const int blk = tid + r * kThreads;
+    if (blk >= nblk) break;
+    const int t0 = (blk % TG) * VN, cb = (blk / TG) * VN;
+    uint4 out[VN];
+    transpose_block<T>(vin_r[r], out);
+    if (vec_ok && t0 + VN <= ntok) {
+#pragma unroll
+      for (int c = 0; c < VN; ++c)
+        *reinterpret_cast<uint4*>(vt + static_cast<size_t>(cb + c) * p.key_stride + t0) = out[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < VN; ++c) {
+        const T* e = reinterpret_cast<const T*>(&out[c]);
+        for (int t = 0; t < VN && t0 + t < ntok; ++t) vt[static_cast<size_t>(cb + c) * p.key_stride + t0 + t] = e[t];
+      }
     }
   }
 }

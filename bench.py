@@ -133,6 +133,26 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def probe_mfma(torch, cwa, blocks=512, iters=20000, reps=3):
+    """MFMA rate the part sustains on a pure v_mfma_f32_32x32x16_bf16 stream (fixed operands),
+    timed with events around the library's measurement kernel."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * iters * 8 * 32768.0
+    cwa.sa_probe_mfma_bf16(out, blocks, iters)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cwa.sa_probe_mfma_bf16(out, blocks, iters)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    tf = flops / (best * 1e-3) / 1e12
+    return {"tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS, "blocks": blocks, "iters": iters,
+            "operands": "fixed per lane (benign, low toggle)"}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -192,6 +212,16 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
     value = w.batch * nc * args.steps / dt
 
+    # ---- per-step GPU time distribution (events on the stream the library uses) ---
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
+
     # ---- per-kernel durations: HIP events on the launch stream ------------------
     s.set_option(cwa.SA_OPT_PROFILE, 1)
     for k_id in range(cwa.SA_K_COUNT):
@@ -215,6 +245,8 @@ def main():
         if n:
             kern[name] = ms / n
     s.set_option(cwa.SA_OPT_PROFILE, 0)
+
+    mfma_probe = probe_mfma(torch, cwa)
 
     nk = st["visible_keys"]
     flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk
@@ -274,6 +306,12 @@ def main():
         "attend_tokens_per_s": w.batch * nc / (attend_ms * 1e-3),
         "pct_bf16_peak_attend": flops / (attend_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stream_cold_start": {"chunks": w.n_chunks, "ms": stream_ms, "ms_per_chunk": stream_ms / w.n_chunks},
+        "step_ms": {"p50": pct(0.5), "p99": pct(0.99), "max": step_ms[-1], "n": len(step_ms)},
+        # a chunk of F latent frames must be produced within F frame periods; this layer's
+        # attention step is one of many inside that budget
+        "chunk_budget_ms": {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)},
+        "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
+        "mfma_probe": mfma_probe,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

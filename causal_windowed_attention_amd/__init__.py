@@ -25,7 +25,7 @@ __all__ = [
     "SaError", "make_config", "sa_status_string", "sa_config_check", "sa_workspace_bytes",
     "sa_stream_create", "sa_stream_destroy", "sa_chunk_attend", "sa_kv_append",
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
-    "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "Stream",
+    "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16", "Stream",
     "SA_F32", "SA_BF16", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
     "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
     "SA_K_ROPE_APPLY", "SA_K_CHUNK_ATTENTION", "SA_K_ATTN_COMBINE", "SA_K_KV_APPEND",
@@ -157,6 +157,11 @@ def sa_profile_read(handle, kernel_id: int, reset: bool = False) -> Tuple[float,
     _check(L.load().sa_profile_read(handle, kernel_id, ctypes.byref(ms), ctypes.byref(n),
                                     1 if reset else 0), "sa_profile_read")
     return ms.value, n.value
+
+
+def sa_probe_mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
+    """Launch the pure-MFMA measurement kernel (out: float32 device tensor of blocks*256)."""
+    _check(L.load().sa_probe_mfma_bf16(_ptr(out), blocks, iters, _stream_ptr(stream)), "sa_probe_mfma_bf16")
 
 
 class Stream:

@@ -85,6 +85,7 @@ SIGNATURES = {
     "sa_stream_set_option": (ctypes.c_int, [_P, _I32, _I64]),
     "sa_profile_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(_I64), _I32]),
+    "sa_probe_mfma_bf16": (ctypes.c_int, [_P, _I32, _I32, _P]),
 }
 
 _lib = None

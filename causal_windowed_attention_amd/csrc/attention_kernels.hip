@@ -851,6 +851,34 @@ __global__ __launch_bounds__(kThreads) void attn_sk_combine(AttnParams p) {
   }
 }
 
+// Measurement aid, not part of the attention path: 4 waves, each issuing
+// v_mfma_f32_32x32x16_bf16 on 8 independent accumulators (the issue pattern
+// that keeps one wave's matrix pipe full), `iters` rounds. Operands are fixed
+// per lane (benign data: few toggling bits). One launch performs
+// blocks * 4 * iters * 8 * 32768 flops; every lane writes one float.
+__global__ __launch_bounds__(kThreads) void mfma_probe_bf16(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(((lane * 7 + i) % 13) * 0.01f);
+    b[i] = static_cast<__bf16>(((lane * 5 + i) % 11) * 0.02f);
+  }
+  f32x16 c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c[j][i];
+  out[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st) {
@@ -870,6 +898,11 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
     if (p.D == 128) hipLaunchKernelGGL(chunk_attention_f32<128>, dim3(n_work), dim3(64), 0, st, p);
     else hipLaunchKernelGGL(chunk_attention_f32<64>, dim3(n_work), dim3(64), 0, st, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_probe_bf16, dim3(blocks), dim3(kThreads), 0, st, out, iters);
   return hipGetLastError();
 }
 

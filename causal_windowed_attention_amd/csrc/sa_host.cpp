@@ -703,4 +703,10 @@ sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int
   return SA_OK;
 }
 
+sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* stream) {
+  if (d_out == nullptr || blocks < 1 || blocks > (1 << 20) || iters < 1) return SA_ERR_INVALID_ARGUMENT;
+  return sa::launch_mfma_probe(d_out, blocks, iters, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SA_OK : SA_ERR_DEVICE;
+}
+
 }  // extern "C"

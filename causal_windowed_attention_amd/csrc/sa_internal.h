@@ -100,5 +100,6 @@ hipError_t launch_rope_refresh(const RefreshParams& p, int dtype, hipStream_t st
 hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st);
 hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st);
 hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st);
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 
 }  // namespace sa

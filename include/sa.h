@@ -262,6 +262,18 @@ sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value);
 sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int64_t* launches,
                           int32_t reset);
 
+/*
+ * Measurement aid, not an operation of the method: launches `blocks`
+ * workgroups of 4 waves that each issue v_mfma_f32_32x32x16_bf16 on 8
+ * independent accumulators for `iters` rounds, i.e. blocks*4*iters*8*32768
+ * flops, so a caller timing it on `stream` gets the MFMA rate the part
+ * sustains (operands are fixed per lane: a benign, low-power case). d_out
+ * (caller-owned device memory) receives blocks*256 floats. Asynchronous;
+ * SA_ERR_INVALID_ARGUMENT for a null d_out, blocks outside [1, 2^20] or
+ * iters < 1.
+ */
+sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -298,3 +298,32 @@ def test_stream_k_schedule(D):
     a, _ = err(outs[2], outs[1])
     assert a <= 1e-2, a
     s.close()
+
+
+def _bf16_round(x):
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.float().double().numpy()
+
+
+@pytest.mark.gpu
+def test_mfma_probe_computes_the_product():
+    """The pure-MFMA measurement kernel really accumulates A.B: every lane's output equals
+    iters * 8 accumulators * (sum of its 16 entries of A.B), A and B built from the per-lane
+    operand formulas and the 32x32x16 operand layout."""
+    blocks, iters = 4, 64
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    cwa.sa_probe_mfma_bf16(out, blocks, iters)
+    torch.cuda.synchronize()
+    a = np.zeros((32, 16)); b = np.zeros((16, 32))
+    for lane in range(64):
+        for e in range(8):
+            a[lane % 32, 8 * (lane // 32) + e] = ((lane * 7 + e) % 13) * 0.01
+            b[8 * (lane // 32) + e, lane % 32] = ((lane * 5 + e) % 11) * 0.02
+    c = _bf16_round(a) @ _bf16_round(b)
+    want = np.empty(64)
+    for lane in range(64):
+        rows = [8 * (j // 4) + 4 * (lane // 32) + j % 4 for j in range(16)]
+        want[lane] = 8 * iters * c[rows, lane % 32].sum()
+    got = host(out).reshape(blocks * 4, 64)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=1e-4)

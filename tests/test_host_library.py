@@ -8,6 +8,7 @@
   prefix [0, visible_chunks) that the attention kernel reads;
 * error conventions: status codes, state unchanged after an error.
 """
+import ctypes
 import os
 import re
 
@@ -25,7 +26,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_exports_every_declared_symbol():
     hdr = open(os.path.join(ROOT, "include", "sa.h")).read()
     hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
-    declared = set(re.findall(r"\b(sa_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", hdr))
     assert len(declared) >= 14
     lib = L.load()
     for name in sorted(declared):
@@ -249,3 +250,13 @@ def test_workspace_layout_and_plans():
             assert 1 <= st["last_kv_splits"] <= lay["max_kv_splits"]
             s.kv_append(None, None)
         assert s.query()["visible_keys"] == slots * nc
+
+
+def test_mfma_probe_argument_errors():
+    """The measurement kernel's entry point validates before touching the device."""
+    lib = L.load()
+    assert lib.sa_probe_mfma_bf16(None, 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    fake = ctypes.c_void_p(0x1000)             # never dereferenced: rejected on the host
+    assert lib.sa_probe_mfma_bf16(fake, 0, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16(fake, 1, 0, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16(fake, (1 << 20) + 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT

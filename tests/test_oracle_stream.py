@@ -20,6 +20,7 @@ import pytest
 
 import synth
 from oracle import HistoryOracle, RingOracle, SHIFT_SINK, StreamSpec, attend_bruteforce, round_bf16
+from oracle.rope import rope3d, token_coords
 from oracle.stream import StreamError
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -301,3 +302,98 @@ def test_synth_inputs():
     d = synth.distinct_set_for(synth.WORKLOADS["long512p"], [500])
     assert d == frozenset({0, 497, 498, 499, 500})
     assert synth.source_id(3, d) != 3 and synth.source_id(499, d) == 499
+
+
+def _explicit_buffer_attend(spec, committed, t_next, q, k, v):
+    """Buffer attend from an explicit chunk list: committed = [(t0, k, v)] in commit order (the
+    first S are the sink); buffer chunk j at t_next + j*F sees the sink, the last W of
+    (committed window chunks, buffer chunks 0..j-1) and itself. Scalar-loop attention."""
+    S, W, F, nc = spec.sink_chunks, spec.window_chunks, spec.frames_per_chunk, spec.tokens_per_chunk
+    f, y, x = token_coords(nc, spec.frame_h, spec.frame_w)
+    rot = lambda u, t0: rope3d(np.transpose(u, (0, 2, 1, 3)), t0 + f, y, x, spec.rope, spec.theta)
+    n = q.shape[1] // nc
+    sink, window = committed[:S], committed[S:]
+    buf = [(t_next + j * F, k[:, j * nc:(j + 1) * nc], v[:, j * nc:(j + 1) * nc]) for j in range(n)]
+    out = np.empty(q.shape)
+    scale = 1.0 / np.sqrt(spec.head_dim)
+    for j in range(n):
+        prior = window + buf[:j]
+        vis = sink + (prior[len(prior) - W:] if W else []) + [buf[j]]
+        K = np.concatenate([rot(kk, t0) for t0, kk, _ in vis], axis=2)
+        V = np.concatenate([np.transpose(vv, (0, 2, 1, 3)) for _, _, vv in vis], axis=2)
+        Q = rot(q[:, j * nc:(j + 1) * nc], t_next + j * F)
+        for b in range(spec.batch):
+            for h in range(spec.heads):
+                o, _ = attend_bruteforce(Q[b, h], K[b, h], V[b, h], scale)
+                out[b, j * nc:(j + 1) * nc, h] = o
+    return out
+
+
+@pytest.mark.parametrize("S,W,n,commits", [(1, 2, 4, 5), (0, 1, 3, 2), (2, 0, 2, 3), (1, 3, 2, 1)])
+def test_buffer_attend_matches_explicit_windows(S, W, n, commits):
+    """Pin: each buffer chunk's visible set is enumerated directly, not through the oracle's
+    ring or history bookkeeping; both formulations must reproduce it."""
+    spec = StreamSpec(batch=1, heads=2, head_dim=8, frame_h=2, frame_w=2, frames_per_chunk=1,
+                      sink_chunks=S, window_chunks=W)
+    hist, ring = HistoryOracle(spec), RingOracle(spec)
+    committed = []
+    for c in range(commits):
+        _, k, v = _rand_chunk(spec, 100 + c)
+        hist.append(k, v)
+        ring.append(k, v)
+        committed.append((c * spec.frames_per_chunk, k, v))
+    q, k, v = _rand_chunk(spec, 7, n_tokens=n * spec.tokens_per_chunk)
+    want = _explicit_buffer_attend(spec, committed, hist.t_next, q, k, v)
+    before = hist.state()
+    for orc in (hist, ring):
+        got, lse = orc.buffer_attend(q, k, v)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+        assert np.all(np.isfinite(lse))
+    assert hist.state() == before                    # a buffer attend changes nothing
+
+
+def test_buffer_attend_single_chunk_is_attend_and_rows():
+    spec = _tiny_spec()
+    orc = HistoryOracle(spec)
+    for c in range(3):
+        _, k, v = _rand_chunk(spec, c)
+        orc.append(k, v)
+    q, k, v = _rand_chunk(spec, 9)
+    o1, l1 = orc.attend(q, k, v)
+    o2, l2 = orc.buffer_attend(q, k, v)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    nc = spec.tokens_per_chunk
+    q, k, v = _rand_chunk(spec, 10, n_tokens=3 * nc)
+    full, lfull = orc.buffer_attend(q, k, v)
+    rows = [0, nc - 1, nc, 2 * nc + 5]
+    part, lpart = orc.buffer_attend(q, k, v, rows=rows)
+    np.testing.assert_allclose(part[:, rows], full[:, rows], rtol=0, atol=1e-12)   # BLAS blocking differs
+    np.testing.assert_allclose(lpart[:, :, rows], lfull[:, :, rows], rtol=0, atol=1e-12)
+    assert np.isnan(part[:, 1]).all()
+
+
+def test_buffer_attend_errors():
+    spec = _tiny_spec(sink_chunks=2)
+    orc = HistoryOracle(spec)
+    _, k, v = _rand_chunk(spec, 0)
+    orc.append(k, v)                                 # sink not full yet
+    q, k, v = _rand_chunk(spec, 1, n_tokens=2 * spec.tokens_per_chunk)
+    with pytest.raises(StreamError) as e:
+        orc.buffer_attend(q, k, v)
+    assert e.value.kind == "bad_state"
+    orc.append(k[:, :spec.tokens_per_chunk], v[:, :spec.tokens_per_chunk])
+    q, k, v = _rand_chunk(spec, 2, n_tokens=spec.tokens_per_chunk + 3)
+    with pytest.raises(StreamError) as e:
+        orc.buffer_attend(q, k, v)
+    assert e.value.kind == "invalid"
+    spec = _tiny_spec(max_t=6)                        # F = 2: chunks at t = 0, 2, 4 fit
+    orc = HistoryOracle(spec)
+    _, k, v = _rand_chunk(spec, 3)
+    orc.append(k, v)
+    q, k, v = _rand_chunk(spec, 4, n_tokens=2 * spec.tokens_per_chunk)
+    orc.buffer_attend(q, k, v)                       # t = 2, 4
+    q, k, v = _rand_chunk(spec, 5, n_tokens=3 * spec.tokens_per_chunk)
+    with pytest.raises(StreamError) as e:
+        orc.buffer_attend(q, k, v)                   # t = 6 is out of range
+    assert e.value.kind == "position_range"

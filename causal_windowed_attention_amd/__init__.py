@@ -25,7 +25,8 @@ __all__ = [
     "SaError", "make_config", "sa_status_string", "sa_config_check", "sa_workspace_bytes",
     "sa_stream_create", "sa_stream_destroy", "sa_chunk_attend", "sa_kv_append",
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
-    "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16", "Stream",
+    "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16",
+    "sa_buffer_attend", "sa_buffer_plan", "Stream",
     "SA_F32", "SA_BF16", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
     "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
     "SA_K_ROPE_APPLY", "SA_K_CHUNK_ATTENTION", "SA_K_ATTN_COMBINE", "SA_K_KV_APPEND",
@@ -53,12 +54,12 @@ def _check(status: int, where: str) -> None:
 
 def make_config(batch, heads, head_dim, frame_h, frame_w, frames_per_chunk, sink_chunks,
                 window_chunks, rope_dims=(0, 0, 0), max_t=0, rope_theta=0.0, softmax_scale=0.0,
-                dtype=SA_BF16) -> sa_config:
+                dtype=SA_BF16, max_buffer_chunks=0) -> sa_config:
     if isinstance(dtype, str):
         dtype = {"bf16": SA_BF16, "f32": SA_F32}[dtype]
     return sa_config(batch, heads, head_dim, frame_h, frame_w, frames_per_chunk, sink_chunks,
                      window_chunks, rope_dims[0], rope_dims[1], rope_dims[2], max_t,
-                     float(rope_theta), float(softmax_scale), dtype)
+                     float(rope_theta), float(softmax_scale), dtype, max_buffer_chunks, 0)
 
 
 def _ptr(x) -> Optional[int]:
@@ -159,6 +160,21 @@ def sa_profile_read(handle, kernel_id: int, reset: bool = False) -> Tuple[float,
     return ms.value, n.value
 
 
+def sa_buffer_attend(handle, q, k, v, n_chunks: int, out, lse=None, stream=None) -> None:
+    _check(L.load().sa_buffer_attend(handle, _ptr(q), _ptr(k), _ptr(v), n_chunks, _ptr(out), _ptr(lse),
+                                     _stream_ptr(stream)), "sa_buffer_attend")
+
+
+def sa_buffer_plan(handle, n_chunks: int):
+    """Per buffer chunk, the [lo, hi) physical key-row ranges a buffer attend would read."""
+    m = L.SA_MAX_KEY_SEGMENTS
+    n_seg = (ctypes.c_int32 * max(n_chunks, 1))()
+    lo = (ctypes.c_int32 * (m * max(n_chunks, 1)))()
+    hi = (ctypes.c_int32 * (m * max(n_chunks, 1)))()
+    _check(L.load().sa_buffer_plan(handle, n_chunks, n_seg, lo, hi), "sa_buffer_plan")
+    return [[(lo[j * m + i], hi[j * m + i]) for i in range(n_seg[j])] for j in range(n_chunks)]
+
+
 def sa_probe_mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
     """Launch the pure-MFMA measurement kernel (out: float32 device tensor of blocks*256)."""
     _check(L.load().sa_probe_mfma_bf16(_ptr(out), blocks, iters, _stream_ptr(stream)), "sa_probe_mfma_bf16")
@@ -211,6 +227,30 @@ class Stream:
                 raise ValueError("lse: expected contiguous float32 [B, H, Nc]")
         sa_chunk_attend(self.handle, q, k, v, out, lse, stream)
         return out
+
+    def buffer_attend(self, q, k, v, out=None, lse=None, stream=None, n_chunks=None):
+        """Moving-buffer attend: q, k, v hold n consecutive chunks [B, n*Nc, H, D]."""
+        if n_chunks is None:
+            if q is None or q.shape[1] % self.Nc:
+                raise ValueError("buffer_attend: q must hold whole chunks (or pass n_chunks)")
+            n_chunks = q.shape[1] // self.Nc
+        rows = n_chunks * self.Nc
+        if self.workspace is not None and out is None:
+            import torch
+            out = torch.empty((self.cfg.batch, rows, self.cfg.heads, self.cfg.head_dim),
+                              dtype=self._torch_dtype(), device=self.workspace.device)
+        for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+            self._check_tensor(t, rows, n)
+        if lse is not None:
+            import torch
+            if tuple(lse.shape) != (self.cfg.batch, self.cfg.heads, rows) or \
+                    lse.dtype != torch.float32 or not lse.is_contiguous():
+                raise ValueError("lse: expected contiguous float32 [B, H, n*Nc]")
+        sa_buffer_attend(self.handle, q, k, v, n_chunks, out, lse, stream)
+        return out
+
+    def buffer_plan(self, n_chunks: int):
+        return sa_buffer_plan(self.handle, n_chunks)
 
     def kv_append(self, k=None, v=None, stream=None):
         if k is not None or v is not None:

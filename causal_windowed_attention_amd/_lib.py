@@ -21,6 +21,8 @@ SA_F32 = 0
 SA_BF16 = 1
 SA_REFRESH_SHIFT_SINK = 1
 SA_MAX_TEMPORAL_PAIRS = 320
+SA_MAX_BUFFER_CHUNKS = 8
+SA_MAX_KEY_SEGMENTS = 4
 # sa_slot_kind
 SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_WINDOW, SA_SLOT_STAGING = 0, 1, 2, 3
 # sa_kernel_id
@@ -37,7 +39,8 @@ class sa_config(ctypes.Structure):
                 ("window_chunks", ctypes.c_int32), ("rope_dim_t", ctypes.c_int32),
                 ("rope_dim_h", ctypes.c_int32), ("rope_dim_w", ctypes.c_int32),
                 ("max_t", ctypes.c_int32), ("rope_theta", ctypes.c_double),
-                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("max_buffer_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class sa_state(ctypes.Structure):
@@ -86,6 +89,9 @@ SIGNATURES = {
     "sa_profile_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(_I64), _I32]),
     "sa_probe_mfma_bf16": (ctypes.c_int, [_P, _I32, _I32, _P]),
+    "sa_buffer_attend": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P]),
+    "sa_buffer_plan": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                      ctypes.POINTER(_I32)]),
 }
 
 _lib = None

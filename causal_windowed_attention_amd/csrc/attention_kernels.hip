@@ -385,11 +385,70 @@ struct PpSmem {
   static constexpr int BYTES = kPpStages * Bf16Geom<D>::BUF;
 };
 
-// One ping-pong work segment: query tile qt of (b, h) = bh against key tiles
-// [t_begin, t_end).
-template <int D>
-__device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int bh, int qt, int t_begin,
-                                           int t_end, int mode, int slot) {
+// The key tiles one work item visits: up to kMaxSegs key-row ranges [lo, hi),
+// each covered by tiles lo / BN .. ceil(hi / BN) - 1 and masked to its range.
+// Every member is wave-uniform; the fixed-size loops keep it in scalar
+// registers.
+struct KeyList {
+  int n, total;                                  // ranges, tiles over all ranges
+  int lo[kMaxSegs], hi[kMaxSegs], t0[kMaxSegs], cum[kMaxSegs];
+};
+
+// Key tiles [t_begin, t_end) of the single range [0, n_keys) (chunk attend, splits, stream-K).
+__device__ __forceinline__ KeyList keys_single(const AttnParams& p, int t_begin, int t_end) {
+  KeyList kl{};
+  kl.n = 1;
+  kl.total = t_end - t_begin;
+  kl.lo[0] = 0;
+  kl.hi[0] = p.n_keys;
+  kl.t0[0] = t_begin;
+  kl.cum[0] = 0;
+  return kl;
+}
+
+// The key ranges of query group g (moving-buffer attend).
+__device__ __forceinline__ KeyList keys_group(const AttnParams& p, int g, int BN) {
+  KeyList kl{};
+  kl.n = p.n_seg[g];
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxSegs; ++k) {
+    if (k < kl.n) {
+      kl.lo[k] = p.seg_lo[g][k];
+      kl.hi[k] = p.seg_hi[g][k];
+      kl.t0[k] = kl.lo[k] / BN;
+      kl.cum[k] = c;
+      c += (kl.hi[k] + BN - 1) / BN - kl.t0[k];
+    }
+  }
+  kl.total = c;
+  return kl;
+}
+
+// Physical key tile of visit i, with the key-row range its keys must lie in.
+__device__ __forceinline__ int key_tile(const KeyList& kl, int i, int& lo, int& hi) {
+  int tile = kl.t0[0] + i;
+  lo = kl.lo[0];
+  hi = kl.hi[0];
+#pragma unroll
+  for (int k = 1; k < kMaxSegs; ++k) {
+    if (k < kl.n && i >= kl.cum[k]) {
+      tile = kl.t0[k] + (i - kl.cum[k]);
+      lo = kl.lo[k];
+      hi = kl.hi[k];
+    }
+  }
+  return tile;
+}
+
+// One ping-pong work segment: query rows [q_base, q_base + BM) of (b, h) = bh,
+// valid below q_end, against key tiles [t_begin, t_end) of the range [0, n_keys)
+// or, with GROUPS (a moving-buffer attend), against the key tiles of kl. The
+// single-range form is a separate instantiation so the chunk attend's kernel
+// carries none of the range bookkeeping.
+template <int D, bool GROUPS>
+__device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int bh, int q_base, int q_end,
+                                           int t_begin, int t_end, const KeyList& kl, int mode, int slot) {
   using G = Bf16Geom<D>;
   constexpr int NW = 8, STAGES = kPpStages;
   constexpr int BN = G::BN;
@@ -405,16 +464,26 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lag = wave >= 4 ? 1 : 0;
   const int l32 = lane & 31, g = lane >> 5;
-  const int n = t_end - t_begin;                 // tiles of this segment (>= 1)
+  const int n = GROUPS ? kl.total : t_end - t_begin;   // tiles of this work item (>= 1)
   const int n_keys = p.n_keys;
+  // physical key tile of visit i and the key-row range its keys must lie in
+  auto visit = [&](int i, int& lo, int& hi) {
+    if constexpr (GROUPS) {
+      return key_tile(kl, i, lo, hi);
+    } else {
+      lo = 0;
+      hi = n_keys;
+      return t_begin + i;
+    }
+  };
 
   const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
   const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
 
-  const int q = qt * BM + wave * 32 + l32;
+  const int q = q_base + wave * 32 + l32;
   bf16x8 bq[KSTEPS];
   {
-    const int qrow = min(q, p.Nc - 1);
+    const int qrow = min(q, q_end - 1);
     const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
@@ -435,8 +504,9 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
   };
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, p.k_bh_stride * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, p.vt_bh_stride * 2);
-  auto issue_tile = [&](int i) {                 // tile t_begin + i into stage i % STAGES
-    const int key0 = (t_begin + i) * BN;
+  auto issue_tile = [&](int i) {                 // visit i into stage i % STAGES
+    int lo_unused, hi_unused;
+    const int key0 = visit(i, lo_unused, hi_unused) * BN;
     char* dst = smem + (i % STAGES) * G::BUF;
 #pragma unroll
     for (int c = 0; c < KCOPIES; ++c) lds_copy16(krs, key0 * G::KROW + k_src(c), dst + (c * NW + wave) * 1024);
@@ -480,13 +550,16 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
       }
   };
   auto softmax = [&](int i) {
-    const int key0 = (t_begin + i) * BN;
-    if (key0 + BN > n_keys) {                     // ragged last tile (wave-uniform branch)
+    int lo, hi;
+    const int key0 = visit(i, lo, hi) * BN;
+    if ((GROUPS && key0 < lo) || key0 + BN > hi) {   // tile cut by its range (wave-uniform branch)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7) >= n_keys) sacc[mt][j] = -__builtin_inff();
+        for (int j = 0; j < 16; ++j) {
+          const int key = key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7);
+          if (key < lo || key >= hi) sacc[mt][j] = -__builtin_inff();
+        }
     }
     float mx = sacc[0][0];
 #pragma unroll
@@ -593,7 +666,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
     if (g == 0) p.sk_part_lse[row] = lse2;
     return;
   }
-  if (q >= p.Nc) return;
+  if (q >= q_end) return;
   const int b = bh / p.H, h = bh - b * p.H;
   if (mode == kPpFinal) {
     __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
@@ -631,9 +704,18 @@ __device__ __forceinline__ int64_t sk_start(int w, int64_t L, int G) { return (s
 // its range as segments; a segment that covers a whole q-tile writes the final
 // rows, a partial one writes slot 2w (the range's first segment) or 2w + 1 (its
 // last), merged afterwards by attn_sk_combine.
-template <int D>
+template <int D, bool GROUPS>
 __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p) {
   __shared__ __attribute__((aligned(1024))) char smem[PpSmem<D>::BYTES];
+  if constexpr (GROUPS) {                        // moving buffer: the q-tile's chunk picks the keys
+    const int w = xcd_remap(blockIdx.x, p.B * p.H * p.q_tiles);
+    const int qt = w % p.q_tiles, bh = w / p.q_tiles;
+    const int grp = qt / p.group_qtiles;
+    const int q_base = grp * p.group_rows + (qt - grp * p.group_qtiles) * (8 * 32);
+    pp_segment<D, true>(p, smem, bh, q_base, (grp + 1) * p.group_rows, 0, 0, keys_group(p, grp, Bf16Geom<D>::BN),
+                        kPpFinal, 0);
+    return;
+  }
   const bool sk = p.sk_groups > 0;
   const int T = p.key_tiles;
   // grid mode: one segment, the work item's (q-tile, split); stream-K: the range of w
@@ -641,6 +723,7 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
   const int w = xcd_remap(blockIdx.x, G);
   const int64_t L = static_cast<int64_t>(p.B) * p.H * p.q_tiles * T;
   const int64_t r0 = sk ? sk_start(w, L, G) : 0, r1 = sk ? sk_start(w + 1, L, G) : 1;
+  const KeyList none{};
   for (int64_t it = r0; it < r1;) {
     int bh, qt, t0, t1, mode, slot;
     if (sk) {
@@ -663,7 +746,7 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
       slot = split;
       it = r1;
     }
-    pp_segment<D>(p, smem, bh, qt, t0, t1, mode, slot);
+    pp_segment<D, false>(p, smem, bh, qt * (8 * 32), p.Nc, t0, t1, none, mode, slot);
     if (it < r1) __syncthreads();                // the next segment reuses every LDS stage
   }
 }
@@ -685,11 +768,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attention_bf16_d64_q64(Attn
 }
 
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_pp(AttnParams p) {
-  chunk_attention_bf16_pp_body<128>(p);
+  chunk_attention_bf16_pp_body<128, false>(p);
 }
 
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d64_pp(AttnParams p) {
-  chunk_attention_bf16_pp_body<64>(p);
+  chunk_attention_bf16_pp_body<64, false>(p);
+}
+
+// moving-buffer attend: query groups with their own key ranges
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_ppg(AttnParams p) {
+  chunk_attention_bf16_pp_body<128, true>(p);
+}
+
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d64_ppg(AttnParams p) {
+  chunk_attention_bf16_pp_body<64, true>(p);
 }
 
 // fp32: one query row per lane, 64 rows per block, 32-key tiles through LDS.
@@ -710,8 +802,18 @@ __global__ __launch_bounds__(64) void chunk_attention_f32(AttnParams p) {
   const float* kbase = static_cast<const float*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride;
   const float* vbase = static_cast<const float*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride;
 
-  const int q = qt * kF32BlockM + lane;
-  const int qrow = min(q, p.Nc - 1);
+  int q_base = qt * kF32BlockM, q_end = p.Nc;
+  KeyList kl;
+  if (p.n_groups > 0) {                          // moving buffer: the q-tile's chunk picks the keys
+    const int grp = qt / p.group_qtiles;
+    q_base = grp * p.group_rows + (qt - grp * p.group_qtiles) * kF32BlockM;
+    q_end = (grp + 1) * p.group_rows;
+    kl = keys_group(p, grp, BN);
+  } else {
+    kl = keys_single(p, t_begin, t_end);
+  }
+  const int q = q_base + lane;
+  const int qrow = min(q, q_end - 1);
   const float* qsrc = static_cast<const float*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
   float qr[D], o[D];
 #pragma unroll
@@ -720,19 +822,20 @@ __global__ __launch_bounds__(64) void chunk_attention_f32(AttnParams p) {
     o[d] = 0.f;
   }
   float m = -__builtin_inff(), l = 0.f;
-  for (int t = t_begin; t < t_end; ++t) {
-    const int key0 = t * BN;
-    const int nk = min(BN, p.n_keys - key0);
+  for (int t = 0; t < kl.total; ++t) {
+    int lo, hi;
+    const int key0 = key_tile(kl, t, lo, hi) * BN;
+    const int r_lo = max(0, lo - key0), r_hi = min(BN, hi - key0);   // keys of the tile in range
     for (int i = lane; i < BN * D; i += 64) {
       const int r = i / D, d = i - r * D;
-      sk[r][d] = r < nk ? kbase[static_cast<size_t>(key0 + r) * D + d] : 0.f;
+      sk[r][d] = r >= r_lo && r < r_hi ? kbase[static_cast<size_t>(key0 + r) * D + d] : 0.f;
     }
     for (int i = lane; i < BN * D; i += 64) {
       const int d = i / BN, r = i - d * BN;
-      sv[r][d] = r < nk ? vbase[static_cast<size_t>(d) * p.key_stride + key0 + r] : 0.f;
+      sv[r][d] = r >= r_lo && r < r_hi ? vbase[static_cast<size_t>(d) * p.key_stride + key0 + r] : 0.f;
     }
     __syncthreads();
-    for (int r = 0; r < nk; ++r) {
+    for (int r = r_lo; r < r_hi; ++r) {
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qr[d], sk[r][d], s);
@@ -746,7 +849,7 @@ __global__ __launch_bounds__(64) void chunk_attention_f32(AttnParams p) {
     }
     __syncthreads();
   }
-  if (q >= p.Nc) return;
+  if (q >= q_end) return;
   const float inv = 1.f / l;
   const float lse2 = m + __log2f(l);
   const int b = bh / p.H, h = bh - b * p.H;
@@ -886,7 +989,10 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
       p.sk_groups > 0 ? p.sk_groups : static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
   if (n_work <= 0) return hipSuccess;
   if (dtype == 1) {
-    if (p.variant == 3) {
+    if (p.n_groups > 0) {
+      hipLaunchKernelGGL(p.D == 128 ? chunk_attention_bf16_d128_ppg : chunk_attention_bf16_d64_ppg, dim3(n_work),
+                         dim3(2 * kThreads), 0, st, p);
+    } else if (p.variant == 3) {
       hipLaunchKernelGGL(p.D == 128 ? chunk_attention_bf16_d128_pp : chunk_attention_bf16_d64_pp, dim3(n_work),
                          dim3(2 * kThreads), 0, st, p);
     } else {

@@ -114,7 +114,7 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
   const T* __restrict__ qin = static_cast<const T*>(p.q);
   const T* __restrict__ vin = static_cast<const T*>(p.v);
   T* __restrict__ kc = static_cast<T*>(p.kcache) + bh * p.k_bh_stride;
-  T* __restrict__ qo = static_cast<T*>(p.qrot) + bh * p.n_tokens * p.D;
+  T* __restrict__ qo = static_cast<T*>(p.qrot) + (bh * p.q_rows + p.q_row0) * p.D;
   T* __restrict__ vt = static_cast<T*>(p.vtcache) + bh * p.vt_bh_stride + p.row0 + n0;
   auto in_off = [&](int n, int c) {
     return ((static_cast<size_t>(b) * p.in_tokens + p.in_tok0 + n) * p.H + h) * p.D + c;

@@ -21,6 +21,7 @@
 #include "../../include/sa.h"
 #include "sa_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -40,7 +41,7 @@ constexpr int kSkGroups = 256;              // persistent workgroups of the stre
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Derived {
-  int32_t B, H, D, Hf, Wf, F, S, W, R, n_slots, Nc, dt, dh, dw, max_t, dtype, elem;
+  int32_t B, H, D, Hf, Wf, F, S, W, R, n_slots, NB, buf_slot0, Nc, dt, dh, dw, max_t, dtype, elem;
   int32_t key_stride, q_tiles, max_splits;
   double theta;
   float scale;
@@ -55,6 +56,8 @@ sa_status derive(const sa_config* c, Derived* d) {
       c->head_dim % 2 != 0)
     return SA_ERR_INVALID_ARGUMENT;
   if (c->dtype != SA_F32 && c->dtype != SA_BF16) return SA_ERR_INVALID_ARGUMENT;
+  if (c->max_buffer_chunks < 0 || c->max_buffer_chunks > SA_MAX_BUFFER_CHUNKS || c->reserved != 0)
+    return SA_ERR_INVALID_ARGUMENT;
   if (!(c->rope_theta >= 0.0) || !(c->softmax_scale >= 0.f) || !std::isfinite(c->rope_theta) ||
       !std::isfinite(c->softmax_scale))
     return SA_ERR_INVALID_ARGUMENT;
@@ -78,7 +81,9 @@ sa_status derive(const sa_config* c, Derived* d) {
   if (static_cast<int64_t>(d->S) + d->W + 1 > (1 << 16)) return SA_ERR_UNSUPPORTED;
   d->R = d->W + 1;
   d->n_slots = d->S + d->R;
-  const int64_t keys = static_cast<int64_t>(d->n_slots) * d->Nc;
+  d->NB = c->max_buffer_chunks;
+  d->buf_slot0 = d->n_slots;                     // buffer chunk i lives in slot n_slots + i
+  const int64_t keys = static_cast<int64_t>(d->n_slots + d->NB) * d->Nc;
   if (keys > (1 << 24)) return SA_ERR_UNSUPPORTED;
   if (d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d->F) * (d->dt / 2) > sa::kMaxTemporalPairs) return SA_ERR_UNSUPPORTED;
@@ -101,7 +106,7 @@ sa_status derive(const sa_config* c, Derived* d) {
   // K rows padded to key_stride per (b, h): a key tile never leaves the allocation
   d->k_bytes = bh * static_cast<size_t>(d->key_stride) * d->D * d->elem;
   d->vt_bytes = bh * static_cast<size_t>(d->D) * d->key_stride * d->elem;
-  d->q_bytes = bh * static_cast<size_t>(d->Nc) * d->D * d->elem;
+  d->q_bytes = bh * static_cast<size_t>(d->NB > 1 ? d->NB : 1) * d->Nc * d->D * d->elem;
   d->part_bytes = d->max_splits > 1
                       ? static_cast<size_t>(d->max_splits) * bh * d->Nc * (static_cast<size_t>(d->D) + 1) * 4
                       : 0;
@@ -208,6 +213,7 @@ void base_write_params(const sa_stream* s, RopeWriteParams* p) {
   p->B = d.B; p->H = d.H; p->D = d.D; p->Hf = d.Hf; p->Wf = d.Wf;
   p->dt = d.dt; p->dh = d.dh; p->dw = d.dw;
   p->n_frames = d.F;
+  p->q_rows = d.Nc;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -282,6 +288,58 @@ int choose_stream_k(const sa_stream* s, int key_tiles, int q_tiles) {
   // last wave lowers the clock by about as much as it cuts cycles, and the combine pass
   // then makes the whole slower.
   return s->schedule_opt == 2 ? kSkGroups : 0;
+}
+
+// Key-row segments of a moving-buffer attend of n chunks: buffer chunk j sees the
+// sink, the newest min(window_valid, W - j) committed window chunks (ring slots of
+// consecutive commits, contiguous modulo R: at most two ranges) and buffer chunks
+// max(0, j - W)..j. Ranges are sorted and adjacent ones merged.
+struct BufferPlan {
+  int32_t n[SA_MAX_BUFFER_CHUNKS];
+  int32_t lo[SA_MAX_BUFFER_CHUNKS][SA_MAX_KEY_SEGMENTS], hi[SA_MAX_BUFFER_CHUNKS][SA_MAX_KEY_SEGMENTS];
+};
+
+sa_status plan_buffer(const sa_stream* s, int32_t n_chunks, BufferPlan* bp) {
+  const Derived& d = s->d;
+  if (n_chunks < 1 || n_chunks > d.NB) return SA_ERR_INVALID_ARGUMENT;
+  if (s->sink_fill < d.S) return SA_ERR_BAD_STATE;
+  const sa_status st = positions_ok(s, static_cast<int64_t>(s->t_next) + static_cast<int64_t>(n_chunks) * d.F);
+  if (st != SA_OK) return st;
+  const int64_t C = s->ring_commits;
+  const int32_t valid = s->window_valid();
+  for (int j = 0; j < n_chunks; ++j) {
+    int32_t lo[SA_MAX_KEY_SEGMENTS], hi[SA_MAX_KEY_SEGMENTS];   // in slots
+    int n = 0;
+    if (d.S > 0) { lo[n] = 0; hi[n] = d.S; ++n; }
+    const int32_t m = std::max(0, std::min(valid, d.W - j));   // committed chunks still in chunk j's window
+    if (m > 0) {
+      const int32_t start = static_cast<int32_t>((C - m) % d.R);
+      if (start + m <= d.R) {
+        lo[n] = d.S + start; hi[n] = d.S + start + m; ++n;
+      } else {
+        lo[n] = d.S + start; hi[n] = d.S + d.R; ++n;
+        lo[n] = d.S; hi[n] = d.S + start + m - d.R; ++n;
+      }
+    }
+    lo[n] = d.buf_slot0 + std::max(0, j - d.W); hi[n] = d.buf_slot0 + j + 1; ++n;
+    for (int a = 1; a < n; ++a)                  // sort by start (n <= 4)
+      for (int b = a; b > 0 && lo[b] < lo[b - 1]; --b) {
+        std::swap(lo[b], lo[b - 1]);
+        std::swap(hi[b], hi[b - 1]);
+      }
+    int out = 0;
+    for (int a = 0; a < n; ++a) {
+      if (out > 0 && lo[a] <= bp->hi[j][out - 1] / d.Nc) {
+        bp->hi[j][out - 1] = std::max(bp->hi[j][out - 1], hi[a] * d.Nc);
+      } else {
+        bp->lo[j][out] = lo[a] * d.Nc;
+        bp->hi[j][out] = hi[a] * d.Nc;
+        ++out;
+      }
+    }
+    bp->n[j] = out;
+  }
+  return SA_OK;
 }
 
 void commit_meta(sa_stream* s) {
@@ -700,6 +758,101 @@ sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int
     pr.total_ms = 0.0;
     pr.launches = 0;
   }
+  return SA_OK;
+}
+
+sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, int32_t* n_seg, int32_t* seg_lo,
+                         int32_t* seg_hi) {
+  if (s == nullptr || n_seg == nullptr || seg_lo == nullptr || seg_hi == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  BufferPlan bp;
+  const sa_status st = plan_buffer(s, n_chunks, &bp);
+  if (st != SA_OK) return st;
+  for (int j = 0; j < n_chunks; ++j) {
+    n_seg[j] = bp.n[j];
+    for (int k = 0; k < SA_MAX_KEY_SEGMENTS; ++k) {
+      seg_lo[j * SA_MAX_KEY_SEGMENTS + k] = k < bp.n[j] ? bp.lo[j][k] : 0;
+      seg_hi[j * SA_MAX_KEY_SEGMENTS + k] = k < bp.n[j] ? bp.hi[j][k] : 0;
+    }
+  }
+  return SA_OK;
+}
+
+sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const void* v, int32_t n_chunks,
+                           void* out, float* lse, void* stream) {
+  if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  const Derived& d = s->d;
+  if (!s->planning()) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return SA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return SA_ERR_INVALID_ARGUMENT;
+  }
+  BufferPlan bp;
+  sa_status st = plan_buffer(s, n_chunks, &bp);
+  if (st != SA_OK) return st;
+  const int bm = d.dtype == SA_BF16 ? sa::kBf16BlockMWide : sa::kF32BlockM;
+  const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
+  const int group_qtiles = (d.Nc + bm - 1) / bm;
+  int max_tiles = 0;
+  for (int j = 0; j < n_chunks; ++j) {
+    int t = 0;
+    for (int i = 0; i < bp.n[j]; ++i) t += (bp.hi[j][i] + bn - 1) / bn - bp.lo[j][i] / bn;
+    max_tiles = t > max_tiles ? t : max_tiles;
+  }
+
+  if (!s->planning()) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (int j = 0; j < n_chunks; ++j) {         // rotate and store buffer chunk j
+      RopeWriteParams rp;
+      base_write_params(s, &rp);
+      rp.q = q; rp.k = k; rp.v = v;
+      rp.qrot = s->qscratch();
+      rp.in_tokens = n_chunks * d.Nc;
+      rp.in_tok0 = j * d.Nc;
+      rp.row0 = (d.buf_slot0 + j) * d.Nc;
+      rp.q_rows = n_chunks * d.Nc;
+      rp.q_row0 = j * d.Nc;
+      fill_temporal(d, static_cast<int64_t>(s->t_next) + static_cast<int64_t>(j) * d.F, d.F, rp.t_cs);
+      st = timed(s, SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply(rp, d.dtype, hs); });
+      if (st != SA_OK) return st;
+    }
+    AttnParams ap;
+    std::memset(&ap, 0, sizeof(ap));
+    ap.q = s->qscratch();
+    ap.kcache = s->kcache();
+    ap.vtcache = s->vtcache();
+    ap.out = out;
+    ap.lse = lse;
+    ap.k_bh_stride = static_cast<int64_t>(d.key_stride) * d.D;
+    ap.vt_bh_stride = static_cast<int64_t>(d.D) * d.key_stride;
+    ap.key_stride = d.key_stride;
+    ap.n_keys = (d.buf_slot0 + d.NB) * d.Nc;
+    ap.Nc = n_chunks * d.Nc;                     // query rows per (b, h)
+    ap.B = d.B; ap.H = d.H; ap.D = d.D;
+    ap.variant = d.dtype == SA_BF16 ? 3 : 0;
+    ap.q_rows_per_block = bm;
+    ap.q_tiles = n_chunks * group_qtiles;
+    ap.kv_splits = 1;
+    ap.key_tiles = max_tiles;
+    ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    ap.n_groups = n_chunks;
+    ap.group_rows = d.Nc;
+    ap.group_qtiles = group_qtiles;
+    for (int j = 0; j < n_chunks; ++j) {
+      ap.n_seg[j] = bp.n[j];
+      for (int i = 0; i < bp.n[j]; ++i) {
+        ap.seg_lo[j][i] = bp.lo[j][i];
+        ap.seg_hi[j][i] = bp.hi[j][i];
+      }
+    }
+    st = timed(s, SA_K_CHUNK_ATTENTION, hs, [&] { return sa::launch_chunk_attention(ap, d.dtype, hs); });
+    if (st != SA_OK) return st;
+  }
+  s->staged_valid = false;
+  s->last_q_tiles = n_chunks * group_qtiles;
+  s->last_kv_splits = 1;
+  s->last_key_tiles = max_tiles;
+  s->last_sk_groups = 0;
   return SA_OK;
 }
 

@@ -21,6 +21,8 @@ constexpr int kF32BlockM = 64;
 constexpr int kF32BlockN = 32;
 // Key-range splits per query tile (partials are merged by attn_combine).
 constexpr int kMaxKvSplits = 8;
+constexpr int kMaxGroups = 8;           // chunks of one moving-buffer attend (SA_MAX_BUFFER_CHUNKS)
+constexpr int kMaxSegs = 4;             // key-row ranges per chunk (SA_MAX_KEY_SEGMENTS)
 
 // Rotate-and-store of a chunk's K (and optionally Q) plus V into the cache:
 // rope_apply (Q -> scratch, K/V -> staging slot), kv_ring_append (K/V -> a slot),
@@ -44,6 +46,8 @@ struct RopeWriteParams {
   int32_t B, H, D, Hf, Wf;
   int32_t dt, dh, dw;
   int32_t n_frames;     // frames covered by t_cs (F)
+  int32_t q_rows;       // rows per (b, h) of the Q scratch
+  int32_t q_row0;       // first Q scratch row written by this launch
   float2 t_cs[kMaxTemporalPairs];  // [frame][d_t/2]: (cos, sin) of (t0 + frame) * theta_t,j
 };
 
@@ -80,6 +84,15 @@ struct AttnParams {
   int32_t sk_groups;    // > 0: stream-K schedule with this many persistent workgroups (variant 3)
   float* sk_part_o;     // [2 * sk_groups][BlockM][D] stream-K partial outputs
   float* sk_part_lse;   // [2 * sk_groups][BlockM] stream-K partial log2-sum-exp
+  // Query groups of a moving-buffer attend: group g holds query rows
+  // [g * group_rows, (g + 1) * group_rows) and attends to its n_seg[g] key-row
+  // ranges [seg_lo, seg_hi). n_groups = 0: one group, rows [0, Nc), keys [0, n_keys).
+  int32_t n_groups;
+  int32_t group_rows;
+  int32_t group_qtiles; // q-tiles per group (q_tiles = n_groups * group_qtiles)
+  int32_t n_seg[kMaxGroups];
+  int32_t seg_lo[kMaxGroups][kMaxSegs];
+  int32_t seg_hi[kMaxGroups][kMaxSegs];
 };
 
 constexpr int kMaxSkGroups = 512;

@@ -77,7 +77,7 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 #define SA_REFRESH_SHIFT_SINK 1u
 
 /*
- * Stream configuration (64 bytes, no padding holes).
+ * Stream configuration (72 bytes, no padding holes).
  *  batch            B >= 1 streams advancing in lockstep (same positions, own caches)
  *  heads            H >= 1
  *  head_dim         D: 64 or 128 (both dtypes)
@@ -90,8 +90,11 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *  rope_theta       RoPE base, 0 selects 10000
  *  softmax_scale    0 selects 1/sqrt(D)
  *  dtype            SA_F32 or SA_BF16 (element type of q, k, v, out and the cache)
+ *  max_buffer_chunks NB in 0..SA_MAX_BUFFER_CHUNKS: chunks one sa_buffer_attend
+ *                   may hold (NB extra cache slots per (b, h), NB*Nc Q scratch rows)
+ *  reserved         must be 0
  * Limits: F * d_t / 2 <= SA_MAX_TEMPORAL_PAIRS; Nc = F*Hf*Wf <= 2^20;
- *         (S + W + 1) * Nc <= 2^24 keys, and the cache of one (b, h) (keys
+ *         (S + W + 1 + NB) * Nc <= 2^24 keys, and the cache of one (b, h) (keys
  *         rounded up to 64, times D times the element size) below 2^31 bytes.
  *         A config over a limit is SA_ERR_UNSUPPORTED.
  */
@@ -103,9 +106,13 @@ typedef struct sa_config {
   double rope_theta;
   float softmax_scale;
   int32_t dtype;
+  int32_t max_buffer_chunks;
+  int32_t reserved;
 } sa_config;
 
 #define SA_MAX_TEMPORAL_PAIRS 320
+#define SA_MAX_BUFFER_CHUNKS 8
+#define SA_MAX_KEY_SEGMENTS 4
 
 /* Host-side stream state (D3) and the plan of the last attend (D4). */
 typedef struct sa_state {
@@ -210,6 +217,37 @@ sa_status sa_stream_destroy(sa_stream* s);
  */
 sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void* v,
                           void* out, float* lse, void* stream);
+
+/*
+ * Moving-buffer attend (StreamDiT: a buffer of consecutive chunks denoised
+ * together, with window attention; the buffer's chunks are the queries of one
+ * call). q, k, v: [B, n*Nc, H, D] holding n consecutive chunks that follow the
+ * committed stream, 1 <= n <= max_buffer_chunks; out: [B, n*Nc, H, D]; lse:
+ * [B, H, n*Nc] float32 or NULL. Buffer chunk j is rotated at positions
+ * t_next + j*F.. and attends (full softmax) to exactly what sa_chunk_attend
+ * would show it once buffer chunks 0..j-1 had been committed: the sink, the
+ * last W chunks of (the committed window, buffer chunks 0..j-1), and itself,
+ * i.e. a block-banded chunk mask. The rotated buffer K/V go to the buffer
+ * slots; the stream state does not change, except that nothing is staged
+ * afterwards (a following sa_kv_append needs explicit k, v). Errors:
+ * SA_ERR_INVALID_ARGUMENT for n outside [1, max_buffer_chunks];
+ * SA_ERR_BAD_STATE while the sink is not full (earlier buffer chunks would
+ * otherwise become sink chunks); SA_ERR_POSITION_RANGE if max_t > 0 and
+ * t_next + n*F > max_t. Always runs the ping-pong kernel for bf16.
+ */
+sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const void* v, int32_t n_chunks,
+                           void* out, float* lse, void* stream);
+
+/*
+ * The key segments a sa_buffer_attend of n_chunks would read now (inspection,
+ * planning handles included): for buffer chunk j, n_seg[j] <= SA_MAX_KEY_SEGMENTS
+ * ranges [seg_lo, seg_hi) of physical key rows of one (b, h), at
+ * seg_lo[j * SA_MAX_KEY_SEGMENTS + i]. Rows s*Nc.. belong to physical slot s:
+ * slots 0..S-1 the sink, S..S+W the window ring, S+W+1+i buffer chunk i.
+ * Segments are disjoint, sorted and not adjacent. Same errors as sa_buffer_attend.
+ */
+sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, int32_t* n_seg, int32_t* seg_lo,
+                         int32_t* seg_hi);
 
 /*
  * Commit one chunk: its k, v ([B, Nc, H, D]) are rotated at positions t_next..

@@ -1,0 +1,113 @@
+"""GPU parity of the moving-buffer attend (sa_buffer_attend) against the fp64 oracle.
+
+The oracle's HistoryOracle.buffer_attend is the definition (each buffer chunk sees what an
+attend would show it after the earlier buffer chunks were committed); it is pinned in
+tests/test_oracle_stream.py against explicitly enumerated windows. Streams are driven
+through commits, refreshes and buffers of several sizes, so the key segments cover the
+sink, wrapped and unwrapped ring ranges and buffer ranges whose chunk boundaries cut
+64-key tiles (Nc not a multiple of 64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_windowed_attention_amd as cwa
+import synth
+from gpu_util import BF16_ABS, BF16_REL, F32_ABS, config_for, dev, err, host, say, spec_for
+from oracle import HistoryOracle
+
+CASES = {
+    # name: (base workload, overrides, max_buffer_chunks)
+    "f32_tiny": ("tiny_f32", {}, 4),
+    "bf16_d128": ("wan1.3b", dict(heads=2, frame_h=6, frame_w=10, frames_per_chunk=3, window_chunks=3), 5),
+    "bf16_d64": ("wan1.3b", dict(heads=2, head_dim=64, frame_h=5, frame_w=7, frames_per_chunk=2,
+                                 sink_chunks=2, window_chunks=2), 4),
+    "bf16_w0": ("wan1.3b", dict(heads=1, frame_h=4, frame_w=9, frames_per_chunk=2, window_chunks=0), 3),
+    "bf16_s0": ("wan1.3b", dict(heads=1, frame_h=4, frame_w=9, frames_per_chunk=2, sink_chunks=0,
+                                window_chunks=2), 3),
+}
+
+
+def _buffer(w, first, n):
+    parts = [synth.chunk_qkv(w, first + j) for j in range(n)]
+    return [np.concatenate([p[i] for p in parts], axis=1) for i in range(3)]
+
+
+def _check(w, got, want, got_lse, want_lse, what):
+    a, r = err(host(got), want)
+    la, _ = err(host(got_lse), want_lse)
+    say(f"  {what}: max {a:.2e} rel {r:.2e}; lse {la:.2e}")
+    if w.dtype == "bf16":
+        assert a <= BF16_ABS and r <= BF16_REL and la <= BF16_ABS, (what, a, r, la)
+    else:
+        assert a <= F32_ABS and la <= F32_ABS, (what, a, la)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", list(CASES))
+def test_buffer_attend_matches_oracle(case):
+    base, kw, nb = CASES[case]
+    w = synth.small_variant(synth.WORKLOADS[base], **kw)
+    say("buffer", case, w.dtype, "H", w.heads, "D", w.head_dim, "Nc", w.tokens_per_chunk,
+        "S", w.sink_chunks, "W", w.window_chunks, "NB", nb)
+    s = cwa.Stream(config_for(w, max_buffer_chunks=nb))
+    hist = HistoryOracle(spec_for(w))
+    state = {"c": 0}
+
+    def commit(k_times):
+        for _ in range(k_times):
+            _, k, v = synth.chunk_qkv(w, state["c"])
+            s.kv_append(dev(k, w.dtype), dev(v, w.dtype))
+            hist.append(k, v)
+            state["c"] += 1
+
+    commit(w.sink_chunks)                        # a buffer attend needs a full sink
+    schedule = [(0, 1), (0, nb), (1, 2), ("refresh", None), (1, nb), (w.window_chunks + 2, nb),
+                (1, max(1, nb - 2)), (2, nb)]
+    for i, (commits, n) in enumerate(schedule):
+        if commits == "refresh":
+            assert s.rope_refresh(-1, 0) == hist.refresh(None, 0)
+            continue
+        commit(commits)
+        q, k, v = _buffer(w, 500 + 10 * i, n)
+        lse = torch.empty((w.batch, w.heads, n * w.tokens_per_chunk), dtype=torch.float32, device="cuda")
+        out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
+        want, want_lse = hist.buffer_attend(q, k, v)
+        _check(w, out, want, lse, want_lse, f"step {i}: {commits} commits then a buffer of {n}")
+        assert s.query()["staged_valid"] == 0
+    # an ordinary attend afterwards is unaffected by the buffer slots
+    q, k, v = synth.chunk_qkv(w, 900)
+    lse = torch.empty((w.batch, w.heads, w.tokens_per_chunk), dtype=torch.float32, device="cuda")
+    out = s.chunk_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
+    want, want_lse = hist.attend(q, k, v)
+    _check(w, out, want, lse, want_lse, "chunk attend after the buffers")
+    s.close()
+
+
+@pytest.mark.gpu
+def test_buffer_attend_full_size_sampled():
+    """long512p shape (H = 24, Nc = 2048, S = 1, W = 3) with a buffer of 4 chunks: sampled
+    rows of two heads against the oracle, after the ring has wrapped."""
+    w = synth.WORKLOADS["long512p"]
+    nb = 4
+    s = cwa.Stream(config_for(w, max_buffer_chunks=nb))
+    hist = HistoryOracle(spec_for(w))
+    for c in range(w.sink_chunks + w.window_chunks + 2):
+        _, k, v = synth.chunk_qkv(w, c)
+        s.kv_append(dev(k, w.dtype), dev(v, w.dtype))
+        hist.append(k, v)
+    q, k, v = _buffer(w, 700, nb)
+    lse = torch.empty((w.batch, w.heads, nb * w.tokens_per_chunk), dtype=torch.float32, device="cuda")
+    out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
+    torch.cuda.synchronize()
+    nc = w.tokens_per_chunk
+    g = np.random.default_rng(5)
+    rows = sorted(set(int(x) for x in g.integers(0, nb * nc, 96)) | {0, nc - 1, nc, nb * nc - 1})
+    heads = [0, w.heads - 1]
+    want, want_lse = hist.buffer_attend(q, k, v, rows=rows, heads=heads)
+    got = host(out)[:, rows][:, :, heads]
+    a, r = err(got, want[:, rows][:, :, heads])
+    la, _ = err(host(lse)[:, heads][:, :, rows], want_lse[:, heads][:, :, rows])
+    say(f"  long512p buffer of {nb}: sampled max {a:.2e} rel {r:.2e}; lse {la:.2e}")
+    assert a <= BF16_ABS and r <= BF16_REL and la <= BF16_ABS
+    s.close()

@@ -8,6 +8,7 @@
   prefix [0, visible_chunks) that the attention kernel reads;
 * error conventions: status codes, state unchanged after an error.
 """
+import copy
 import ctypes
 import os
 import re
@@ -36,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     import ctypes
-    assert ctypes.sizeof(L.sa_config) == 64
+    assert ctypes.sizeof(L.sa_config) == 72
     assert ctypes.sizeof(L.sa_state) == 16 + 14 * 4
     assert ctypes.sizeof(L.sa_slot_info) == 16
 
@@ -127,6 +128,108 @@ def test_planning_bookkeeping_matches_oracle(S, W, seed):
             assert st["staged_valid"] == 1
             assert st["last_key_tiles"] == -(-st["visible_keys"] // 64)
     s.close()
+
+
+def _buffer_slots_expected(s, orc, spec, j):
+    """Physical slots buffer chunk j must read: the oracle's visible set after committing
+    buffer chunks 0..j-1, mapped to slots (sink slots, window slots by chunk id, buffer slot
+    S + W + 1 + i for buffer chunk i)."""
+    tmp = copy.deepcopy(orc)
+    z = _dummy(spec)
+    for _ in range(j):
+        tmp.append(z, z)
+    st = s.query()
+    by_id = {}
+    for slot in range(st["n_slots"]):
+        info = s.slot(slot)
+        if info["kind"] == cwa.SA_SLOT_WINDOW:
+            by_id[info["chunk_id"]] = slot
+    buf0 = spec.sink_chunks + spec.window_chunks + 1
+    want = set()
+    for kind, cid, _ in tmp.visible():
+        if kind == "sink":
+            continue
+        want.add(by_id[cid] if cid < orc.n_appends else buf0 + cid - orc.n_appends)
+    return want | set(range(spec.sink_chunks))
+
+
+@pytest.mark.parametrize("S,W,NB,seed", [(1, 2, 4, 0), (1, 6, 8, 1), (2, 3, 5, 2), (0, 2, 3, 3),
+                                         (1, 0, 2, 4), (0, 0, 1, 5), (3, 1, 8, 6)])
+def test_buffer_plan_matches_oracle(S, W, NB, seed):
+    """Bit-exact: the key segments of every buffer chunk cover exactly the slots of the
+    chunks the oracle's buffer reading makes visible, as disjoint sorted ranges."""
+    cfg = _cfg(sink_chunks=S, window_chunks=W, max_buffer_chunks=NB)
+    s = cwa.Stream(cfg, planning=True)
+    spec = _spec(cfg)
+    nc = spec.tokens_per_chunk
+    orc = HistoryOracle(spec)
+    g = np.random.default_rng(seed)
+    z = _dummy(spec)
+    for step in range(120):
+        n = int(g.integers(1, NB + 1))
+        if orc.sink_fill < S:
+            with pytest.raises(cwa.SaError) as e:
+                s.buffer_plan(n)
+            assert e.value.status == L.SA_ERR_BAD_STATE
+        else:
+            plan = s.buffer_plan(n)
+            for j, segs in enumerate(plan):
+                assert 1 <= len(segs) <= L.SA_MAX_KEY_SEGMENTS
+                slots = set()
+                for a, (lo, hi) in enumerate(segs):
+                    assert lo % nc == 0 and hi % nc == 0 and lo < hi
+                    if a:
+                        assert lo > segs[a - 1][1]               # sorted, disjoint, not adjacent
+                    slots |= set(range(lo // nc, hi // nc))
+                assert slots == _buffer_slots_expected(s, orc, spec, j), (step, j, segs)
+            before = s.query()
+            cwa.sa_buffer_attend(s.handle, None, None, None, n, None)
+            after = s.query()
+            assert after["staged_valid"] == 0
+            for key in ("t_next", "n_appends", "sink_fill", "ring_commits", "visible_keys"):
+                assert after[key] == before[key]
+        r = g.random()
+        if r < 0.75:
+            cwa.sa_kv_append(s.handle, 1, 1)
+            orc.append(z, z)
+        elif r < 0.9:
+            base = int(g.choice([-1, 0, 3]))
+            assert s.rope_refresh(base, 0) == orc.refresh(None if base == -1 else base, 0)
+        elif S > 0:
+            cwa.sa_sink_update(s.handle, 1, 1)
+            orc.sink_update(_dummy(spec, S * nc), _dummy(spec, S * nc))
+    s.close()
+
+
+def test_buffer_attend_errors():
+    for kw, code in [(dict(max_buffer_chunks=-1), L.SA_ERR_INVALID_ARGUMENT),
+                     (dict(max_buffer_chunks=L.SA_MAX_BUFFER_CHUNKS + 1), L.SA_ERR_INVALID_ARGUMENT)]:
+        assert cwa.sa_config_check(_cfg(**kw)) == code
+    cfg = _cfg(max_buffer_chunks=2)
+    cfg.reserved = 1
+    assert cwa.sa_config_check(cfg) == L.SA_ERR_INVALID_ARGUMENT
+    s = cwa.Stream(_cfg(max_buffer_chunks=0), planning=True)
+    cwa.sa_kv_append(s.handle, 1, 1)                   # sink full
+    with pytest.raises(cwa.SaError) as e:
+        s.buffer_plan(1)
+    assert e.value.status == L.SA_ERR_INVALID_ARGUMENT
+    s = cwa.Stream(_cfg(max_buffer_chunks=3, max_t=8), planning=True)   # F = 2
+    with pytest.raises(cwa.SaError) as e:
+        cwa.sa_buffer_attend(s.handle, None, None, None, 1, None)       # sink not full
+    assert e.value.status == L.SA_ERR_BAD_STATE
+    cwa.sa_kv_append(s.handle, 1, 1)                   # t_next = 2
+    for n, code in [(0, L.SA_ERR_INVALID_ARGUMENT), (4, L.SA_ERR_INVALID_ARGUMENT),
+                    (3, L.SA_OK)]:                      # chunks at t = 2, 4, 6 < 8
+        if code == L.SA_OK:
+            cwa.sa_buffer_attend(s.handle, None, None, None, n, None)
+        else:
+            with pytest.raises(cwa.SaError) as e:
+                cwa.sa_buffer_attend(s.handle, None, None, None, n, None)
+            assert e.value.status == code
+    cwa.sa_kv_append(s.handle, 1, 1)                   # t_next = 4: t = 8 would be needed
+    with pytest.raises(cwa.SaError) as e:
+        cwa.sa_buffer_attend(s.handle, None, None, None, 3, None)
+    assert e.value.status == L.SA_ERR_POSITION_RANGE
 
 
 def test_zero_copy_commit_rules():

@@ -153,6 +153,51 @@ def probe_mfma(torch, cwa, blocks=512, iters=20000, reps=3):
             "operands": "fixed per lane (benign, low toggle)"}
 
 
+def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20):
+    """Moving-buffer attend (n chunks as queries in one call) at steady state: call time,
+    kernel time, and algorithmic FLOPs over each chunk's visible keys (from sa_buffer_plan)."""
+    import numpy as np
+    w = synth.WORKLOADS[name]
+    cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
+                          w.sink_chunks, w.window_chunks, dtype="bf16", max_buffer_chunks=n)
+    s = cwa.Stream(cfg, device="cuda")
+    nc = w.tokens_per_chunk
+    for c in range(w.sink_chunks + w.window_chunks + 1):
+        _, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in synth.chunk_qkv(w, c))
+        s.kv_append(k, v)
+    parts = [synth.chunk_qkv(w, 200 + j) for j in range(n)]
+    q, k, v = (torch.from_numpy(np.concatenate([p_[i] for p_ in parts], axis=1)).to(torch.bfloat16).cuda()
+               for i in range(3))
+    out = torch.empty_like(q)
+    keys = [sum(hi - lo for lo, hi in segs) for segs in s.buffer_plan(n)]
+    flops = sum(4.0 * w.batch * w.heads * w.head_dim * nc * kj for kj in keys)
+    for _ in range(3):
+        s.buffer_attend(q, k, v, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        s.buffer_attend(q, k, v, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    call_ms = a.elapsed_time(b) / steps
+    s.set_option(cwa.SA_OPT_PROFILE, 1)
+    for k_id in range(cwa.SA_K_COUNT):
+        s.profile_read(k_id, reset=True)
+    for _ in range(steps):
+        s.buffer_attend(q, k, v, out=out)
+    attn_ms, na = s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+    rope_ms, nr = s.profile_read(cwa.SA_K_ROPE_APPLY, reset=True)
+    s.close()
+    attn_ms /= max(na, 1)
+    tf = flops / (attn_ms * 1e-3) / 1e12
+    return {"workload": name, "buffer_chunks": n, "tokens_per_call": w.batch * n * nc,
+            "tokens_per_s": w.batch * n * nc / (call_ms * 1e-3), "ms_per_call": call_ms,
+            "attention_ms": attn_ms, "rope_apply_ms_per_chunk": rope_ms / max(nr, 1),
+            "visible_keys_per_chunk": keys, "flops_per_call": flops, "tflops": tf,
+            "frac_of_peak": tf / PEAK_BF16_TFLOPS, "kernel": "chunk_attention_bf16_d128_ppg"}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -247,6 +292,7 @@ def main():
     s.set_option(cwa.SA_OPT_PROFILE, 0)
 
     mfma_probe = probe_mfma(torch, cwa)
+    buffer_res = bench_buffer(torch, cwa, synth)
 
     nk = st["visible_keys"]
     flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk
@@ -312,6 +358,7 @@ def main():
         "chunk_budget_ms": {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)},
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
+        "buffer_attend": buffer_res,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

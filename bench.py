@@ -198,6 +198,51 @@ def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20):
             "frac_of_peak": tf / PEAK_BF16_TFLOPS, "kernel": "chunk_attention_bf16_d128_ppg"}
 
 
+def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 4), steps=20):
+    """Ragged batch: n steady-state streams (each its own cache and position) attended in one
+    launch; per n the call time, attended tokens/s and the attention kernel's TFLOP/s."""
+    import numpy as np
+    w = synth.WORKLOADS[name]
+    cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
+                          w.sink_chunks, w.window_chunks, dtype="bf16")
+    nc = w.tokens_per_chunk
+    streams, qs, ks, vs, outs = [], [], [], [], []
+    for i in range(max(sizes)):
+        s = cwa.Stream(cfg, device="cuda")
+        for c in range(w.sink_chunks + w.window_chunks + i):   # full windows, different positions
+            _, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in synth.chunk_qkv(w, 50 * i + c))
+            s.kv_append(k, v)
+        q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in synth.chunk_qkv(w, 900 + i))
+        streams.append(s); qs.append(q); ks.append(k); vs.append(v); outs.append(torch.empty_like(q))
+    res = {}
+    for n in sizes:
+        args = (streams[:n], qs[:n], ks[:n], vs[:n], outs[:n])
+        for _ in range(3):
+            cwa.sa_batch_attend(*args)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            cwa.sa_batch_attend(*args)
+        b.record()
+        torch.cuda.synchronize()
+        call_ms = a.elapsed_time(b) / steps
+        streams[0].set_option(cwa.SA_OPT_PROFILE, 1)
+        streams[0].profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+        for _ in range(steps):
+            cwa.sa_batch_attend(*args)
+        attn_ms, na = streams[0].profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+        streams[0].set_option(cwa.SA_OPT_PROFILE, 0)
+        attn_ms /= max(na, 1)
+        flops = sum(4.0 * w.batch * w.heads * w.head_dim * nc * st.query()["visible_keys"] for st in streams[:n])
+        tf = flops / (attn_ms * 1e-3) / 1e12
+        res[n] = {"ms_per_call": call_ms, "tokens_per_s": n * w.batch * nc / (call_ms * 1e-3),
+                  "attention_ms": attn_ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+    for s in streams:
+        s.close()
+    return {"workload": name, "streams": res, "kernel": "chunk_attention_bf16_d128_ppg"}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -293,6 +338,7 @@ def main():
 
     mfma_probe = probe_mfma(torch, cwa)
     buffer_res = bench_buffer(torch, cwa, synth)
+    batch_res = bench_batch(torch, cwa, synth)
 
     nk = st["visible_keys"]
     flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk
@@ -359,6 +405,7 @@ def main():
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
         "buffer_attend": buffer_res,
+        "batch_attend": batch_res,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -26,7 +26,7 @@ __all__ = [
     "sa_stream_create", "sa_stream_destroy", "sa_chunk_attend", "sa_kv_append",
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
     "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16",
-    "sa_buffer_attend", "sa_buffer_plan", "Stream",
+    "sa_buffer_attend", "sa_buffer_plan", "sa_batch_attend", "Stream",
     "SA_F32", "SA_BF16", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
     "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
     "SA_K_ROPE_APPLY", "SA_K_CHUNK_ATTENTION", "SA_K_ATTN_COMBINE", "SA_K_KV_APPEND",
@@ -173,6 +173,15 @@ def sa_buffer_plan(handle, n_chunks: int):
     hi = (ctypes.c_int32 * (m * max(n_chunks, 1)))()
     _check(L.load().sa_buffer_plan(handle, n_chunks, n_seg, lo, hi), "sa_buffer_plan")
     return [[(lo[j * m + i], hi[j * m + i]) for i in range(n_seg[j])] for j in range(n_chunks)]
+
+
+def sa_batch_attend(handles, qs, ks, vs, outs, lses=None, stream=None) -> None:
+    """Ragged batch: one attend per handle (each at its own state), one attention launch."""
+    n = len(handles)
+    arr = lambda xs: (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in xs]) if xs is not None else None
+    h = (ctypes.c_void_p * max(n, 1))(*[x.handle if isinstance(x, Stream) else x for x in handles])
+    _check(L.load().sa_batch_attend(n, h, arr(qs), arr(ks), arr(vs), arr(outs), arr(lses),
+                                    _stream_ptr(stream)), "sa_batch_attend")
 
 
 def sa_probe_mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:

@@ -23,6 +23,7 @@ SA_REFRESH_SHIFT_SINK = 1
 SA_MAX_TEMPORAL_PAIRS = 320
 SA_MAX_BUFFER_CHUNKS = 8
 SA_MAX_KEY_SEGMENTS = 4
+SA_MAX_BATCH_STREAMS = 8
 # sa_slot_kind
 SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_WINDOW, SA_SLOT_STAGING = 0, 1, 2, 3
 # sa_kernel_id
@@ -92,6 +93,8 @@ SIGNATURES = {
     "sa_buffer_attend": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P]),
     "sa_buffer_plan": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                       ctypes.POINTER(_I32)]),
+    "sa_batch_attend": (ctypes.c_int, [_I32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                       ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
 }
 
 _lib = None

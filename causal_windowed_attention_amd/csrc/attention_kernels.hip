@@ -394,6 +394,41 @@ struct KeyList {
   int lo[kMaxSegs], hi[kMaxSegs], t0[kMaxSegs], cum[kMaxSegs];
 };
 
+// Where one work item's operands live: rotated Q rows, K and V^T caches, output and
+// LSE, with `rows` query rows per (b, h). A chunk attend or a moving buffer uses the
+// kernel arguments; a ragged batch's group g uses stream g's own buffers.
+struct Bases {
+  const void* q;
+  const void* kcache;
+  const void* vtcache;
+  void* out;
+  float* lse;
+  int rows;
+};
+
+__device__ __forceinline__ Bases bases_shared(const AttnParams& p) {
+  return Bases{p.q, p.kcache, p.vtcache, p.out, p.lse, p.Nc};
+}
+
+// Values read from the argument arrays with a group index are wave-uniform, but the
+// compiler cannot always prove it; without these hints a buffer resource built from
+// such a pointer is wrapped in a readfirstlane loop at every copy.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* x) {
+  const uint64_t u = reinterpret_cast<uint64_t>(x);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u & 0xffffffffu)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  return reinterpret_cast<T*>(lo | (hi << 32));
+}
+
+__device__ __forceinline__ Bases bases_group(const AttnParams& p, int g) {
+  if (!p.ragged) return bases_shared(p);
+  return Bases{uniform_ptr(p.g_q[g]), uniform_ptr(p.g_kc[g]), uniform_ptr(p.g_vt[g]), uniform_ptr(p.g_out[g]),
+               uniform_ptr(p.g_lse[g]), p.group_rows};
+}
+
 // Key tiles [t_begin, t_end) of the single range [0, n_keys) (chunk attend, splits, stream-K).
 __device__ __forceinline__ KeyList keys_single(const AttnParams& p, int t_begin, int t_end) {
   KeyList kl{};
@@ -409,13 +444,13 @@ __device__ __forceinline__ KeyList keys_single(const AttnParams& p, int t_begin,
 // The key ranges of query group g (moving-buffer attend).
 __device__ __forceinline__ KeyList keys_group(const AttnParams& p, int g, int BN) {
   KeyList kl{};
-  kl.n = p.n_seg[g];
+  kl.n = uniform(p.n_seg[g]);
   int c = 0;
 #pragma unroll
   for (int k = 0; k < kMaxSegs; ++k) {
     if (k < kl.n) {
-      kl.lo[k] = p.seg_lo[g][k];
-      kl.hi[k] = p.seg_hi[g][k];
+      kl.lo[k] = uniform(p.seg_lo[g][k]);
+      kl.hi[k] = uniform(p.seg_hi[g][k]);
       kl.t0[k] = kl.lo[k] / BN;
       kl.cum[k] = c;
       c += (kl.hi[k] + BN - 1) / BN - kl.t0[k];
@@ -447,8 +482,9 @@ __device__ __forceinline__ int key_tile(const KeyList& kl, int i, int& lo, int& 
 // single-range form is a separate instantiation so the chunk attend's kernel
 // carries none of the range bookkeeping.
 template <int D, bool GROUPS>
-__device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int bh, int q_base, int q_end,
-                                           int t_begin, int t_end, const KeyList& kl, int mode, int slot) {
+__device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs, char* smem, int bh, int q_base,
+                                           int q_end, int t_begin, int t_end, const KeyList& kl, int mode,
+                                           int slot) {
   using G = Bf16Geom<D>;
   constexpr int NW = 8, STAGES = kPpStages;
   constexpr int BN = G::BN;
@@ -477,14 +513,14 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
     }
   };
 
-  const char* kbase = static_cast<const char*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
-  const char* vbase = static_cast<const char*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
+  const char* kbase = static_cast<const char*>(bs.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
+  const char* vbase = static_cast<const char*>(bs.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
 
   const int q = q_base + wave * 32 + l32;
   bf16x8 bq[KSTEPS];
   {
     const int qrow = min(q, q_end - 1);
-    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
+    const __bf16* qsrc = static_cast<const __bf16*>(bs.q) + (static_cast<size_t>(bh) * bs.rows + qrow) * D;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
   }
@@ -669,7 +705,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
   if (q >= q_end) return;
   const int b = bh / p.H, h = bh - b * p.H;
   if (mode == kPpFinal) {
-    __bf16* dst = static_cast<__bf16*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
+    __bf16* dst = static_cast<__bf16*>(bs.out) + ((static_cast<size_t>(b) * bs.rows + q) * p.H + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -680,7 +716,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, char* smem, int 
         for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[dt][4 * jj + e] * inv);
         *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
       }
-    if (p.lse != nullptr && g == 0) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
+    if (bs.lse != nullptr && g == 0) bs.lse[static_cast<size_t>(bh) * bs.rows + q] = lse2 * kLn2;
   } else {
     const size_t row = (static_cast<size_t>(slot) * p.B * p.H + bh) * p.Nc + q;
     float* dst = p.part_o + row * D;
@@ -709,11 +745,12 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
   __shared__ __attribute__((aligned(1024))) char smem[PpSmem<D>::BYTES];
   if constexpr (GROUPS) {                        // moving buffer: the q-tile's chunk picks the keys
     const int w = xcd_remap(blockIdx.x, p.B * p.H * p.q_tiles);
-    const int qt = w % p.q_tiles, bh = w / p.q_tiles;
-    const int grp = qt / p.group_qtiles;
-    const int q_base = grp * p.group_rows + (qt - grp * p.group_qtiles) * (8 * 32);
-    pp_segment<D, true>(p, smem, bh, q_base, (grp + 1) * p.group_rows, 0, 0, keys_group(p, grp, Bf16Geom<D>::BN),
-                        kPpFinal, 0);
+    const int qt = uniform(w % p.q_tiles), bh = uniform(w / p.q_tiles);
+    const int grp = uniform(qt / p.group_qtiles);
+    const int qtg = qt - grp * p.group_qtiles;
+    const int row0 = p.ragged ? 0 : grp * p.group_rows;   // a ragged group has rows of its own
+    pp_segment<D, true>(p, bases_group(p, grp), smem, bh, row0 + qtg * (8 * 32), row0 + p.group_rows, 0, 0,
+                        keys_group(p, grp, Bf16Geom<D>::BN), kPpFinal, 0);
     return;
   }
   const bool sk = p.sk_groups > 0;
@@ -746,7 +783,7 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
       slot = split;
       it = r1;
     }
-    pp_segment<D, false>(p, smem, bh, qt * (8 * 32), p.Nc, t0, t1, none, mode, slot);
+    pp_segment<D, false>(p, bases_shared(p), smem, bh, qt * (8 * 32), p.Nc, t0, t1, none, mode, slot);
     if (it < r1) __syncthreads();                // the next segment reuses every LDS stage
   }
 }
@@ -799,22 +836,24 @@ __global__ __launch_bounds__(64) void chunk_attention_f32(AttnParams p) {
   const int bh = rest / p.kv_splits;
   const int t_begin = static_cast<int>((static_cast<int64_t>(split) * p.key_tiles) / p.kv_splits);
   const int t_end = static_cast<int>((static_cast<int64_t>(split + 1) * p.key_tiles) / p.kv_splits);
-  const float* kbase = static_cast<const float*>(p.kcache) + static_cast<size_t>(bh) * p.k_bh_stride;
-  const float* vbase = static_cast<const float*>(p.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride;
-
   int q_base = qt * kF32BlockM, q_end = p.Nc;
   KeyList kl;
-  if (p.n_groups > 0) {                          // moving buffer: the q-tile's chunk picks the keys
+  Bases bs = bases_shared(p);
+  if (p.n_groups > 0) {                          // moving buffer or ragged batch: the q-tile's group
     const int grp = qt / p.group_qtiles;
-    q_base = grp * p.group_rows + (qt - grp * p.group_qtiles) * kF32BlockM;
-    q_end = (grp + 1) * p.group_rows;
+    const int row0 = p.ragged ? 0 : grp * p.group_rows;
+    q_base = row0 + (qt - grp * p.group_qtiles) * kF32BlockM;
+    q_end = row0 + p.group_rows;
     kl = keys_group(p, grp, BN);
+    bs = bases_group(p, grp);
   } else {
     kl = keys_single(p, t_begin, t_end);
   }
+  const float* kbase = static_cast<const float*>(bs.kcache) + static_cast<size_t>(bh) * p.k_bh_stride;
+  const float* vbase = static_cast<const float*>(bs.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride;
   const int q = q_base + lane;
   const int qrow = min(q, q_end - 1);
-  const float* qsrc = static_cast<const float*>(p.q) + (static_cast<size_t>(bh) * p.Nc + qrow) * D;
+  const float* qsrc = static_cast<const float*>(bs.q) + (static_cast<size_t>(bh) * bs.rows + qrow) * D;
   float qr[D], o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -854,10 +893,10 @@ __global__ __launch_bounds__(64) void chunk_attention_f32(AttnParams p) {
   const float lse2 = m + __log2f(l);
   const int b = bh / p.H, h = bh - b * p.H;
   if (p.kv_splits == 1) {
-    float* dst = static_cast<float*>(p.out) + ((static_cast<size_t>(b) * p.Nc + q) * p.H + h) * D;
+    float* dst = static_cast<float*>(bs.out) + ((static_cast<size_t>(b) * bs.rows + q) * p.H + h) * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
-    if (p.lse != nullptr) p.lse[static_cast<size_t>(bh) * p.Nc + q] = lse2 * kLn2;
+    if (bs.lse != nullptr) bs.lse[static_cast<size_t>(bh) * bs.rows + q] = lse2 * kLn2;
   } else {
     const size_t row = (static_cast<size_t>(split) * p.B * p.H + bh) * p.Nc + q;
 #pragma unroll

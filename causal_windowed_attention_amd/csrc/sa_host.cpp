@@ -856,6 +856,94 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
   return SA_OK;
 }
 
+sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* const* q, const void* const* k,
+                          const void* const* v, void* const* out, float* const* lse, void* stream) {
+  if (n < 1 || n > SA_MAX_BATCH_STREAMS || streams == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < n; ++i)
+    if (streams[i] == nullptr) return SA_ERR_INVALID_ARGUMENT;
+  const sa_stream* s0 = streams[0];
+  const Derived& d = s0->d;
+  const bool planning = s0->planning();
+  for (int i = 0; i < n; ++i) {
+    const sa_stream* si = streams[i];
+    for (int j = 0; j < i; ++j)
+      if (streams[j] == si) return SA_ERR_INVALID_ARGUMENT;     // one entry per handle
+    const Derived& e = si->d;
+    if (si->planning() != planning || e.B != d.B || e.H != d.H || e.D != d.D || e.Hf != d.Hf || e.Wf != d.Wf ||
+        e.F != d.F || e.S != d.S || e.W != d.W || e.NB != d.NB || e.dtype != d.dtype || e.dt != d.dt ||
+        e.dh != d.dh || e.dw != d.dw || e.theta != d.theta || e.scale != d.scale || e.max_t != d.max_t)
+      return SA_ERR_INVALID_ARGUMENT;
+    if (!planning) {
+      if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return SA_ERR_INVALID_ARGUMENT;
+      if (q[i] == nullptr || k[i] == nullptr || v[i] == nullptr || out[i] == nullptr) return SA_ERR_INVALID_ARGUMENT;
+      if (!aligned16(q[i]) || !aligned16(k[i]) || !aligned16(v[i]) || !aligned16(out[i]) ||
+          (lse != nullptr && (reinterpret_cast<uintptr_t>(lse[i]) & 3u) != 0))
+        return SA_ERR_INVALID_ARGUMENT;
+    }
+    const sa_status st = positions_ok(si, static_cast<int64_t>(si->t_next) + e.F);
+    if (st != SA_OK) return st;
+  }
+  const int bm = d.dtype == SA_BF16 ? sa::kBf16BlockMWide : sa::kF32BlockM;
+  const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
+  const int group_qtiles = (d.Nc + bm - 1) / bm;
+  if (!planning) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    AttnParams ap;
+    std::memset(&ap, 0, sizeof(ap));
+    for (int i = 0; i < n; ++i) {                // stage each entry's chunk in its own workspace
+      sa_stream* si = streams[i];
+      RopeWriteParams rp;
+      base_write_params(si, &rp);
+      rp.q = q[i]; rp.k = k[i]; rp.v = v[i];
+      rp.qrot = si->qscratch();
+      rp.row0 = si->staging_slot() * d.Nc;
+      fill_temporal(d, si->t_next, d.F, rp.t_cs);
+      const sa_status st = timed(si, SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply(rp, d.dtype, hs); });
+      if (st != SA_OK) return st;
+      ap.g_q[i] = si->qscratch();
+      ap.g_kc[i] = si->kcache();
+      ap.g_vt[i] = si->vtcache();
+      ap.g_out[i] = out[i];
+      ap.g_lse[i] = lse != nullptr ? lse[i] : nullptr;
+      ap.n_seg[i] = 1;
+      ap.seg_lo[i][0] = 0;
+      ap.seg_hi[i][0] = si->visible_chunks() * d.Nc;   // the physical prefix an attend reads
+    }
+    ap.k_bh_stride = static_cast<int64_t>(d.key_stride) * d.D;
+    ap.vt_bh_stride = static_cast<int64_t>(d.D) * d.key_stride;
+    ap.key_stride = d.key_stride;
+    ap.n_keys = (d.buf_slot0 + d.NB) * d.Nc;
+    ap.Nc = d.Nc;
+    ap.B = d.B; ap.H = d.H; ap.D = d.D;
+    ap.variant = d.dtype == SA_BF16 ? 3 : 0;
+    ap.q_rows_per_block = bm;
+    ap.q_tiles = n * group_qtiles;
+    ap.kv_splits = 1;
+    ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    ap.n_groups = n;
+    ap.group_rows = d.Nc;
+    ap.group_qtiles = group_qtiles;
+    ap.ragged = 1;
+    int max_tiles = 0;
+    for (int i = 0; i < n; ++i) max_tiles = std::max(max_tiles, (ap.seg_hi[i][0] + bn - 1) / bn);
+    ap.key_tiles = max_tiles;
+    const sa_status st = timed(streams[0], SA_K_CHUNK_ATTENTION, hs,
+                               [&] { return sa::launch_chunk_attention(ap, d.dtype, hs); });
+    if (st != SA_OK) return st;
+  }
+  for (int i = 0; i < n; ++i) {                  // as after sa_chunk_attend
+    sa_stream* si = streams[i];
+    si->staged_valid = true;
+    si->staged_t = si->t_next;
+    si->staged_slot = si->staging_slot();
+    si->last_q_tiles = group_qtiles;
+    si->last_kv_splits = 1;
+    si->last_key_tiles = (si->visible_chunks() * d.Nc + bn - 1) / bn;
+    si->last_sk_groups = 0;
+  }
+  return SA_OK;
+}
+
 sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* stream) {
   if (d_out == nullptr || blocks < 1 || blocks > (1 << 20) || iters < 1) return SA_ERR_INVALID_ARGUMENT;
   return sa::launch_mfma_probe(d_out, blocks, iters, static_cast<hipStream_t>(stream)) == hipSuccess

@@ -93,6 +93,14 @@ struct AttnParams {
   int32_t n_seg[kMaxGroups];
   int32_t seg_lo[kMaxGroups][kMaxSegs];
   int32_t seg_hi[kMaxGroups][kMaxSegs];
+  // ragged = 1 (a ragged batch): group g is an independent stream with its own
+  // bases below and query rows [0, group_rows); the shared fields above are unused
+  int32_t ragged;
+  const void* g_q[kMaxGroups];
+  const void* g_kc[kMaxGroups];
+  const void* g_vt[kMaxGroups];
+  void* g_out[kMaxGroups];
+  float* g_lse[kMaxGroups];
 };
 
 constexpr int kMaxSkGroups = 512;

@@ -113,6 +113,7 @@ typedef struct sa_config {
 #define SA_MAX_TEMPORAL_PAIRS 320
 #define SA_MAX_BUFFER_CHUNKS 8
 #define SA_MAX_KEY_SEGMENTS 4
+#define SA_MAX_BATCH_STREAMS 8
 
 /* Host-side stream state (D3) and the plan of the last attend (D4). */
 typedef struct sa_state {
@@ -237,6 +238,20 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
  */
 sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const void* v, int32_t n_chunks,
                            void* out, float* lse, void* stream);
+
+/*
+ * Ragged batch (StreamDiffusionV2 Stream-Batch: one launch serving several
+ * streams, each at its own chunk index and position): the same as calling
+ * sa_chunk_attend(streams[i], q[i], k[i], v[i], out[i], lse[i]) for i < n, but
+ * with one attention launch over all entries, each with its own visible keys.
+ * 1 <= n <= SA_MAX_BATCH_STREAMS distinct handles created from equal configs
+ * (all planning handles or none); lse may be NULL, as may any lse[i]. Every
+ * entry is validated before any launch: on an error no state changes. Each
+ * handle's profiler records its own RoPE launch; the attention launch is
+ * recorded on streams[0].
+ */
+sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* const* q, const void* const* k,
+                          const void* const* v, void* const* out, float* const* lse, void* stream);
 
 /*
  * The key segments a sa_buffer_attend of n_chunks would read now (inspection,

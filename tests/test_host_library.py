@@ -363,3 +363,38 @@ def test_mfma_probe_argument_errors():
     assert lib.sa_probe_mfma_bf16(fake, 0, 1, None) == L.SA_ERR_INVALID_ARGUMENT
     assert lib.sa_probe_mfma_bf16(fake, 1, 0, None) == L.SA_ERR_INVALID_ARGUMENT
     assert lib.sa_probe_mfma_bf16(fake, (1 << 20) + 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+
+
+def test_batch_attend_planning_semantics_and_errors():
+    """A ragged batch is n chunk attends: each handle stages its chunk (a zero-copy commit
+    follows), plans are per handle; every entry is validated before anything changes."""
+    cfg = _cfg(window_chunks=3, max_t=40)
+    hs = [cwa.Stream(cfg, planning=True) for _ in range(4)]
+    for i, s in enumerate(hs):                       # different states: 0, 2, 4 and 6 commits
+        for _ in range(2 * i):
+            cwa.sa_kv_append(s.handle, 1, 1)
+    cwa.sa_batch_attend(hs, None, None, None, None)
+    for s in hs:
+        st = s.query()
+        assert st["staged_valid"] == 1
+        assert st["last_key_tiles"] == -(-st["visible_keys"] // 64) and st["last_kv_splits"] == 1
+        s.kv_append(None, None)                      # zero-copy commit of the staged chunk
+    t_before = [s.query()["t_next"] for s in hs]
+    for bad, code in [([], L.SA_ERR_INVALID_ARGUMENT), (hs + hs[:1], L.SA_ERR_INVALID_ARGUMENT),
+                      ([hs[0], cwa.Stream(_cfg(window_chunks=2, max_t=40), planning=True)],
+                       L.SA_ERR_INVALID_ARGUMENT)]:
+        with pytest.raises(cwa.SaError) as e:
+            cwa.sa_batch_attend(bad, None, None, None, None)
+        assert e.value.status == code
+    many = [cwa.Stream(cfg, planning=True) for _ in range(L.SA_MAX_BATCH_STREAMS + 1)]
+    with pytest.raises(cwa.SaError) as e:
+        cwa.sa_batch_attend(many, None, None, None, None)
+    assert e.value.status == L.SA_ERR_INVALID_ARGUMENT
+    while hs[3].query()["t_next"] + cfg.frames_per_chunk <= cfg.max_t:   # push one stream to the end
+        cwa.sa_kv_append(hs[3].handle, 1, 1)
+    staged = [s.query()["staged_valid"] for s in hs]
+    with pytest.raises(cwa.SaError) as e:
+        cwa.sa_batch_attend(hs, None, None, None, None)
+    assert e.value.status == L.SA_ERR_POSITION_RANGE
+    assert [s.query()["staged_valid"] for s in hs] == staged      # nothing changed
+    assert [s.query()["t_next"] for s in hs[:3]] == t_before[:3]

@@ -145,35 +145,46 @@ class _Common:
             if a.shape != (s.batch, n, s.heads, s.head_dim):
                 raise StreamError("invalid", f"expected [B, {n}, H, D], got {a.shape}")
 
-    def buffer_attend(self, q, k, v, rows=None, heads=None):
-        """Moving-buffer attend (StreamDiT: a buffer of consecutive chunks denoised together,
-        with window attention). q, k, v hold n consecutive chunks [B, n*Nc, H, D] that follow
-        the committed stream; buffer chunk j sits at t_next + j*F. Chunk j attends to what an
-        attend would see once buffer chunks 0..j-1 were committed: the sink, the last W chunks
-        of (committed window, buffer 0..j-1), and itself -- a block-banded chunk mask. Needs a
-        full sink (else earlier buffer chunks would become sink chunks). State unchanged.
-        rows: global query rows in [0, n*Nc). Returns O [B, n*Nc, H, D], LSE [B, H, n*Nc]."""
+    def buffer_attend(self, q, k, v, rows=None, heads=None, steps=False):
+        """Several chunks that follow the committed stream, attended in one call; q, k, v hold
+        n consecutive chunks [B, n*Nc, H, D] and buffer chunk j sits at t_next + j*F.
+
+        steps=False, the moving buffer (StreamDiT: a buffer of consecutive chunks denoised
+        together, with window attention): chunk j attends to what an attend would see once
+        buffer chunks 0..j-1 were committed -- the sink, the last W chunks of (committed window,
+        buffer 0..j-1), and itself: a block-banded chunk mask. Needs a full sink (else earlier
+        buffer chunks would become sink chunks).
+
+        steps=True, Stream-Batch over denoising steps (StreamDiffusionV2: chunks in flight at
+        different denoising steps form one batch): no buffer chunk is committed yet, so chunk j
+        attends to the committed context an attend would see now (sink and window) and itself.
+
+        State unchanged. rows: global query rows in [0, n*Nc).
+        Returns O [B, n*Nc, H, D], LSE [B, H, n*Nc]."""
         s = self.spec
         nc = s.tokens_per_chunk
         if q.ndim != 4 or q.shape[1] == 0 or q.shape[1] % nc:
             raise StreamError("invalid", f"buffer of {q.shape[1] if q.ndim == 4 else '?'} tokens is not whole chunks")
         n = q.shape[1] // nc
         self._check_chunk(q, k, v, n_tokens=n * nc)
-        if self.sink_fill < s.sink_chunks:
-            raise StreamError("bad_state", "a buffer attend needs a full sink")
+        if not steps and self.sink_fill < s.sink_chunks:
+            raise StreamError("bad_state", "a moving-buffer attend needs a full sink")
         B, H, D = s.batch, s.heads, s.head_dim
         out = np.full((B, n * nc, H, D), np.nan)
         lse = np.full((B, H, n * nc), np.nan)
         tmp = copy.deepcopy(self)
         for j in range(n):
             sl = slice(j * nc, (j + 1) * nc)
+            if steps:                                # same committed context, j chunks further on
+                tmp = copy.deepcopy(self)
+                tmp.t_next = self.t_next + j * s.frames_per_chunk
             r = None if rows is None else [x - j * nc for x in rows if j * nc <= x < (j + 1) * nc]
             if r is None or r:
                 o, lj = tmp.attend(q[:, sl], k[:, sl], v[:, sl], rows=r, heads=heads)
                 out[:, sl], lse[:, :, sl] = o, lj
             else:
                 tmp._check_positions()
-            if j + 1 < n:
+            if not steps and j + 1 < n:
                 tmp.append(k[:, sl], v[:, sl])
         return out, lse
 

@@ -11,6 +11,7 @@
   without it, only the sink logits move;
 * storage emulation stores bf16-exact values and stays close to fp64.
 """
+import copy
 import json
 import math
 import os
@@ -304,10 +305,11 @@ def test_synth_inputs():
     assert synth.source_id(3, d) != 3 and synth.source_id(499, d) == 499
 
 
-def _explicit_buffer_attend(spec, committed, t_next, q, k, v):
+def _explicit_buffer_attend(spec, committed, t_next, q, k, v, steps=False):
     """Buffer attend from an explicit chunk list: committed = [(t0, k, v)] in commit order (the
     first S are the sink); buffer chunk j at t_next + j*F sees the sink, the last W of
-    (committed window chunks, buffer chunks 0..j-1) and itself. Scalar-loop attention."""
+    (committed window chunks, buffer chunks 0..j-1) and itself -- or, with steps, the sink,
+    the last W committed window chunks and itself. Scalar-loop attention."""
     S, W, F, nc = spec.sink_chunks, spec.window_chunks, spec.frames_per_chunk, spec.tokens_per_chunk
     f, y, x = token_coords(nc, spec.frame_h, spec.frame_w)
     rot = lambda u, t0: rope3d(np.transpose(u, (0, 2, 1, 3)), t0 + f, y, x, spec.rope, spec.theta)
@@ -317,8 +319,8 @@ def _explicit_buffer_attend(spec, committed, t_next, q, k, v):
     out = np.empty(q.shape)
     scale = 1.0 / np.sqrt(spec.head_dim)
     for j in range(n):
-        prior = window + buf[:j]
-        vis = sink + (prior[len(prior) - W:] if W else []) + [buf[j]]
+        prior = window if steps else window + buf[:j]
+        vis = sink + (prior[max(0, len(prior) - W):] if W else []) + [buf[j]]
         K = np.concatenate([rot(kk, t0) for t0, kk, _ in vis], axis=2)
         V = np.concatenate([np.transpose(vv, (0, 2, 1, 3)) for _, _, vv in vis], axis=2)
         Q = rot(q[:, j * nc:(j + 1) * nc], t_next + j * F)
@@ -329,8 +331,10 @@ def _explicit_buffer_attend(spec, committed, t_next, q, k, v):
     return out
 
 
-@pytest.mark.parametrize("S,W,n,commits", [(1, 2, 4, 5), (0, 1, 3, 2), (2, 0, 2, 3), (1, 3, 2, 1)])
-def test_buffer_attend_matches_explicit_windows(S, W, n, commits):
+@pytest.mark.parametrize("S,W,n,commits", [(1, 2, 4, 5), (0, 1, 3, 2), (2, 0, 2, 3), (1, 3, 2, 1),
+                                           (1, 3, 3, 3)])
+@pytest.mark.parametrize("steps", [False, True])
+def test_buffer_attend_matches_explicit_windows(S, W, n, commits, steps):
     """Pin: each buffer chunk's visible set is enumerated directly, not through the oracle's
     ring or history bookkeeping; both formulations must reproduce it."""
     spec = StreamSpec(batch=1, heads=2, head_dim=8, frame_h=2, frame_w=2, frames_per_chunk=1,
@@ -343,13 +347,37 @@ def test_buffer_attend_matches_explicit_windows(S, W, n, commits):
         ring.append(k, v)
         committed.append((c * spec.frames_per_chunk, k, v))
     q, k, v = _rand_chunk(spec, 7, n_tokens=n * spec.tokens_per_chunk)
-    want = _explicit_buffer_attend(spec, committed, hist.t_next, q, k, v)
+    want = _explicit_buffer_attend(spec, committed, hist.t_next, q, k, v, steps=steps)
     before = hist.state()
     for orc in (hist, ring):
-        got, lse = orc.buffer_attend(q, k, v)
+        got, lse = orc.buffer_attend(q, k, v, steps=steps)
         np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
         assert np.all(np.isfinite(lse))
     assert hist.state() == before                    # a buffer attend changes nothing
+
+
+def test_steps_buffer_partial_sink_and_first_chunk():
+    """Stream-Batch over denoising steps: chunk 0 of the batch is exactly an attend; a partial
+    sink is allowed (the chunks see the committed sink chunks and themselves); the banded
+    buffer's chunk 0 agrees with it, later chunks differ once the band admits chunk 0."""
+    spec = _tiny_spec(sink_chunks=2, window_chunks=2)
+    nc = spec.tokens_per_chunk
+    orc = HistoryOracle(spec)
+    _, k, v = _rand_chunk(spec, 0)
+    orc.append(k, v)                                 # one of two sink chunks
+    q, k, v = _rand_chunk(spec, 1, n_tokens=3 * nc)
+    o, _ = orc.buffer_attend(q, k, v, steps=True)
+    tmp = copy.deepcopy(orc)
+    for j in range(3):
+        o1, _ = tmp.attend(q[:, j * nc:(j + 1) * nc], k[:, j * nc:(j + 1) * nc], v[:, j * nc:(j + 1) * nc])
+        np.testing.assert_allclose(o[:, j * nc:(j + 1) * nc], o1, rtol=0, atol=1e-12)
+        tmp.t_next += spec.frames_per_chunk          # same context, next position
+    _, k2, v2 = _rand_chunk(spec, 2)
+    orc.append(k2, v2)                               # the sink is full now
+    ob, _ = orc.buffer_attend(q, k, v)
+    os_, _ = orc.buffer_attend(q, k, v, steps=True)
+    np.testing.assert_allclose(ob[:, :nc], os_[:, :nc], rtol=0, atol=1e-12)
+    assert np.abs(ob[:, nc:] - os_[:, nc:]).max() > 1e-3
 
 
 def test_buffer_attend_single_chunk_is_attend_and_rows():

@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deadline-ms", type=float, default=1.0,
+                    help="per-call deadline for the ragged-batch size choice (an example SLO)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget for the oracle baseline sample")
     ap.add_argument("--profile-steps", type=int, default=20)
@@ -153,9 +155,10 @@ def probe_mfma(torch, cwa, blocks=512, iters=20000, reps=3):
             "operands": "fixed per lane (benign, low toggle)"}
 
 
-def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20):
-    """Moving-buffer attend (n chunks as queries in one call) at steady state: call time,
-    kernel time, and algorithmic FLOPs over each chunk's visible keys (from sa_buffer_plan)."""
+def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20, steps_mode=False):
+    """Buffer attend (n chunks as queries in one call; the moving buffer, or with steps_mode
+    Stream-Batch over denoising steps) at steady state: call time, kernel time, and
+    algorithmic FLOPs over each chunk's visible keys (from sa_buffer_plan)."""
     import numpy as np
     w = synth.WORKLOADS[name]
     cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
@@ -169,15 +172,15 @@ def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20):
     q, k, v = (torch.from_numpy(np.concatenate([p_[i] for p_ in parts], axis=1)).to(torch.bfloat16).cuda()
                for i in range(3))
     out = torch.empty_like(q)
-    keys = [sum(hi - lo for lo, hi in segs) for segs in s.buffer_plan(n)]
+    keys = [sum(hi - lo for lo, hi in segs) for segs in s.buffer_plan(n, steps=steps_mode)]
     flops = sum(4.0 * w.batch * w.heads * w.head_dim * nc * kj for kj in keys)
     for _ in range(3):
-        s.buffer_attend(q, k, v, out=out)
+        s.buffer_attend(q, k, v, out=out, steps=steps_mode)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
-        s.buffer_attend(q, k, v, out=out)
+        s.buffer_attend(q, k, v, out=out, steps=steps_mode)
     b.record()
     torch.cuda.synchronize()
     call_ms = a.elapsed_time(b) / steps
@@ -185,22 +188,32 @@ def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20):
     for k_id in range(cwa.SA_K_COUNT):
         s.profile_read(k_id, reset=True)
     for _ in range(steps):
-        s.buffer_attend(q, k, v, out=out)
+        s.buffer_attend(q, k, v, out=out, steps=steps_mode)
     attn_ms, na = s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
     rope_ms, nr = s.profile_read(cwa.SA_K_ROPE_APPLY, reset=True)
     s.close()
     attn_ms /= max(na, 1)
     tf = flops / (attn_ms * 1e-3) / 1e12
-    return {"workload": name, "buffer_chunks": n, "tokens_per_call": w.batch * n * nc,
+    return {"workload": name, "mode": "steps" if steps_mode else "moving buffer",
+            "buffer_chunks": n, "tokens_per_call": w.batch * n * nc,
             "tokens_per_s": w.batch * n * nc / (call_ms * 1e-3), "ms_per_call": call_ms,
             "attention_ms": attn_ms, "rope_apply_ms_per_chunk": rope_ms / max(nr, 1),
             "visible_keys_per_chunk": keys, "flops_per_call": flops, "tflops": tf,
             "frac_of_peak": tf / PEAK_BF16_TFLOPS, "kernel": "chunk_attention_bf16_d128_ppg"}
 
 
-def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 4), steps=20):
+def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), steps=20, deadline_ms=1.0,
+                calls=200):
     """Ragged batch: n steady-state streams (each its own cache and position) attended in one
-    launch; per n the call time, attended tokens/s and the attention kernel's TFLOP/s."""
+    launch; per n the call time, attended tokens/s and the attention kernel's TFLOP/s.
+
+    Then a deadline-driven choice of n: a least-squares latency model ms(n) = a + b*waves(n)
+    over the measured sizes, waves(n) = ceil(n * workgroups per stream / CUs) (one 256-row
+    workgroup per CU at a time), gives the largest n whose predicted call time meets
+    deadline_ms; that
+    batch runs `calls` times, each call timed by its own events, and the miss rate (calls over
+    the deadline) and the mean jitter (mean |difference| of consecutive call times) are
+    reported."""
     import numpy as np
     w = synth.WORKLOADS[name]
     cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
@@ -238,9 +251,32 @@ def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 4), steps=20):
         tf = flops / (attn_ms * 1e-3) / 1e12
         res[n] = {"ms_per_call": call_ms, "tokens_per_s": n * w.batch * nc / (call_ms * 1e-3),
                   "attention_ms": attn_ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = w.batch * w.heads * streams[0].query()["last_q_tiles"]      # workgroups per stream
+    waves = lambda n: -(-n * wg // cus)
+    xs = np.array([waves(n) for n in sizes], dtype=np.float64)
+    ys = np.array([res[n]["ms_per_call"] for n in sizes])
+    slope, icept = np.polyfit(xs, ys, 1)
+    fits = [n for n in range(1, max(sizes) + 1) if icept + slope * waves(n) <= deadline_ms]
+    n = max(fits) if fits else 1
+    args = (streams[:n], qs[:n], ks[:n], vs[:n], outs[:n])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record()
+        cwa.sa_batch_attend(*args)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    sched = {"deadline_ms_per_call": deadline_ms,
+             "model_ms": {"intercept": icept, "per_wave": slope, "workgroups_per_stream": wg, "cus": cus},
+             "chosen_streams": n, "predicted_ms": icept + slope * waves(n), "calls": calls,
+             "p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)),
+             "miss_rate": float(np.mean(t > deadline_ms)), "mean_jitter_ms": float(np.mean(np.abs(np.diff(t)))),
+             "tokens_per_s": n * w.batch * nc / (float(np.mean(t)) * 1e-3)}
     for s in streams:
         s.close()
-    return {"workload": name, "streams": res, "kernel": "chunk_attention_bf16_d128_ppg"}
+    return {"workload": name, "streams": res, "deadline_schedule": sched,
+            "kernel": "chunk_attention_bf16_d128_ppg"}
 
 
 def main():
@@ -338,7 +374,8 @@ def main():
 
     mfma_probe = probe_mfma(torch, cwa)
     buffer_res = bench_buffer(torch, cwa, synth)
-    batch_res = bench_batch(torch, cwa, synth)
+    steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
+    batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
 
     nk = st["visible_keys"]
     flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk
@@ -405,6 +442,7 @@ def main():
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
         "buffer_attend": buffer_res,
+        "steps_attend": steps_res,
         "batch_attend": batch_res,
     }
     if not args.no_cpu_baseline:

@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 from . import _lib as L
 from ._lib import (SA_BF16, SA_F32, SA_K_ATTN_COMBINE, SA_K_CHUNK_ATTENTION, SA_K_COUNT,
                    SA_K_KV_APPEND, SA_K_ROPE_APPLY, SA_K_ROPE_REFRESH, SA_K_SINK_UPDATE,
-                   SA_OK, SA_OPT_ATTN_VARIANT, SA_OPT_KV_SPLITS, SA_OPT_SCHEDULE, SA_OPT_PROFILE, SA_REFRESH_SHIFT_SINK,
+                   SA_BUFFER_STEPS, SA_OK, SA_OPT_ATTN_VARIANT, SA_OPT_KV_SPLITS, SA_OPT_SCHEDULE, SA_OPT_PROFILE, SA_REFRESH_SHIFT_SINK,
                    SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_STAGING, SA_SLOT_WINDOW, sa_config)
 
 __all__ = [
@@ -160,18 +160,18 @@ def sa_profile_read(handle, kernel_id: int, reset: bool = False) -> Tuple[float,
     return ms.value, n.value
 
 
-def sa_buffer_attend(handle, q, k, v, n_chunks: int, out, lse=None, stream=None) -> None:
-    _check(L.load().sa_buffer_attend(handle, _ptr(q), _ptr(k), _ptr(v), n_chunks, _ptr(out), _ptr(lse),
+def sa_buffer_attend(handle, q, k, v, n_chunks: int, out, lse=None, stream=None, flags: int = 0) -> None:
+    _check(L.load().sa_buffer_attend(handle, _ptr(q), _ptr(k), _ptr(v), n_chunks, flags, _ptr(out), _ptr(lse),
                                      _stream_ptr(stream)), "sa_buffer_attend")
 
 
-def sa_buffer_plan(handle, n_chunks: int):
+def sa_buffer_plan(handle, n_chunks: int, flags: int = 0):
     """Per buffer chunk, the [lo, hi) physical key-row ranges a buffer attend would read."""
     m = L.SA_MAX_KEY_SEGMENTS
     n_seg = (ctypes.c_int32 * max(n_chunks, 1))()
     lo = (ctypes.c_int32 * (m * max(n_chunks, 1)))()
     hi = (ctypes.c_int32 * (m * max(n_chunks, 1)))()
-    _check(L.load().sa_buffer_plan(handle, n_chunks, n_seg, lo, hi), "sa_buffer_plan")
+    _check(L.load().sa_buffer_plan(handle, n_chunks, flags, n_seg, lo, hi), "sa_buffer_plan")
     return [[(lo[j * m + i], hi[j * m + i]) for i in range(n_seg[j])] for j in range(n_chunks)]
 
 
@@ -237,8 +237,9 @@ class Stream:
         sa_chunk_attend(self.handle, q, k, v, out, lse, stream)
         return out
 
-    def buffer_attend(self, q, k, v, out=None, lse=None, stream=None, n_chunks=None):
-        """Moving-buffer attend: q, k, v hold n consecutive chunks [B, n*Nc, H, D]."""
+    def buffer_attend(self, q, k, v, out=None, lse=None, stream=None, n_chunks=None, steps=False):
+        """Buffer attend: q, k, v hold n consecutive chunks [B, n*Nc, H, D]; steps selects
+        Stream-Batch over denoising steps instead of the moving buffer."""
         if n_chunks is None:
             if q is None or q.shape[1] % self.Nc:
                 raise ValueError("buffer_attend: q must hold whole chunks (or pass n_chunks)")
@@ -255,11 +256,12 @@ class Stream:
             if tuple(lse.shape) != (self.cfg.batch, self.cfg.heads, rows) or \
                     lse.dtype != torch.float32 or not lse.is_contiguous():
                 raise ValueError("lse: expected contiguous float32 [B, H, n*Nc]")
-        sa_buffer_attend(self.handle, q, k, v, n_chunks, out, lse, stream)
+        sa_buffer_attend(self.handle, q, k, v, n_chunks, out, lse, stream,
+                         L.SA_BUFFER_STEPS if steps else 0)
         return out
 
-    def buffer_plan(self, n_chunks: int):
-        return sa_buffer_plan(self.handle, n_chunks)
+    def buffer_plan(self, n_chunks: int, steps=False):
+        return sa_buffer_plan(self.handle, n_chunks, L.SA_BUFFER_STEPS if steps else 0)
 
     def kv_append(self, k=None, v=None, stream=None):
         if k is not None or v is not None:

@@ -24,6 +24,7 @@ SA_MAX_TEMPORAL_PAIRS = 320
 SA_MAX_BUFFER_CHUNKS = 8
 SA_MAX_KEY_SEGMENTS = 4
 SA_MAX_BATCH_STREAMS = 8
+SA_BUFFER_STEPS = 1
 # sa_slot_kind
 SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_WINDOW, SA_SLOT_STAGING = 0, 1, 2, 3
 # sa_kernel_id
@@ -90,8 +91,8 @@ SIGNATURES = {
     "sa_profile_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(_I64), _I32]),
     "sa_probe_mfma_bf16": (ctypes.c_int, [_P, _I32, _I32, _P]),
-    "sa_buffer_attend": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P]),
-    "sa_buffer_plan": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+    "sa_buffer_attend": (ctypes.c_int, [_P, _P, _P, _P, _I32, _U32, _P, _P, _P]),
+    "sa_buffer_plan": (ctypes.c_int, [_P, _I32, _U32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                       ctypes.POINTER(_I32)]),
     "sa_batch_attend": (ctypes.c_int, [_I32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                                        ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),

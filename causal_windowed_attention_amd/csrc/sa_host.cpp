@@ -290,19 +290,22 @@ int choose_stream_k(const sa_stream* s, int key_tiles, int q_tiles) {
   return s->schedule_opt == 2 ? kSkGroups : 0;
 }
 
-// Key-row segments of a moving-buffer attend of n chunks: buffer chunk j sees the
-// sink, the newest min(window_valid, W - j) committed window chunks (ring slots of
-// consecutive commits, contiguous modulo R: at most two ranges) and buffer chunks
-// max(0, j - W)..j. Ranges are sorted and adjacent ones merged.
+// Key-row segments of a buffer attend of n chunks. Moving buffer: buffer chunk j sees
+// the sink, the newest min(window_valid, W - j) committed window chunks and buffer
+// chunks max(0, j - W)..j. Steps (SA_BUFFER_STEPS): the committed sink chunks, all
+// window_valid committed window chunks and buffer chunk j alone. The window chunks
+// are ring slots of consecutive commits, contiguous modulo R: at most two ranges.
+// Ranges are sorted and adjacent ones merged.
 struct BufferPlan {
   int32_t n[SA_MAX_BUFFER_CHUNKS];
   int32_t lo[SA_MAX_BUFFER_CHUNKS][SA_MAX_KEY_SEGMENTS], hi[SA_MAX_BUFFER_CHUNKS][SA_MAX_KEY_SEGMENTS];
 };
 
-sa_status plan_buffer(const sa_stream* s, int32_t n_chunks, BufferPlan* bp) {
+sa_status plan_buffer(const sa_stream* s, int32_t n_chunks, uint32_t flags, BufferPlan* bp) {
   const Derived& d = s->d;
-  if (n_chunks < 1 || n_chunks > d.NB) return SA_ERR_INVALID_ARGUMENT;
-  if (s->sink_fill < d.S) return SA_ERR_BAD_STATE;
+  if (n_chunks < 1 || n_chunks > d.NB || (flags & ~SA_BUFFER_STEPS) != 0) return SA_ERR_INVALID_ARGUMENT;
+  const bool steps = (flags & SA_BUFFER_STEPS) != 0;
+  if (!steps && s->sink_fill < d.S) return SA_ERR_BAD_STATE;
   const sa_status st = positions_ok(s, static_cast<int64_t>(s->t_next) + static_cast<int64_t>(n_chunks) * d.F);
   if (st != SA_OK) return st;
   const int64_t C = s->ring_commits;
@@ -310,8 +313,9 @@ sa_status plan_buffer(const sa_stream* s, int32_t n_chunks, BufferPlan* bp) {
   for (int j = 0; j < n_chunks; ++j) {
     int32_t lo[SA_MAX_KEY_SEGMENTS], hi[SA_MAX_KEY_SEGMENTS];   // in slots
     int n = 0;
-    if (d.S > 0) { lo[n] = 0; hi[n] = d.S; ++n; }
-    const int32_t m = std::max(0, std::min(valid, d.W - j));   // committed chunks still in chunk j's window
+    if (s->sink_fill > 0) { lo[n] = 0; hi[n] = s->sink_fill; ++n; }
+    // committed chunks still in chunk j's window
+    const int32_t m = steps ? valid : std::max(0, std::min(valid, d.W - j));
     if (m > 0) {
       const int32_t start = static_cast<int32_t>((C - m) % d.R);
       if (start + m <= d.R) {
@@ -321,7 +325,7 @@ sa_status plan_buffer(const sa_stream* s, int32_t n_chunks, BufferPlan* bp) {
         lo[n] = d.S; hi[n] = d.S + start + m - d.R; ++n;
       }
     }
-    lo[n] = d.buf_slot0 + std::max(0, j - d.W); hi[n] = d.buf_slot0 + j + 1; ++n;
+    lo[n] = d.buf_slot0 + (steps ? j : std::max(0, j - d.W)); hi[n] = d.buf_slot0 + j + 1; ++n;
     for (int a = 1; a < n; ++a)                  // sort by start (n <= 4)
       for (int b = a; b > 0 && lo[b] < lo[b - 1]; --b) {
         std::swap(lo[b], lo[b - 1]);
@@ -761,11 +765,11 @@ sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int
   return SA_OK;
 }
 
-sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, int32_t* n_seg, int32_t* seg_lo,
-                         int32_t* seg_hi) {
+sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, uint32_t flags, int32_t* n_seg,
+                         int32_t* seg_lo, int32_t* seg_hi) {
   if (s == nullptr || n_seg == nullptr || seg_lo == nullptr || seg_hi == nullptr) return SA_ERR_INVALID_ARGUMENT;
   BufferPlan bp;
-  const sa_status st = plan_buffer(s, n_chunks, &bp);
+  const sa_status st = plan_buffer(s, n_chunks, flags, &bp);
   if (st != SA_OK) return st;
   for (int j = 0; j < n_chunks; ++j) {
     n_seg[j] = bp.n[j];
@@ -778,7 +782,7 @@ sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, int32_t* n_seg, i
 }
 
 sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const void* v, int32_t n_chunks,
-                           void* out, float* lse, void* stream) {
+                           uint32_t flags, void* out, float* lse, void* stream) {
   if (s == nullptr) return SA_ERR_INVALID_ARGUMENT;
   const Derived& d = s->d;
   if (!s->planning()) {
@@ -788,7 +792,7 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
       return SA_ERR_INVALID_ARGUMENT;
   }
   BufferPlan bp;
-  sa_status st = plan_buffer(s, n_chunks, &bp);
+  sa_status st = plan_buffer(s, n_chunks, flags, &bp);
   if (st != SA_OK) return st;
   const int bm = d.dtype == SA_BF16 ? sa::kBf16BlockMWide : sa::kF32BlockM;
   const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;

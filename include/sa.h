@@ -219,25 +219,35 @@ sa_status sa_stream_destroy(sa_stream* s);
 sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void* v,
                           void* out, float* lse, void* stream);
 
+/* sa_buffer_attend / sa_buffer_plan flags */
+#define SA_BUFFER_STEPS 1u   /* Stream-Batch over denoising steps (see below)        */
+
 /*
- * Moving-buffer attend (StreamDiT: a buffer of consecutive chunks denoised
- * together, with window attention; the buffer's chunks are the queries of one
- * call). q, k, v: [B, n*Nc, H, D] holding n consecutive chunks that follow the
- * committed stream, 1 <= n <= max_buffer_chunks; out: [B, n*Nc, H, D]; lse:
- * [B, H, n*Nc] float32 or NULL. Buffer chunk j is rotated at positions
- * t_next + j*F.. and attends (full softmax) to exactly what sa_chunk_attend
- * would show it once buffer chunks 0..j-1 had been committed: the sink, the
- * last W chunks of (the committed window, buffer chunks 0..j-1), and itself,
- * i.e. a block-banded chunk mask. The rotated buffer K/V go to the buffer
- * slots; the stream state does not change, except that nothing is staged
- * afterwards (a following sa_kv_append needs explicit k, v). Errors:
- * SA_ERR_INVALID_ARGUMENT for n outside [1, max_buffer_chunks];
- * SA_ERR_BAD_STATE while the sink is not full (earlier buffer chunks would
- * otherwise become sink chunks); SA_ERR_POSITION_RANGE if max_t > 0 and
- * t_next + n*F > max_t. Always runs the ping-pong kernel for bf16.
+ * Several chunks that follow the committed stream as the queries of one call.
+ * q, k, v: [B, n*Nc, H, D] holding n consecutive chunks, 1 <= n <=
+ * max_buffer_chunks; out: [B, n*Nc, H, D]; lse: [B, H, n*Nc] float32 or NULL.
+ * Buffer chunk j is rotated at positions t_next + j*F.. and attends (full
+ * softmax) to:
+ *  flags = 0, moving buffer (StreamDiT: a buffer of consecutive chunks
+ *    denoised together, with window attention): exactly what sa_chunk_attend
+ *    would show it once buffer chunks 0..j-1 had been committed -- the sink,
+ *    the last W chunks of (the committed window, buffer chunks 0..j-1), and
+ *    itself, i.e. a block-banded chunk mask. Needs a full sink
+ *    (SA_ERR_BAD_STATE otherwise: earlier buffer chunks would become sink
+ *    chunks).
+ *  flags = SA_BUFFER_STEPS, Stream-Batch over denoising steps
+ *    (StreamDiffusionV2: chunks in flight at different denoising steps form
+ *    one batch; none is committed yet): what sa_chunk_attend would show now
+ *    (the committed sink chunks and window) plus itself; no buffer chunk sees
+ *    another. Any sink fill.
+ * The rotated buffer K/V go to the buffer slots; the stream state does not
+ * change, except that nothing is staged afterwards (a following sa_kv_append
+ * needs explicit k, v). Errors: SA_ERR_INVALID_ARGUMENT for n outside
+ * [1, max_buffer_chunks] or unknown flags; SA_ERR_POSITION_RANGE if max_t > 0
+ * and t_next + n*F > max_t. Always runs the ping-pong kernel for bf16.
  */
 sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const void* v, int32_t n_chunks,
-                           void* out, float* lse, void* stream);
+                           uint32_t flags, void* out, float* lse, void* stream);
 
 /*
  * Ragged batch (StreamDiffusionV2 Stream-Batch: one launch serving several
@@ -254,15 +264,15 @@ sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* cons
                           const void* const* v, void* const* out, float* const* lse, void* stream);
 
 /*
- * The key segments a sa_buffer_attend of n_chunks would read now (inspection,
+ * The key segments a sa_buffer_attend of n_chunks and flags would read now (inspection,
  * planning handles included): for buffer chunk j, n_seg[j] <= SA_MAX_KEY_SEGMENTS
  * ranges [seg_lo, seg_hi) of physical key rows of one (b, h), at
  * seg_lo[j * SA_MAX_KEY_SEGMENTS + i]. Rows s*Nc.. belong to physical slot s:
  * slots 0..S-1 the sink, S..S+W the window ring, S+W+1+i buffer chunk i.
  * Segments are disjoint, sorted and not adjacent. Same errors as sa_buffer_attend.
  */
-sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, int32_t* n_seg, int32_t* seg_lo,
-                         int32_t* seg_hi);
+sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, uint32_t flags, int32_t* n_seg,
+                         int32_t* seg_lo, int32_t* seg_hi);
 
 /*
  * Commit one chunk: its k, v ([B, Nc, H, D]) are rotated at positions t_next..

@@ -1,8 +1,9 @@
-"""GPU parity of the moving-buffer attend (sa_buffer_attend) against the fp64 oracle.
+"""GPU parity of the buffer attend (sa_buffer_attend) against the fp64 oracle, in both modes.
 
-The oracle's HistoryOracle.buffer_attend is the definition (each buffer chunk sees what an
-attend would show it after the earlier buffer chunks were committed); it is pinned in
-tests/test_oracle_stream.py against explicitly enumerated windows. Streams are driven
+The oracle's HistoryOracle.buffer_attend is the definition (moving buffer: each buffer chunk
+sees what an attend would show it after the earlier buffer chunks were committed; steps: each
+sees the committed context and itself); it is pinned in tests/test_oracle_stream.py against
+explicitly enumerated windows. Streams are driven
 through commits, refreshes and buffers of several sizes, so the key segments cover the
 sink, wrapped and unwrapped ring ranges and buffer ranges whose chunk boundaries cut
 64-key tiles (Nc not a multiple of 64).
@@ -44,11 +45,12 @@ def _check(w, got, want, got_lse, want_lse, what):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("steps", [False, True])
 @pytest.mark.parametrize("case", list(CASES))
-def test_buffer_attend_matches_oracle(case):
+def test_buffer_attend_matches_oracle(case, steps):
     base, kw, nb = CASES[case]
     w = synth.small_variant(synth.WORKLOADS[base], **kw)
-    say("buffer", case, w.dtype, "H", w.heads, "D", w.head_dim, "Nc", w.tokens_per_chunk,
+    say("buffer", case, "steps" if steps else "banded", w.dtype, "H", w.heads, "D", w.head_dim, "Nc", w.tokens_per_chunk,
         "S", w.sink_chunks, "W", w.window_chunks, "NB", nb)
     s = cwa.Stream(config_for(w, max_buffer_chunks=nb))
     hist = HistoryOracle(spec_for(w))
@@ -61,9 +63,9 @@ def test_buffer_attend_matches_oracle(case):
             hist.append(k, v)
             state["c"] += 1
 
-    commit(w.sink_chunks)                        # a buffer attend needs a full sink
-    schedule = [(0, 1), (0, nb), (1, 2), ("refresh", None), (1, nb), (w.window_chunks + 2, nb),
-                (1, max(1, nb - 2)), (2, nb)]
+    # a moving-buffer attend needs a full sink; steps start with nothing committed
+    schedule = [(0 if steps else w.sink_chunks, 1), (0, nb), (1, 2), ("refresh", None), (1, nb),
+                (w.window_chunks + 2, nb), (1, max(1, nb - 2)), (2, nb)]
     for i, (commits, n) in enumerate(schedule):
         if commits == "refresh":
             assert s.rope_refresh(-1, 0) == hist.refresh(None, 0)
@@ -71,8 +73,8 @@ def test_buffer_attend_matches_oracle(case):
         commit(commits)
         q, k, v = _buffer(w, 500 + 10 * i, n)
         lse = torch.empty((w.batch, w.heads, n * w.tokens_per_chunk), dtype=torch.float32, device="cuda")
-        out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
-        want, want_lse = hist.buffer_attend(q, k, v)
+        out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse, steps=steps)
+        want, want_lse = hist.buffer_attend(q, k, v, steps=steps)
         _check(w, out, want, lse, want_lse, f"step {i}: {commits} commits then a buffer of {n}")
         assert s.query()["staged_valid"] == 0
     # an ordinary attend afterwards is unaffected by the buffer slots
@@ -85,7 +87,8 @@ def test_buffer_attend_matches_oracle(case):
 
 
 @pytest.mark.gpu
-def test_buffer_attend_full_size_sampled():
+@pytest.mark.parametrize("steps", [False, True])
+def test_buffer_attend_full_size_sampled(steps):
     """long512p shape (H = 24, Nc = 2048, S = 1, W = 3) with a buffer of 4 chunks: sampled
     rows of two heads against the oracle, after the ring has wrapped."""
     w = synth.WORKLOADS["long512p"]
@@ -98,16 +101,16 @@ def test_buffer_attend_full_size_sampled():
         hist.append(k, v)
     q, k, v = _buffer(w, 700, nb)
     lse = torch.empty((w.batch, w.heads, nb * w.tokens_per_chunk), dtype=torch.float32, device="cuda")
-    out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
+    out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse, steps=steps)
     torch.cuda.synchronize()
     nc = w.tokens_per_chunk
     g = np.random.default_rng(5)
     rows = sorted(set(int(x) for x in g.integers(0, nb * nc, 96)) | {0, nc - 1, nc, nb * nc - 1})
     heads = [0, w.heads - 1]
-    want, want_lse = hist.buffer_attend(q, k, v, rows=rows, heads=heads)
+    want, want_lse = hist.buffer_attend(q, k, v, rows=rows, heads=heads, steps=steps)
     got = host(out)[:, rows][:, :, heads]
     a, r = err(got, want[:, rows][:, :, heads])
     la, _ = err(host(lse)[:, heads][:, :, rows], want_lse[:, heads][:, :, rows])
-    say(f"  long512p buffer of {nb}: sampled max {a:.2e} rel {r:.2e}; lse {la:.2e}")
+    say(f"  long512p {'steps' if steps else 'buffer'} of {nb}: sampled max {a:.2e} rel {r:.2e}; lse {la:.2e}")
     assert a <= BF16_ABS and r <= BF16_REL and la <= BF16_ABS
     s.close()

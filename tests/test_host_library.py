@@ -130,13 +130,13 @@ def test_planning_bookkeeping_matches_oracle(S, W, seed):
     s.close()
 
 
-def _buffer_slots_expected(s, orc, spec, j):
+def _buffer_slots_expected(s, orc, spec, j, steps):
     """Physical slots buffer chunk j must read: the oracle's visible set after committing
-    buffer chunks 0..j-1, mapped to slots (sink slots, window slots by chunk id, buffer slot
-    S + W + 1 + i for buffer chunk i)."""
+    buffer chunks 0..j-1 (moving buffer) or as it stands (steps), mapped to slots (sink
+    slots, window slots by chunk id, buffer slot S + W + 1 + i for buffer chunk i)."""
     tmp = copy.deepcopy(orc)
     z = _dummy(spec)
-    for _ in range(j):
+    for _ in range(0 if steps else j):
         tmp.append(z, z)
     st = s.query()
     by_id = {}
@@ -145,17 +145,18 @@ def _buffer_slots_expected(s, orc, spec, j):
         if info["kind"] == cwa.SA_SLOT_WINDOW:
             by_id[info["chunk_id"]] = slot
     buf0 = spec.sink_chunks + spec.window_chunks + 1
-    want = set()
+    want = {buf0 + j} if steps else set()
     for kind, cid, _ in tmp.visible():
-        if kind == "sink":
+        if kind == "sink" or (steps and kind == "self"):     # steps: self is buffer chunk j
             continue
         want.add(by_id[cid] if cid < orc.n_appends else buf0 + cid - orc.n_appends)
-    return want | set(range(spec.sink_chunks))
+    return want | set(range(orc.sink_fill))
 
 
 @pytest.mark.parametrize("S,W,NB,seed", [(1, 2, 4, 0), (1, 6, 8, 1), (2, 3, 5, 2), (0, 2, 3, 3),
                                          (1, 0, 2, 4), (0, 0, 1, 5), (3, 1, 8, 6)])
-def test_buffer_plan_matches_oracle(S, W, NB, seed):
+@pytest.mark.parametrize("steps", [False, True])
+def test_buffer_plan_matches_oracle(S, W, NB, seed, steps):
     """Bit-exact: the key segments of every buffer chunk cover exactly the slots of the
     chunks the oracle's buffer reading makes visible, as disjoint sorted ranges."""
     cfg = _cfg(sink_chunks=S, window_chunks=W, max_buffer_chunks=NB)
@@ -165,14 +166,15 @@ def test_buffer_plan_matches_oracle(S, W, NB, seed):
     orc = HistoryOracle(spec)
     g = np.random.default_rng(seed)
     z = _dummy(spec)
+    flags = L.SA_BUFFER_STEPS if steps else 0
     for step in range(120):
         n = int(g.integers(1, NB + 1))
-        if orc.sink_fill < S:
+        if orc.sink_fill < S and not steps:
             with pytest.raises(cwa.SaError) as e:
                 s.buffer_plan(n)
             assert e.value.status == L.SA_ERR_BAD_STATE
         else:
-            plan = s.buffer_plan(n)
+            plan = s.buffer_plan(n, steps=steps)
             for j, segs in enumerate(plan):
                 assert 1 <= len(segs) <= L.SA_MAX_KEY_SEGMENTS
                 slots = set()
@@ -181,9 +183,9 @@ def test_buffer_plan_matches_oracle(S, W, NB, seed):
                     if a:
                         assert lo > segs[a - 1][1]               # sorted, disjoint, not adjacent
                     slots |= set(range(lo // nc, hi // nc))
-                assert slots == _buffer_slots_expected(s, orc, spec, j), (step, j, segs)
+                assert slots == _buffer_slots_expected(s, orc, spec, j, steps), (step, j, segs)
             before = s.query()
-            cwa.sa_buffer_attend(s.handle, None, None, None, n, None)
+            cwa.sa_buffer_attend(s.handle, None, None, None, n, None, flags=flags)
             after = s.query()
             assert after["staged_valid"] == 0
             for key in ("t_next", "n_appends", "sink_fill", "ring_commits", "visible_keys"):
@@ -227,9 +229,16 @@ def test_buffer_attend_errors():
                 cwa.sa_buffer_attend(s.handle, None, None, None, n, None)
             assert e.value.status == code
     cwa.sa_kv_append(s.handle, 1, 1)                   # t_next = 4: t = 8 would be needed
-    with pytest.raises(cwa.SaError) as e:
-        cwa.sa_buffer_attend(s.handle, None, None, None, 3, None)
-    assert e.value.status == L.SA_ERR_POSITION_RANGE
+    for flags in (0, L.SA_BUFFER_STEPS):
+        with pytest.raises(cwa.SaError) as e:
+            cwa.sa_buffer_attend(s.handle, None, None, None, 3, None, flags=flags)
+        assert e.value.status == L.SA_ERR_POSITION_RANGE
+    for flags in (2, 0x80000000):                       # unknown flags
+        with pytest.raises(cwa.SaError) as e:
+            cwa.sa_buffer_attend(s.handle, None, None, None, 1, None, flags=flags)
+        assert e.value.status == L.SA_ERR_INVALID_ARGUMENT
+    s = cwa.Stream(_cfg(sink_chunks=2, max_buffer_chunks=2), planning=True)
+    assert s.buffer_plan(2, steps=True) == [[(s.Nc * 5, s.Nc * 6)], [(s.Nc * 6, s.Nc * 7)]]   # nothing committed
 
 
 def test_zero_copy_commit_rules():

@@ -41,6 +41,7 @@ import numpy as np
 
 from .attention import attend
 from .bf16 import round_bf16
+from .fp8 import round_e4m3
 from .rope import rope3d, rope_split, rotate_temporal, token_coords
 
 SHIFT_SINK = 1
@@ -282,13 +283,14 @@ class HistoryOracle(_Common):
 class RingOracle(_Common):
     """Rotated keys in S sink slots + W window slots; refresh re-rotates stored keys.
 
-    storage: None (pure fp64), 'bf16' or 'f32' -- round every stored value (rotated
-    Q, rotated K, V, re-rotated K) the way a device cache of that type holds it.
+    storage: None (pure fp64), 'bf16', 'f32' or 'fp8' -- round every stored value
+    (rotated Q, rotated K, V, re-rotated K) the way a device cache of that type holds
+    it ('fp8': E4M3, saturating).
     """
 
     def __init__(self, spec: StreamSpec, storage: Optional[str] = None):
         super().__init__(spec)
-        if storage not in (None, "bf16", "f32"):
+        if storage not in (None, "bf16", "f32", "fp8"):
             raise ValueError(storage)
         self.storage = storage
         B, H, Nc, D = spec.batch, spec.heads, spec.tokens_per_chunk, spec.head_dim
@@ -306,6 +308,8 @@ class RingOracle(_Common):
             return round_bf16(x)
         if self.storage == "f32":
             return np.asarray(x, dtype=np.float32).astype(np.float64)
+        if self.storage == "fp8":
+            return round_e4m3(x)
         return np.array(x, dtype=np.float64)
 
     def _window_slots(self) -> List[int]:

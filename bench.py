@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "attended query tokens/sec + ms/chunk; % bf16 MFMA peak (1 MI355X)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -200,6 +201,50 @@ def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20, steps_mode=F
             "attention_ms": attn_ms, "rope_apply_ms_per_chunk": rope_ms / max(nr, 1),
             "visible_keys_per_chunk": keys, "flops_per_call": flops, "tflops": tf,
             "frac_of_peak": tf / PEAK_BF16_TFLOPS, "kernel": "chunk_attention_bf16_d128_ppg"}
+
+
+def bench_fp8(torch, cwa, synth, name="wan1.3b", steps=30):
+    """The same steady-state step (attend + commit) on a stream with an fp8 (E4M3) cache:
+    bf16 inputs and outputs, fp8 MFMAs. Step time, the attention kernel's time and its
+    algorithmic FLOP rate against the fp8 peak; the bf16 step is the headline line."""
+    w = synth.WORKLOADS[name]
+    cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
+                          w.sink_chunks, w.window_chunks, dtype="fp8")
+    s = cwa.Stream(cfg, device="cuda")
+    nc = w.tokens_per_chunk
+    pool = [tuple(torch.from_numpy(x).to(torch.bfloat16).cuda() for x in synth.chunk_qkv(w, c)) for c in range(8)]
+    out = torch.empty_like(pool[0][0])
+    for c in range(w.sink_chunks + w.window_chunks + 1):
+        q, k, v = pool[c % 8]
+        s.chunk_attend(q, k, v, out=out)
+        s.kv_append()
+    def step(i):
+        q, k, v = pool[i % 8]
+        s.chunk_attend(q, k, v, out=out)
+        s.kv_append()
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    step_ms = a.elapsed_time(b) / steps
+    s.set_option(cwa.SA_OPT_PROFILE, 1)
+    s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+    for i in range(steps):
+        step(i)
+    attn_ms, na = s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+    keys = s.query()["visible_keys"]
+    s.close()
+    attn_ms /= max(na, 1)
+    flops = 4.0 * w.batch * w.heads * w.head_dim * nc * keys
+    tf = flops / (attn_ms * 1e-3) / 1e12
+    return {"workload": name, "dtype": "fp8 e4m3 cache (bf16 in/out)", "ms_per_step": step_ms,
+            "tokens_per_s": w.batch * nc / (step_ms * 1e-3), "attention_ms": attn_ms, "visible_keys": keys,
+            "tflops": tf, "frac_of_fp8_peak": tf / PEAK_FP8_TFLOPS, "kernel": "chunk_attention_fp8_d128_pp"}
 
 
 def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), steps=20, deadline_ms=1.0,
@@ -374,6 +419,7 @@ def main():
 
     mfma_probe = probe_mfma(torch, cwa)
     buffer_res = bench_buffer(torch, cwa, synth)
+    fp8_res = bench_fp8(torch, cwa, synth)
     steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
     batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
 
@@ -441,6 +487,7 @@ def main():
         "chunk_budget_ms": {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)},
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
+        "fp8_attend": fp8_res,
         "buffer_attend": buffer_res,
         "steps_attend": steps_res,
         "batch_attend": batch_res,

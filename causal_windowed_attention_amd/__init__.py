@@ -16,7 +16,7 @@ import ctypes
 from typing import Optional, Tuple
 
 from . import _lib as L
-from ._lib import (SA_BF16, SA_F32, SA_K_ATTN_COMBINE, SA_K_CHUNK_ATTENTION, SA_K_COUNT,
+from ._lib import (SA_BF16, SA_F32, SA_FP8, SA_K_ATTN_COMBINE, SA_K_CHUNK_ATTENTION, SA_K_COUNT,
                    SA_K_KV_APPEND, SA_K_ROPE_APPLY, SA_K_ROPE_REFRESH, SA_K_SINK_UPDATE,
                    SA_BUFFER_STEPS, SA_OK, SA_OPT_ATTN_VARIANT, SA_OPT_KV_SPLITS, SA_OPT_SCHEDULE, SA_OPT_PROFILE, SA_REFRESH_SHIFT_SINK,
                    SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_STAGING, SA_SLOT_WINDOW, sa_config)
@@ -27,7 +27,7 @@ __all__ = [
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
     "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16",
     "sa_buffer_attend", "sa_buffer_plan", "sa_batch_attend", "Stream",
-    "SA_F32", "SA_BF16", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
+    "SA_F32", "SA_BF16", "SA_FP8", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
     "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
     "SA_K_ROPE_APPLY", "SA_K_CHUNK_ATTENTION", "SA_K_ATTN_COMBINE", "SA_K_KV_APPEND",
     "SA_K_ROPE_REFRESH", "SA_K_SINK_UPDATE", "SA_K_COUNT",
@@ -56,7 +56,7 @@ def make_config(batch, heads, head_dim, frame_h, frame_w, frames_per_chunk, sink
                 window_chunks, rope_dims=(0, 0, 0), max_t=0, rope_theta=0.0, softmax_scale=0.0,
                 dtype=SA_BF16, max_buffer_chunks=0) -> sa_config:
     if isinstance(dtype, str):
-        dtype = {"bf16": SA_BF16, "f32": SA_F32}[dtype]
+        dtype = {"bf16": SA_BF16, "f32": SA_F32, "fp8": SA_FP8}[dtype]
     return sa_config(batch, heads, head_dim, frame_h, frame_w, frames_per_chunk, sink_chunks,
                      window_chunks, rope_dims[0], rope_dims[1], rope_dims[2], max_t,
                      float(rope_theta), float(softmax_scale), dtype, max_buffer_chunks, 0)
@@ -208,7 +208,11 @@ class Stream:
     # -- argument checks (shapes and dtypes; the library checks the rest) --------
     def _torch_dtype(self):
         import torch
-        return torch.bfloat16 if self.cfg.dtype == SA_BF16 else torch.float32
+        return torch.float32 if self.cfg.dtype == SA_F32 else torch.bfloat16
+
+    def _cache_dtype(self):
+        import torch
+        return {SA_F32: torch.float32, SA_BF16: torch.bfloat16, SA_FP8: torch.float8_e4m3fn}[self.cfg.dtype]
 
     def _check_tensor(self, t, n_tokens, name):
         if self.workspace is None and t is None:
@@ -300,7 +304,7 @@ class Stream:
         bh = self.cfg.batch * self.cfg.heads
         n = bh * lay["key_stride"] * self.cfg.head_dim
         raw = self.workspace[lay["k_offset"]:lay["k_offset"] + n * lay["elem_bytes"]]
-        return raw.view(self._torch_dtype()).view(bh, lay["key_stride"], self.cfg.head_dim)
+        return raw.view(self._cache_dtype()).view(bh, lay["key_stride"], self.cfg.head_dim)
 
     def vt_cache_view(self):
         """[B*H, D, key_stride] transposed values."""
@@ -308,7 +312,7 @@ class Stream:
         bh = self.cfg.batch * self.cfg.heads
         n = bh * self.cfg.head_dim * lay["key_stride"]
         raw = self.workspace[lay["vt_offset"]:lay["vt_offset"] + n * lay["elem_bytes"]]
-        return raw.view(self._torch_dtype()).view(bh, self.cfg.head_dim, lay["key_stride"])
+        return raw.view(self._cache_dtype()).view(bh, self.cfg.head_dim, lay["key_stride"])
 
     def q_scratch_view(self):
         """[B*H, Nc, D] rotated queries of the last attend."""
@@ -316,7 +320,7 @@ class Stream:
         bh = self.cfg.batch * self.cfg.heads
         n = bh * self.Nc * self.cfg.head_dim
         raw = self.workspace[lay["q_offset"]:lay["q_offset"] + n * lay["elem_bytes"]]
-        return raw.view(self._torch_dtype()).view(bh, self.Nc, self.cfg.head_dim)
+        return raw.view(self._cache_dtype()).view(bh, self.Nc, self.cfg.head_dim)
 
     def close(self):
         if self.handle is not None:

@@ -19,6 +19,7 @@ SA_ERR_DEVICE = 6
 # sa_dtype
 SA_F32 = 0
 SA_BF16 = 1
+SA_FP8 = 2
 SA_REFRESH_SHIFT_SINK = 1
 SA_MAX_TEMPORAL_PAIRS = 320
 SA_MAX_BUFFER_CHUNKS = 8

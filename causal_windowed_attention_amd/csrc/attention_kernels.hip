@@ -42,6 +42,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kThreads = 256;
@@ -117,6 +119,43 @@ struct Bf16Geom {
 // row is only raised when a tile's maximum exceeds it by more than this, so
 // un-normalised weights stay below 2^8 and the O rescale runs rarely.
 constexpr float kRescaleThreshold = 8.0f;
+
+// fp8 tile geometry: as Bf16Geom with one byte per element. A stage holds a K
+// tile (64 keys x D bytes) and a V^T tile (D x 64 bytes); 128-byte K rows use
+// the two-rows-per-bank-window swizzle, 64-byte V^T rows c ^ ((r >> 2) & 3).
+template <int D, int BN_ = kBf16BlockN>
+struct Fp8Geom {
+  static constexpr int BN = BN_;
+  static constexpr int KROW = D;              // bytes per K row
+  static constexpr int VROW = BN;             // bytes per V^T row
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int KC = D / 16;
+  static constexpr int VC = BN / 16;
+};
+
+// The fp8 PV product takes, per lane, 32 P bytes as its B operand: byte 16 a + j
+// of lane half g is element j of score accumulator a. With the K tile's rows in
+// natural order that element belongs to key 32 a + 8 (j / 4) + 4 g + j % 4; the
+// V^T operand bytes of lane half g are keys 32 g .. 32 g + 31 in order. Storing
+// key k(t) in LDS row t, with k = 32 g + 16 a + j for t = 32 a + 8 (j / 4) + 4 g
+// + j % 4 (a permutation of the six index bits), makes the two orders agree, so
+// V^T tiles are copied unpermuted.
+__device__ __forceinline__ int fp8_key_of_row(int t) {
+  return (t & 3) | (((t >> 3) & 3) << 2) | (((t >> 5) & 1) << 4) | (((t >> 2) & 1) << 5);
+}
+
+// fp8 softmax weights are formed as 2^(s - m) with m the running maximum minus
+// this shift, so the largest weight of a row sits at 2^4 .. 2^8 (E4M3 holds up
+// to 448) and weights down to 2^-10 of it stay in E4M3's normal range.
+constexpr float kP8Shift = 4.0f;
+
+// v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 (format 0) and unit block
+// scales (E8M0 127 = 2^0).
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 
 #ifndef PP_READ_AHEAD
 #define PP_READ_AHEAD 2
@@ -380,9 +419,12 @@ __device__ __forceinline__ float xor32(float x) {
 enum PpOut { kPpFinal = 0, kPpSplit = 1, kPpStreamK = 2 };
 constexpr int kPpStages = 4;
 
-template <int D>
+template <int D, bool F8>
+using PpGeom = std::conditional_t<F8, Fp8Geom<D>, Bf16Geom<D>>;
+
+template <int D, bool F8>
 struct PpSmem {
-  static constexpr int BYTES = kPpStages * Bf16Geom<D>::BUF;
+  static constexpr int BYTES = kPpStages * PpGeom<D, F8>::BUF;
 };
 
 // The key tiles one work item visits: up to kMaxSegs key-row ranges [lo, hi),
@@ -480,16 +522,20 @@ __device__ __forceinline__ int key_tile(const KeyList& kl, int i, int& lo, int& 
 // valid below q_end, against key tiles [t_begin, t_end) of the range [0, n_keys)
 // or, with GROUPS (a moving-buffer attend), against the key tiles of kl. The
 // single-range form is a separate instantiation so the chunk attend's kernel
-// carries none of the range bookkeeping.
-template <int D, bool GROUPS>
+// carries none of the range bookkeeping. F8: E4M3 Q, K, V^T and P with the
+// 32x32x64 fp8 MFMA (fp32 accumulation) instead of bf16 with 32x32x16.
+template <int D, bool GROUPS, bool F8>
 __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs, char* smem, int bh, int q_base,
                                            int q_end, int t_begin, int t_end, const KeyList& kl, int mode,
                                            int slot) {
-  using G = Bf16Geom<D>;
+  using G = PpGeom<D, F8>;
+  using Op = std::conditional_t<F8, i32x8, bf16x8>;   // one MFMA operand per lane
+  constexpr int ES = F8 ? 1 : 2;                 // bytes per cached element
+  constexpr int KK = F8 ? 64 : 16;               // MFMA reduction depth
   constexpr int NW = 8, STAGES = kPpStages;
   constexpr int BN = G::BN;
   constexpr int BM = NW * 32;
-  constexpr int KSTEPS = D / 16, MT = BN / 32, DT = D / 32, PSTEPS = BN / 16;
+  constexpr int KSTEPS = D / KK, MT = BN / 32, DT = D / 32, PSTEPS = BN / KK;
   constexpr int KCOPIES = G::KBYTES / 1024 / NW;
   constexpr int VCOPIES = G::VBYTES / 1024 / NW;
   constexpr int PER_TILE = KCOPIES + VCOPIES;
@@ -513,16 +559,16 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     }
   };
 
-  const char* kbase = static_cast<const char*>(bs.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
-  const char* vbase = static_cast<const char*>(bs.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
+  const char* kbase = static_cast<const char*>(bs.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * ES;
+  const char* vbase = static_cast<const char*>(bs.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * ES;
 
   const int q = q_base + wave * 32 + l32;
-  bf16x8 bq[KSTEPS];
+  Op bq[KSTEPS];                                 // Q^T operand: lane l holds query l % 32
   {
     const int qrow = min(q, q_end - 1);
-    const __bf16* qsrc = static_cast<const __bf16*>(bs.q) + (static_cast<size_t>(bh) * bs.rows + qrow) * D;
+    const char* qsrc = static_cast<const char*>(bs.q) + (static_cast<size_t>(bh) * bs.rows + qrow) * D * ES;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s + 8 * g);
+    for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const Op*>(qsrc + (KK * s + (KK / 2) * g) * ES);
   }
 
   // Copy sources (byte offsets) of copy c of this wave; K rows of every (b, h)
@@ -531,15 +577,15 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
   auto k_src = [&](int c) {
     const int P = (c * NW + wave) * 64 + lane;
     const int r = P / G::KC;
-    return swap_bits23(r) * G::KROW + swz(P % G::KC, r, G::KC) * 16;
+    return (F8 ? fp8_key_of_row(r) : swap_bits23(r)) * G::KROW + swz(P % G::KC, r, G::KC) * 16;
   };
   auto v_src = [&](int c) {
     const int P = (c * NW + wave) * 64 + lane;
     const int d = P / G::VC;
-    return d * p.key_stride * 2 + swz(P % G::VC, d, G::VC) * 16;
+    return d * p.key_stride * ES + swz(P % G::VC, d, G::VC) * 16;
   };
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, p.k_bh_stride * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, p.vt_bh_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, p.k_bh_stride * ES);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, p.vt_bh_stride * ES);
   auto issue_tile = [&](int i) {                 // visit i into stage i % STAGES
     int lo_unused, hi_unused;
     const int key0 = visit(i, lo_unused, hi_unused) * BN;
@@ -547,20 +593,46 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
 #pragma unroll
     for (int c = 0; c < KCOPIES; ++c) lds_copy16(krs, key0 * G::KROW + k_src(c), dst + (c * NW + wave) * 1024);
 #pragma unroll
-    for (int c = 0; c < VCOPIES; ++c) lds_copy16(vrs, key0 * 2 + v_src(c), dst + G::KBYTES + (c * NW + wave) * 1024);
+    for (int c = 0; c < VCOPIES; ++c) lds_copy16(vrs, key0 * ES + v_src(c), dst + G::KBYTES + (c * NW + wave) * 1024);
   };
 
   // K operand address of k-step s: row l32, swizzled chunk of logical chunk 2s + g,
   // recomputed per read (two VALU ops) rather than held in 8 registers
+  // Operand reads. bf16: 16 bytes per lane, logical chunk 2 s + g of row l32.
+  // fp8: 32 bytes per lane, logical chunks 4 s + 2 g and 4 s + 2 g + 1 (two reads).
   const int ka_row = l32 * G::KROW;
   auto ka = [&](int s) { return ka_row + swz(2 * s + g, l32, G::KC) * 16; };
   auto va = [&](int s) { return G::KBYTES + l32 * G::VROW + swz(2 * s + g, l32, G::VC) * 16; };
+  auto k_op = [&](const char* stage, int s, int mt) -> Op {
+    if constexpr (F8) {
+      const char* row = stage + ka_row + mt * 32 * G::KROW;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(row + swz(4 * s + 2 * g, l32, G::KC) * 16);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(row + swz(4 * s + 2 * g + 1, l32, G::KC) * 16);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(stage + ka(s) + mt * 32 * G::KROW);
+    }
+  };
+  auto v_op = [&](const char* stage, int s, int dt) -> Op {
+    if constexpr (F8) {                          // PSTEPS = 1: the whole 64-byte row pair
+      const char* row = stage + G::KBYTES + (dt * 32 + l32) * G::VROW;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(row + swz(2 * g, l32, G::VC) * 16);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(row + swz(2 * g + 1, l32, G::VC) * 16);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(stage + va(s) + dt * 32 * G::VROW);
+    }
+  };
+  auto mma = [](const Op& a, const Op& b, const f32x16& c) -> f32x16 {
+    if constexpr (F8) return mfma_fp8(a, b, c);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  };
 
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x16{};
   f32x16 sacc[MT];
-  bf16x8 pb[PSTEPS];
+  Op pb[PSTEPS];
   float m = -__builtin_inff(), l = 0.f;
 
   auto qk = [&](int i) {
@@ -570,20 +642,14 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + ka(s) + mt * 32 * G::KROW);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
-      }
+      for (int mt = 0; mt < MT; ++mt) sacc[mt] = mma(k_op(stage, s, mt), bq[s], sacc[mt]);
   };
   auto pv = [&](int i) {
     const char* stage = smem + (i % STAGES) * G::BUF;
 #pragma unroll
     for (int s = 0; s < PSTEPS; ++s)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + va(s) + dt * 32 * G::VROW);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mma(v_op(stage, s, dt), pb[s], o[dt]);
   };
   auto softmax = [&](int i) {
     int lo, hi;
@@ -593,7 +659,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7);
+          const int key = F8 ? key0 + 32 * g + 16 * mt + j : key0 + 32 * mt + 16 * (j >> 3) + 8 * g + (j & 7);
           if (key < lo || key >= hi) sacc[mt][j] = -__builtin_inff();
         }
     }
@@ -604,7 +670,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mt][j]);
     mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
     if (__any(mx > m + kRescaleThreshold)) {
-      const float m_new = fmaxf(m, mx);
+      const float m_new = fmaxf(m, F8 ? mx - kP8Shift : mx);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
       l *= alpha;
@@ -612,14 +678,28 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
       for (int d = 0; d < DT; ++d) o[d] *= alpha;
     }
     float rs = 0.f;
+    if constexpr (F8) {                          // byte 16 a + j <- element j of accumulator a
 #pragma unroll
-    for (int s = 0; s < PSTEPS; ++s)
+      for (int w = 0; w < 8; ++w) {
+        float e4[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pvl = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m));
-        rs += pvl;
-        pb[s][e] = static_cast<__bf16>(pvl);
+        for (int k = 0; k < 4; ++k) {
+          e4[k] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + k], p.scale_log2, -m));
+          rs += e4[k];
+        }
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4[0], e4[1], 0, false);
+        pb[0][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e4[2], e4[3], lo, true);
       }
+    } else {
+#pragma unroll
+      for (int s = 0; s < PSTEPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pvl = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m));
+          rs += pvl;
+          pb[s][e] = static_cast<__bf16>(pvl);
+        }
+    }
     l += rs;
   };
 
@@ -637,16 +717,17 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     for (int k = 0; k < KSTEPS * MT; ++k) {
       const int s = k / MT, mt = k % MT;
       const int sv = k / DT, dt = k % DT;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ka(s) + mt * 32 * G::KROW);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(vs + va(sv) + dt * 32 * G::VROW);
-      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[mt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pb[sv], o[dt], 0, 0, 0);
+      const Op a = k_op(ks, s, mt);
+      const Op v = v_op(vs, sv, dt);
+      sacc[mt] = mma(a, bq[s], sacc[mt]);
+      o[dt] = mma(v, pb[sv], o[dt]);
     }
     constexpr int AHEAD = PP_READ_AHEAD;                   // steps of operand reads in flight
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);   // operands of steps 0 .. AHEAD-1
+    constexpr int RD = F8 ? 4 : 2;                         // LDS reads per step
+    __builtin_amdgcn_sched_group_barrier(0x100, RD * AHEAD, 0);  // operands of steps 0 .. AHEAD-1
 #pragma unroll
     for (int k = 0; k < KSTEPS * MT; ++k) {
-      if (k + AHEAD < KSTEPS * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // step k+AHEAD reads
+      if (k + AHEAD < KSTEPS * MT) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);  // step k+AHEAD reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // step k MFMAs
     }
   };
@@ -740,17 +821,17 @@ __device__ __forceinline__ int64_t sk_start(int w, int64_t L, int G) { return (s
 // its range as segments; a segment that covers a whole q-tile writes the final
 // rows, a partial one writes slot 2w (the range's first segment) or 2w + 1 (its
 // last), merged afterwards by attn_sk_combine.
-template <int D, bool GROUPS>
-__device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p) {
-  __shared__ __attribute__((aligned(1024))) char smem[PpSmem<D>::BYTES];
+template <int D, bool GROUPS, bool F8>
+__device__ __forceinline__ void chunk_attention_pp_body(const AttnParams& p) {
+  __shared__ __attribute__((aligned(1024))) char smem[PpSmem<D, F8>::BYTES];
   if constexpr (GROUPS) {                        // moving buffer: the q-tile's chunk picks the keys
     const int w = xcd_remap(blockIdx.x, p.B * p.H * p.q_tiles);
     const int qt = uniform(w % p.q_tiles), bh = uniform(w / p.q_tiles);
     const int grp = uniform(qt / p.group_qtiles);
     const int qtg = qt - grp * p.group_qtiles;
     const int row0 = p.ragged ? 0 : grp * p.group_rows;   // a ragged group has rows of its own
-    pp_segment<D, true>(p, bases_group(p, grp), smem, bh, row0 + qtg * (8 * 32), row0 + p.group_rows, 0, 0,
-                        keys_group(p, grp, Bf16Geom<D>::BN), kPpFinal, 0);
+    pp_segment<D, true, F8>(p, bases_group(p, grp), smem, bh, row0 + qtg * (8 * 32), row0 + p.group_rows, 0, 0,
+                            keys_group(p, grp, Bf16Geom<D>::BN), kPpFinal, 0);
     return;
   }
   const bool sk = p.sk_groups > 0;
@@ -783,7 +864,7 @@ __device__ __forceinline__ void chunk_attention_bf16_pp_body(const AttnParams& p
       slot = split;
       it = r1;
     }
-    pp_segment<D, false>(p, bases_shared(p), smem, bh, qt * (8 * 32), p.Nc, t0, t1, none, mode, slot);
+    pp_segment<D, false, F8>(p, bases_shared(p), smem, bh, qt * (8 * 32), p.Nc, t0, t1, none, mode, slot);
     if (it < r1) __syncthreads();                // the next segment reuses every LDS stage
   }
 }
@@ -805,20 +886,29 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attention_bf16_d64_q64(Attn
 }
 
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_pp(AttnParams p) {
-  chunk_attention_bf16_pp_body<128, false>(p);
+  chunk_attention_pp_body<128, false, false>(p);
 }
 
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d64_pp(AttnParams p) {
-  chunk_attention_bf16_pp_body<64, false>(p);
+  chunk_attention_pp_body<64, false, false>(p);
 }
 
 // moving-buffer attend: query groups with their own key ranges
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_ppg(AttnParams p) {
-  chunk_attention_bf16_pp_body<128, true>(p);
+  chunk_attention_pp_body<128, true, false>(p);
 }
 
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d64_ppg(AttnParams p) {
-  chunk_attention_bf16_pp_body<64, true>(p);
+  chunk_attention_pp_body<64, true, false>(p);
+}
+
+// fp8 cache (E4M3 Q, K, V^T; P rounded to E4M3): the same schedule on the fp8 MFMA
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_fp8_d128_pp(AttnParams p) {
+  chunk_attention_pp_body<128, false, true>(p);
+}
+
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_fp8_d128_ppg(AttnParams p) {
+  chunk_attention_pp_body<128, true, true>(p);
 }
 
 // fp32: one query row per lane, 64 rows per block, 32-key tiles through LDS.
@@ -1027,7 +1117,10 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
   const int64_t n_work =
       p.sk_groups > 0 ? p.sk_groups : static_cast<int64_t>(p.B) * p.H * p.q_tiles * p.kv_splits;
   if (n_work <= 0) return hipSuccess;
-  if (dtype == 1) {
+  if (dtype == 2) {                              // fp8 cache: head_dim 128 only (checked by the host)
+    hipLaunchKernelGGL(p.n_groups > 0 ? chunk_attention_fp8_d128_ppg : chunk_attention_fp8_d128_pp, dim3(n_work),
+                       dim3(2 * kThreads), 0, st, p);
+  } else if (dtype == 1) {
     if (p.n_groups > 0) {
       hipLaunchKernelGGL(p.D == 128 ? chunk_attention_bf16_d128_ppg : chunk_attention_bf16_d64_ppg, dim3(n_work),
                          dim3(2 * kThreads), 0, st, p);
@@ -1062,7 +1155,7 @@ hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st
   const int64_t total = static_cast<int64_t>(p.B) * p.H * p.Nc * (p.D / 4);
   if (total <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((total + kThreads - 1) / kThreads));
-  if (dtype == 1) hipLaunchKernelGGL(attn_combine<__bf16>, grid, dim3(kThreads), 0, st, p);
+  if (dtype == 1 || dtype == 2) hipLaunchKernelGGL(attn_combine<__bf16>, grid, dim3(kThreads), 0, st, p);
   else hipLaunchKernelGGL(attn_combine<float>, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }

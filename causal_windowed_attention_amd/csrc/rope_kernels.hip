@@ -10,7 +10,10 @@
 // "Sommario tecnico" 2.A.2). cos/sin come from host fp64 tables rounded to
 // fp32 (spatial tables in the workspace, the chunk's temporal table by value),
 // so no device trigonometry runs. Arithmetic is fp32; stores round to the cache
-// type (bf16: round to nearest even).
+// type (bf16: round to nearest even; fp8: E4M3 of the OCP 8-bit float format,
+// clamped to +-448 and rounded to nearest even by v_cvt_pk_fp8_f32, whose
+// unclamped result above 464 would be NaN). Inputs are fp32 for an fp32 cache
+// and bf16 for a bf16 or fp8 cache.
 //
 // All four are HBM-bound streaming kernels: every input element is read once
 // and every output element written once, with 16-byte vector accesses. V is
@@ -26,12 +29,23 @@ constexpr int kTileTokens = 64;
 constexpr int kThreads = 256;
 
 template <typename T> struct alignas(16) Vec16 { T e[16 / sizeof(T)]; };
+// N elements of a storage type, stored as one vector
+template <typename T, int N> struct alignas(N * sizeof(T)) VecN { T e[N]; };
+
+// One E4M3 value (OCP 8-bit float: bias 7, 3 mantissa bits, largest finite 448).
+struct fp8e4m3 { uint8_t bits; };
+constexpr float kE4M3Max = 448.f;
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f(fp8e4m3 x) { return __builtin_amdgcn_cvt_f32_fp8(x.bits, 0); }
 template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return static_cast<__bf16>(x); }
+template <> __device__ __forceinline__ fp8e4m3 from_f<fp8e4m3>(float x) {
+  const float c = fminf(fmaxf(x, -kE4M3Max), kE4M3Max);
+  return fp8e4m3{static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xff)};
+}
 
 // (cos, sin) of the pair starting at even channel ch of a token at (frame, y, x).
 __device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const RopeWriteParams& p, int ch,
@@ -43,16 +57,29 @@ __device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const RopeWritePa
   return p.w_cs[x * (p.dw >> 1) + (ch >> 1)];
 }
 
-template <typename T>
-__device__ __forceinline__ Vec16<T> rotate(const Vec16<T>& in, const float2 (&cs)[16 / sizeof(T) / 2]) {
-  constexpr int NP = 16 / sizeof(T) / 2;
-  Vec16<T> out;
+// Rotated pairs of one 16-byte input vector, rounded to the storage type TS.
+template <typename TI, typename TS>
+__device__ __forceinline__ VecN<TS, 16 / sizeof(TI)> rotate(const Vec16<TI>& in,
+                                                           const float2 (&cs)[16 / sizeof(TI) / 2]) {
+  constexpr int NP = 16 / sizeof(TI) / 2;
+  VecN<TS, 2 * NP> out;
 #pragma unroll
   for (int e = 0; e < NP; ++e) {
     const float u0 = to_f(in.e[2 * e]), u1 = to_f(in.e[2 * e + 1]);
-    out.e[2 * e] = from_f<T>(u0 * cs[e].x - u1 * cs[e].y);
-    out.e[2 * e + 1] = from_f<T>(u0 * cs[e].y + u1 * cs[e].x);
+    out.e[2 * e] = from_f<TS>(u0 * cs[e].x - u1 * cs[e].y);
+    out.e[2 * e + 1] = from_f<TS>(u0 * cs[e].y + u1 * cs[e].x);
   }
+  return out;
+}
+
+// A 16-byte vector of input elements rounded to the storage type.
+template <typename TI, typename TS>
+__device__ __forceinline__ VecN<TS, 16 / sizeof(TI)> convert(const uint4& in) {
+  constexpr int N = 16 / sizeof(TI);
+  const TI* e = reinterpret_cast<const TI*>(&in);
+  VecN<TS, N> out;
+#pragma unroll
+  for (int i = 0; i < N; ++i) out.e[i] = from_f<TS>(to_f(e[i]));
   return out;
 }
 
@@ -87,9 +114,12 @@ __device__ __forceinline__ void transpose_block(const uint4 (&in)[16 / sizeof(T)
 //  * V: thread owns a VN x VN (tokens x channels) block, transposes it in
 //    registers and stores VN 16-byte rows of V^T; lanes with consecutive token
 //    groups of one channel group write 128 contiguous bytes per channel row.
-template <typename T, bool HAS_Q>
+// TI: input element type; TS: cache (storage) element type.
+template <typename TI, typename TS, bool HAS_Q>
 __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
-  constexpr int VN = 16 / sizeof(T);             // elements per 16-byte vector
+  using T = TI;
+  using VecS = VecN<TS, 16 / sizeof(TI)>;
+  constexpr int VN = 16 / sizeof(T);             // elements per 16-byte input vector
   constexpr int MAXJ = 32 / VN;                  // K/Q vectors per thread (D <= 128)
   __shared__ float2 s_tcs[kMaxTemporalPairs];
   __shared__ int s_fyx[kTileTokens][3];          // (frame, y, x) of the tile's tokens
@@ -113,9 +143,9 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
   const T* __restrict__ kin = static_cast<const T*>(p.k);
   const T* __restrict__ qin = static_cast<const T*>(p.q);
   const T* __restrict__ vin = static_cast<const T*>(p.v);
-  T* __restrict__ kc = static_cast<T*>(p.kcache) + bh * p.k_bh_stride;
-  T* __restrict__ qo = static_cast<T*>(p.qrot) + (bh * p.q_rows + p.q_row0) * p.D;
-  T* __restrict__ vt = static_cast<T*>(p.vtcache) + bh * p.vt_bh_stride + p.row0 + n0;
+  TS* __restrict__ kc = static_cast<TS*>(p.kcache) + bh * p.k_bh_stride;
+  TS* __restrict__ qo = static_cast<TS*>(p.qrot) + (bh * p.q_rows + p.q_row0) * p.D;
+  TS* __restrict__ vt = static_cast<TS*>(p.vtcache) + bh * p.vt_bh_stride + p.row0 + n0;
   auto in_off = [&](int n, int c) {
     return ((static_cast<size_t>(b) * p.in_tokens + p.in_tok0 + n) * p.H + h) * p.D + c;
   };
@@ -158,13 +188,14 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
       float2 cs[VN / 2];
 #pragma unroll
       for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, p, c0 + 2 * e, s_fyx[tl][0], s_fyx[tl][1], s_fyx[tl][2]);
-      *reinterpret_cast<Vec16<T>*>(kc + static_cast<size_t>(p.row0 + n) * p.D + c0) = rotate<T>(kv[j], cs);
-      if constexpr (HAS_Q) *reinterpret_cast<Vec16<T>*>(qo + static_cast<size_t>(n) * p.D + c0) = rotate<T>(qv[j], cs);
+      *reinterpret_cast<VecS*>(kc + static_cast<size_t>(p.row0 + n) * p.D + c0) = rotate<TI, TS>(kv[j], cs);
+      if constexpr (HAS_Q)
+        *reinterpret_cast<VecS*>(qo + static_cast<size_t>(n) * p.D + c0) = rotate<TI, TS>(qv[j], cs);
     }
   }
 
   // ---- V: VN x VN register transposes straight into V^T ---------------------
-  const bool vec_ok = (p.row0 % VN) == 0;        // 16-byte aligned V^T rows
+  const bool vec_ok = (p.row0 % VN) == 0;        // vector-aligned V^T rows
 #pragma unroll
   for (int r = 0; r < MAXB; ++r) {
     const int blk = tid + r * kThreads;
@@ -175,30 +206,30 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
     if (vec_ok && t0 + VN <= ntok) {
 #pragma unroll
       for (int c = 0; c < VN; ++c)
-        *reinterpret_cast<uint4*>(vt + static_cast<size_t>(cb + c) * p.key_stride + t0) = out[c];
+        *reinterpret_cast<VecS*>(vt + static_cast<size_t>(cb + c) * p.key_stride + t0) = convert<TI, TS>(out[c]);
     } else {
 #pragma unroll
       for (int c = 0; c < VN; ++c) {
-        const T* e = reinterpret_cast<const T*>(&out[c]);
-        for (int t = 0; t < VN && t0 + t < ntok; ++t) vt[static_cast<size_t>(cb + c) * p.key_stride + t0 + t] = e[t];
+        const VecS e = convert<TI, TS>(out[c]);
+        for (int t = 0; t < VN && t0 + t < ntok; ++t) vt[static_cast<size_t>(cb + c) * p.key_stride + t0 + t] = e.e[t];
       }
     }
   }
 }
 
-template <typename T>
+template <typename TI, typename TS>
 __global__ __launch_bounds__(kThreads) void rope_apply(RopeWriteParams p) {
-  rope_write_body<T, true>(p);
+  rope_write_body<TI, TS, true>(p);
 }
 
-template <typename T>
+template <typename TI, typename TS>
 __global__ __launch_bounds__(kThreads) void kv_ring_append(RopeWriteParams p) {
-  rope_write_body<T, false>(p);
+  rope_write_body<TI, TS, false>(p);
 }
 
-template <typename T>
+template <typename TI, typename TS>
 __global__ __launch_bounds__(kThreads) void sink_update(RopeWriteParams p) {
-  rope_write_body<T, false>(p);
+  rope_write_body<TI, TS, false>(p);
 }
 
 // One thread per (row, temporal pair) of one slot of one (b, h).
@@ -225,35 +256,28 @@ __global__ __launch_bounds__(kThreads) void rope_refresh(RefreshParams p) {
 
 }  // namespace
 
-hipError_t launch_rope_apply(const RopeWriteParams& p, int dtype, hipStream_t st) {
-  if (p.n_tokens <= 0) return hipSuccess;
-  const dim3 grid((p.n_tokens + kTileTokens - 1) / kTileTokens, p.H, p.B);
-  if (dtype == 1) hipLaunchKernelGGL(rope_apply<__bf16>, grid, dim3(kThreads), 0, st, p);
-  else hipLaunchKernelGGL(rope_apply<float>, grid, dim3(kThreads), 0, st, p);
-  return hipGetLastError();
-}
+// dtype: 0 = fp32 in, fp32 cache; 1 = bf16 in, bf16 cache; 2 = bf16 in, fp8 cache
+#define SA_WRITE_LAUNCHER(NAME, KERNEL)                                                             \
+  hipError_t NAME(const RopeWriteParams& p, int dtype, hipStream_t st) {                            \
+    if (p.n_tokens <= 0) return hipSuccess;                                                         \
+    const dim3 grid((p.n_tokens + kTileTokens - 1) / kTileTokens, p.H, p.B);                        \
+    if (dtype == 2) hipLaunchKernelGGL((KERNEL<__bf16, fp8e4m3>), grid, dim3(kThreads), 0, st, p);  \
+    else if (dtype == 1) hipLaunchKernelGGL((KERNEL<__bf16, __bf16>), grid, dim3(kThreads), 0, st, p); \
+    else hipLaunchKernelGGL((KERNEL<float, float>), grid, dim3(kThreads), 0, st, p);                \
+    return hipGetLastError();                                                                       \
+  }
 
-hipError_t launch_kv_append(const RopeWriteParams& p, int dtype, hipStream_t st) {
-  if (p.n_tokens <= 0) return hipSuccess;
-  const dim3 grid((p.n_tokens + kTileTokens - 1) / kTileTokens, p.H, p.B);
-  if (dtype == 1) hipLaunchKernelGGL(kv_ring_append<__bf16>, grid, dim3(kThreads), 0, st, p);
-  else hipLaunchKernelGGL(kv_ring_append<float>, grid, dim3(kThreads), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_sink_update(const RopeWriteParams& p, int dtype, hipStream_t st) {
-  if (p.n_tokens <= 0) return hipSuccess;
-  const dim3 grid((p.n_tokens + kTileTokens - 1) / kTileTokens, p.H, p.B);
-  if (dtype == 1) hipLaunchKernelGGL(sink_update<__bf16>, grid, dim3(kThreads), 0, st, p);
-  else hipLaunchKernelGGL(sink_update<float>, grid, dim3(kThreads), 0, st, p);
-  return hipGetLastError();
-}
+SA_WRITE_LAUNCHER(launch_rope_apply, rope_apply)
+SA_WRITE_LAUNCHER(launch_kv_append, kv_ring_append)
+SA_WRITE_LAUNCHER(launch_sink_update, sink_update)
+#undef SA_WRITE_LAUNCHER
 
 hipError_t launch_rope_refresh(const RefreshParams& p, int dtype, hipStream_t st) {
   const int64_t items = static_cast<int64_t>(p.Nc) * (p.dt >> 1);
   if (items <= 0 || p.n_slot <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((items + kThreads - 1) / kThreads), p.n_slot, p.BH);
-  if (dtype == 1) hipLaunchKernelGGL(rope_refresh<__bf16>, grid, dim3(kThreads), 0, st, p);
+  if (dtype == 2) hipLaunchKernelGGL(rope_refresh<fp8e4m3>, grid, dim3(kThreads), 0, st, p);
+  else if (dtype == 1) hipLaunchKernelGGL(rope_refresh<__bf16>, grid, dim3(kThreads), 0, st, p);
   else hipLaunchKernelGGL(rope_refresh<float>, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }

@@ -55,7 +55,7 @@ sa_status derive(const sa_config* c, Derived* d) {
       c->sink_chunks < 0 || c->window_chunks < 0 || c->max_t < 0 || c->head_dim < 2 ||
       c->head_dim % 2 != 0)
     return SA_ERR_INVALID_ARGUMENT;
-  if (c->dtype != SA_F32 && c->dtype != SA_BF16) return SA_ERR_INVALID_ARGUMENT;
+  if (c->dtype != SA_F32 && c->dtype != SA_BF16 && c->dtype != SA_FP8) return SA_ERR_INVALID_ARGUMENT;
   if (c->max_buffer_chunks < 0 || c->max_buffer_chunks > SA_MAX_BUFFER_CHUNKS || c->reserved != 0)
     return SA_ERR_INVALID_ARGUMENT;
   if (!(c->rope_theta >= 0.0) || !(c->softmax_scale >= 0.f) || !std::isfinite(c->rope_theta) ||
@@ -65,7 +65,7 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->B = c->batch; d->H = c->heads; d->D = c->head_dim; d->Hf = c->frame_h; d->Wf = c->frame_w;
   d->F = c->frames_per_chunk; d->S = c->sink_chunks; d->W = c->window_chunks; d->max_t = c->max_t;
   d->dtype = c->dtype;
-  d->elem = c->dtype == SA_BF16 ? 2 : 4;
+  d->elem = c->dtype == SA_BF16 ? 2 : c->dtype == SA_FP8 ? 1 : 4;   // cache and Q scratch element
   if (c->rope_dim_t == 0 && c->rope_dim_h == 0 && c->rope_dim_w == 0) {
     d->dh = d->dw = 2 * (d->D / 6);
     d->dt = d->D - 2 * d->dh;
@@ -86,6 +86,7 @@ sa_status derive(const sa_config* c, Derived* d) {
   const int64_t keys = static_cast<int64_t>(d->n_slots + d->NB) * d->Nc;
   if (keys > (1 << 24)) return SA_ERR_UNSUPPORTED;
   if (d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
+  if (d->dtype == SA_FP8 && d->D != 128) return SA_ERR_UNSUPPORTED;   // one fp8 kernel: D = 128
   if (static_cast<int64_t>(d->F) * (d->dt / 2) > sa::kMaxTemporalPairs) return SA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d->B) * d->H > 65535) return SA_ERR_UNSUPPORTED;
   if (d->max_t > 0 && static_cast<int64_t>(d->S) * d->F > d->max_t) return SA_ERR_POSITION_RANGE;
@@ -95,7 +96,7 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->key_stride = static_cast<int32_t>(align_up(static_cast<size_t>(keys), 64));
   // bf16 tile copies address one (b, h) region through a buffer resource (32-bit offsets)
   if (static_cast<int64_t>(d->key_stride) * d->D * d->elem >= (int64_t{1} << 31)) return SA_ERR_UNSUPPORTED;
-  const int bm = d->dtype == SA_BF16 ? sa::kBf16BlockM : sa::kF32BlockM;
+  const int bm = d->dtype != SA_F32 ? sa::kBf16BlockM : sa::kF32BlockM;
   d->q_tiles = (d->Nc + bm - 1) / bm;
   // partial buffers only where splitting can help filling the chip
   const int64_t blocks = static_cast<int64_t>(d->B) * d->H * d->q_tiles;
@@ -111,7 +112,7 @@ sa_status derive(const sa_config* c, Derived* d) {
                       ? static_cast<size_t>(d->max_splits) * bh * d->Nc * (static_cast<size_t>(d->D) + 1) * 4
                       : 0;
   // stream-K partials: 2 slots per persistent workgroup, BlockM rows of D + 1 floats
-  d->sk_bytes = d->dtype == SA_BF16
+  d->sk_bytes = d->dtype != SA_F32
                     ? static_cast<size_t>(2 * kSkGroups) * sa::kBf16BlockMWide * (static_cast<size_t>(d->D) + 1) * 4
                     : 0;
   d->tab_bytes = (static_cast<size_t>(d->Hf) * (d->dh / 2) + static_cast<size_t>(d->Wf) * (d->dw / 2)) * 8;
@@ -241,16 +242,17 @@ sa_status timed(sa_stream* s, int kid, hipStream_t st, F&& launch) {
   return SA_OK;
 }
 
-// bf16 attention kernel variant used for this stream (automatic: the
-// ping-pong kernel, variant 3).
+// MFMA attention kernel variant used for this stream (automatic: the ping-pong
+// kernel, variant 3; an fp8 cache has no other); 0 for the fp32 kernel.
 int attn_variant(const sa_stream* s) {
-  if (s->d.dtype != SA_BF16) return 0;
+  if (s->d.dtype == SA_F32) return 0;
+  if (s->d.dtype == SA_FP8) return 3;
   return s->variant_opt == 0 ? 3 : s->variant_opt;
 }
 
 // Query rows per workgroup of the attention kernel used for this stream.
 int attn_block_m(const sa_stream* s) {
-  if (s->d.dtype != SA_BF16) return sa::kF32BlockM;
+  if (s->d.dtype == SA_F32) return sa::kF32BlockM;
   return attn_variant(s) == 1 ? sa::kBf16BlockM : sa::kBf16BlockMWide;
 }
 
@@ -480,7 +482,7 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
 
   const int32_t slot = s->staging_slot();
   const int32_t n_keys = s->visible_chunks() * d.Nc;
-  const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
+  const int bn = d.dtype != SA_F32 ? sa::kBf16BlockN : sa::kF32BlockN;
   const int key_tiles = (n_keys + bn - 1) / bn;
   const int bm = attn_block_m(s);
   const int q_tiles = (d.Nc + bm - 1) / bm;
@@ -727,7 +729,8 @@ sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value) {
       s->kv_splits_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_ATTN_VARIANT:
-      if (value < 0 || value > 3) return SA_ERR_INVALID_ARGUMENT;
+      if (value < 0 || value > 3 || (s->d.dtype == SA_FP8 && value != 0 && value != 3))
+        return SA_ERR_INVALID_ARGUMENT;
       s->variant_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_SCHEDULE:
@@ -794,8 +797,8 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
   BufferPlan bp;
   sa_status st = plan_buffer(s, n_chunks, flags, &bp);
   if (st != SA_OK) return st;
-  const int bm = d.dtype == SA_BF16 ? sa::kBf16BlockMWide : sa::kF32BlockM;
-  const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
+  const int bm = d.dtype != SA_F32 ? sa::kBf16BlockMWide : sa::kF32BlockM;
+  const int bn = d.dtype != SA_F32 ? sa::kBf16BlockN : sa::kF32BlockN;
   const int group_qtiles = (d.Nc + bm - 1) / bm;
   int max_tiles = 0;
   for (int j = 0; j < n_chunks; ++j) {
@@ -833,7 +836,7 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
     ap.n_keys = (d.buf_slot0 + d.NB) * d.Nc;
     ap.Nc = n_chunks * d.Nc;                     // query rows per (b, h)
     ap.B = d.B; ap.H = d.H; ap.D = d.D;
-    ap.variant = d.dtype == SA_BF16 ? 3 : 0;
+    ap.variant = d.dtype != SA_F32 ? 3 : 0;
     ap.q_rows_per_block = bm;
     ap.q_tiles = n_chunks * group_qtiles;
     ap.kv_splits = 1;
@@ -887,8 +890,8 @@ sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* cons
     const sa_status st = positions_ok(si, static_cast<int64_t>(si->t_next) + e.F);
     if (st != SA_OK) return st;
   }
-  const int bm = d.dtype == SA_BF16 ? sa::kBf16BlockMWide : sa::kF32BlockM;
-  const int bn = d.dtype == SA_BF16 ? sa::kBf16BlockN : sa::kF32BlockN;
+  const int bm = d.dtype != SA_F32 ? sa::kBf16BlockMWide : sa::kF32BlockM;
+  const int bn = d.dtype != SA_F32 ? sa::kBf16BlockN : sa::kF32BlockN;
   const int group_qtiles = (d.Nc + bm - 1) / bm;
   if (!planning) {
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -919,7 +922,7 @@ sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* cons
     ap.n_keys = (d.buf_slot0 + d.NB) * d.Nc;
     ap.Nc = d.Nc;
     ap.B = d.B; ap.H = d.H; ap.D = d.D;
-    ap.variant = d.dtype == SA_BF16 ? 3 : 0;
+    ap.variant = d.dtype != SA_F32 ? 3 : 0;
     ap.q_rows_per_block = bm;
     ap.q_tiles = n * group_qtiles;
     ap.kv_splits = 1;

@@ -25,7 +25,8 @@
  *  - Softmax scale defaults to 1/sqrt(D).
  *
  * Layouts. q, k, v and out are [B, Nc, H, D] contiguous (token-major, what a
- * fused QKV projection writes), Nc = F*Hf*Wf, element type = config dtype.
+ * fused QKV projection writes), Nc = F*Hf*Wf, element type = config dtype
+ * (bf16 for SA_FP8).
  * lse is [B, H, Nc] float32 (natural log). The workspace is opaque device
  * memory sized by sa_workspace_bytes(); sa_stream_layout() describes it for
  * inspection.
@@ -71,7 +72,18 @@ typedef enum sa_status {
   SA_ERR_DEVICE = 6              /* a HIP call failed                                */
 } sa_status;
 
-typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+/*
+ * SA_FP8: q, k, v and out are bf16; the rotated Q scratch, the K cache and the
+ * V^T cache hold E4M3 values (OCP 8-bit float: 3 mantissa bits, largest finite
+ * 448), each rounded to nearest even after clamping to +-448; the attention
+ * products run on the fp8 MFMA with fp32 accumulation, and the softmax weights
+ * are rounded to E4M3 before the PV product (weights of a row are formed
+ * relative to its running maximum minus 4 in log2 units, so they stay below
+ * 2^8). A lower-precision variant of the same method (SANA-Streaming's
+ * mixed-precision policy quantises attention query/key projections); its
+ * error bound is derived from the E4M3 rounding of the weights.
+ */
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_FP8 = 2 } sa_dtype;
 
 /* sa_rope_refresh flags */
 #define SA_REFRESH_SHIFT_SINK 1u
@@ -80,7 +92,7 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  * Stream configuration (72 bytes, no padding holes).
  *  batch            B >= 1 streams advancing in lockstep (same positions, own caches)
  *  heads            H >= 1
- *  head_dim         D: 64 or 128 (both dtypes)
+ *  head_dim         D: 64 or 128 (SA_F32, SA_BF16); 128 (SA_FP8)
  *  frame_h, frame_w latent grid of one frame, >= 1
  *  frames_per_chunk F >= 1 (one temporal RoPE unit per latent frame)
  *  sink_chunks      S >= 0 persistent sink chunks
@@ -89,7 +101,8 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *  max_t            0: unbounded; else every position used must be < max_t
  *  rope_theta       RoPE base, 0 selects 10000
  *  softmax_scale    0 selects 1/sqrt(D)
- *  dtype            SA_F32 or SA_BF16 (element type of q, k, v, out and the cache)
+ *  dtype            SA_F32, SA_BF16 (element type of q, k, v, out and the cache)
+ *                   or SA_FP8 (bf16 q, k, v, out; E4M3 cache)
  *  max_buffer_chunks NB in 0..SA_MAX_BUFFER_CHUNKS: chunks one sa_buffer_attend
  *                   may hold (NB extra cache slots per (b, h), NB*Nc Q scratch rows)
  *  reserved         must be 0
@@ -173,7 +186,7 @@ typedef enum sa_option {
   SA_OPT_PROFILE = 1,       /* 1: record HIP events around every launch (sa_profile_read)    */
   SA_OPT_ATTN_VARIANT = 2,  /* bf16 attention kernel: 0 automatic (3), 1 = 4 waves x 32
                                query rows, 2 = 4 waves x 64 rows, 3 = 8 waves x 32 rows with
-                               a ping-pong MFMA/softmax schedule                             */
+                               a ping-pong MFMA/softmax schedule (SA_FP8: 0 or 3 only)       */
   SA_OPT_SCHEDULE = 3       /* variant 3 work distribution: 0 automatic (1), 1 = one workgroup per
                                (b, h, q-tile, split), 2 = stream-K (persistent workgroups
                                sharing the q-tile x key-tile iterations evenly, partial tiles

@@ -356,10 +356,9 @@ class RingOracle(_Common):
                 self._store(_rotate_chunk(s, k, self.t_next)),
                 self._store(_heads_major(v)))
 
-    def attend(self, q, k, v, rows=None, heads=None):
-        self._check_chunk(q, k, v)
-        self._check_positions()
-        s = self.spec
+    def operands(self, q, k, v):
+        """(Qrot, keys, vals) of the attend call: the stored rotated queries [B,H,Nc,D] and
+        the stored visible keys and values, lists of [B,H,Nc,D] in sink, window, self order."""
         qrot, kself, vself = self.staged(q, k, v)
         keys = [self.sink_k[j] for j, m in enumerate(self.sink_meta) if m[0]]
         vals = [self.sink_v[j] for j, m in enumerate(self.sink_meta) if m[0]]
@@ -368,7 +367,13 @@ class RingOracle(_Common):
             vals.append(self.ring_v[j])
         keys.append(kself)
         vals.append(vself)
-        return _attend_all(s, qrot, keys, vals, rows=rows, heads=heads)
+        return qrot, keys, vals
+
+    def attend(self, q, k, v, rows=None, heads=None):
+        self._check_chunk(q, k, v)
+        self._check_positions()
+        qrot, keys, vals = self.operands(q, k, v)
+        return _attend_all(self.spec, qrot, keys, vals, rows=rows, heads=heads)
 
     def append(self, k, v):
         self._check_chunk(k, v)

@@ -52,7 +52,7 @@ class Workload:
     n_chunks: int
     refresh_every: int = 0          # 0: never; else refresh before chunk c when c % refresh_every == 0
     refresh_base: int = -1          # -1: default base (sink_chunks * frames_per_chunk)
-    dtype: str = "bf16"             # "bf16" or "f32"
+    dtype: str = "bf16"             # "bf16", "f32" or "fp8" (bf16 inputs, E4M3 cache)
     outlier_channels: int = 0
     outlier_scale: float = 1.0
 
@@ -166,7 +166,7 @@ def source_id(c: int, distinct: Optional[frozenset]) -> int:
 
 
 def draw(w: Workload, src_chunk: int, tensor_id: int, n_tokens: Optional[int] = None) -> np.ndarray:
-    """One seeded tensor [B, n_tokens, H, D] in float32 (bf16-exact for bf16 workloads).
+    """One seeded tensor [B, n_tokens, H, D] in float32 (bf16-exact for bf16 and fp8 workloads).
 
     Token blocks of TOKEN_BLOCK tokens of each stream b have their own generator
     keyed by (20261203, config id, b, chunk, tensor id, block), so the result
@@ -184,7 +184,7 @@ def draw(w: Workload, src_chunk: int, tensor_id: int, n_tokens: Optional[int] = 
         if scale_outliers:
             for h in range(w.heads):
                 x[:, h, outl[h]] *= np.float32(w.outlier_scale)
-        if w.dtype == "bf16":
+        if w.dtype in ("bf16", "fp8"):            # bf16 activations (fp8 caches take bf16 inputs)
             x = to_bf16_exact(x)
         out[b, t0:t1] = x
 

@@ -35,7 +35,7 @@ def spec_for(w: synth.Workload, heads=None) -> StreamSpec:
 
 def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp8"):
         t = t.to(torch.bfloat16)            # exact: the inputs are bf16-representable
     return t.cuda()
 

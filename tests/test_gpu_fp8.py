@@ -1,0 +1,182 @@
+"""GPU parity of the fp8 cache variant (SA_FP8) against the fp64 oracle.
+
+What the device stores is checked code by code: V is a plain bf16 -> E4M3 rounding and
+must match the oracle's E4M3 rounding exactly; rotated K and Q come from an fp32
+rotation on the device and an fp64 one in the oracle, so an element may take the other
+neighbour only where the fp32 rotation error can reach an E4M3 rounding boundary.
+
+Attention is compared with the storage-emulating oracle (RingOracle, storage 'fp8':
+exact softmax over the E4M3-rounded Q, K and V the device holds). The device also
+rounds the softmax weights to E4M3 before the PV product, which the oracle does not;
+the tolerance is derived from that rounding. Weight j of row i, in units of the
+normalised weights P_ij, is rounded with an error of at most h_ij = max(2^-4 P_ij,
+2^-10 max_j P_ij / 2^4): a relative half-step of 2^-4 in E4M3's normal range, or half
+the subnormal step 2^-9 at the kernel's weight scale (the largest weight of a row is at
+least 2^4 there). The errors are independent and unbiased (round to nearest even), so
+output element (i, d) deviates with a standard deviation of at most
+sigma_id = sqrt(sum_j h_ij^2 v_jd^2 / 3). The test allows 6 sigma, plus 2^-8 |O| for
+the bf16 output rounding and 2e-3 for the fp32 / fp8-MFMA accumulation. The error
+against the pure fp64 oracle (dominated by the E4M3 rounding of Q and K) is printed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_windowed_attention_amd as cwa
+import synth
+from gpu_util import config_for, dev, host, say, spec_for
+from oracle import HistoryOracle, RingOracle, attention_probs, round_e4m3
+
+pytestmark = pytest.mark.gpu
+
+LSE_ABS = 5e-3
+
+CASES = {
+    # Nc = 180 and 70: key tiles straddle chunk boundaries, the last query tile is ragged
+    "d128_s1w3": dict(heads=2, frame_h=6, frame_w=10, frames_per_chunk=3, window_chunks=3),
+    "d128_s2w2": dict(heads=1, frame_h=5, frame_w=7, frames_per_chunk=2, sink_chunks=2, window_chunks=2),
+}
+
+
+def _workload(**kw):
+    return synth.small_variant(synth.WORKLOADS["wan1.3b"], dtype="fp8", **kw)
+
+
+def fp8_tolerance(qrot, keys, vals, scale, rows=None):
+    """Per-element tolerance [B, Nq, H, D] and the emulated output, from the stored
+    operands of one attend (see the module docstring)."""
+    B, H, Nc, D = qrot.shape
+    r = np.arange(Nc) if rows is None else np.asarray(rows)
+    tol = np.zeros((B, len(r), H, D))
+    out = np.zeros((B, len(r), H, D))
+    for b in range(B):
+        for h in range(H):
+            K = np.concatenate([k[b, h] for k in keys], axis=0)
+            V = np.concatenate([v[b, h] for v in vals], axis=0)
+            P = attention_probs(qrot[b, h, r], K, scale)
+            hmax = np.maximum(2.0 ** -4 * P, 2.0 ** -10 * P.max(axis=1, keepdims=True) / 16.0)
+            sigma = np.sqrt((hmax ** 2) @ (V ** 2) / 3.0)
+            o = P @ V
+            out[b, :, h] = o
+            tol[b, :, h] = 6.0 * sigma + 2.0 ** -8 * np.abs(o) + 2e-3
+    return tol, out
+
+
+def _check_attend(what, got, got_lse, emu_out, emu_lse, tol, pure_out=None, rows=None, heads=None):
+    g = host(got)
+    gl = host(got_lse)
+    if rows is not None:
+        g = g[:, rows][:, :, heads]
+        gl = gl[:, heads][:, :, rows]
+    d = np.abs(g - emu_out)
+    ratio = float((d / tol).max())
+    la = float(np.abs(gl - emu_lse).max())
+    msg = f"  {what}: max err {d.max():.2e}, max err/tol {ratio:.3f}, lse {la:.2e}"
+    if pure_out is not None:
+        msg += f"; vs pure fp64 max {np.abs(g - pure_out).max():.2e}"
+    say(msg)
+    assert ratio <= 1.0 and la <= LSE_ABS, (what, ratio, la)
+
+
+def _check_codes(what, got, want_fp64, delta):
+    """got: E4M3 values from the device; want_fp64: the exact (unrounded) values; delta:
+    bound on the device's fp32 error of each element (0 where its value is exact)."""
+    lo, hi = round_e4m3(want_fp64 - delta), round_e4m3(want_fp64 + delta)
+    ok = (got == lo) | (got == hi)
+    exact = (delta == 0)
+    say(f"  {what}: {int((~ok).sum())} codes outside the rounding interval of {ok.size}; "
+        f"{int((lo != hi).sum())} elements near a boundary")
+    assert ok.all(), what
+    assert np.array_equal(got[exact], round_e4m3(want_fp64[exact])), what
+
+
+def _pair_delta(x):
+    """fp32 error bound of a rotated pair element: 2^-21 (|u0| + |u1|) of its input pair."""
+    a = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])
+    return np.repeat(a, 2, axis=-1) * 2.0 ** -21
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_fp8_stream_matches_oracle(case):
+    w = _workload(**CASES[case])
+    nc = w.tokens_per_chunk
+    say(f"fp8 {case}: H {w.heads} D {w.head_dim} Nc {nc} S {w.sink_chunks} W {w.window_chunks}")
+    s = cwa.Stream(config_for(w))
+    spec = spec_for(w)
+    emu, pure_ring, hist = RingOracle(spec, storage="fp8"), RingOracle(spec), HistoryOracle(spec)
+    n_chunks = w.sink_chunks + w.window_chunks + 4
+    for c in range(n_chunks):
+        if c == w.sink_chunks + w.window_chunks + 1:
+            d = s.rope_refresh(-1, 0)
+            assert d == emu.refresh(None, 0) == pure_ring.refresh(None, 0) == hist.refresh(None, 0)
+        if c == n_chunks - 2:
+            ks, vs = synth.sink_kv(w, 0)
+            s.sink_update(dev(ks, w.dtype), dev(vs, w.dtype))
+            for o in (emu, pure_ring, hist):
+                o.sink_update(ks, vs)
+        q, k, v = synth.chunk_qkv(w, c)
+        lse = torch.empty((w.batch, w.heads, nc), dtype=torch.float32, device="cuda")
+        out = s.chunk_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
+        torch.cuda.synchronize()
+        qrot, keys, vals = emu.operands(q, k, v)
+        tol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale)
+        _, emu_lse = emu.attend(q, k, v)
+        pure_out, _ = hist.attend(q, k, v)
+        _check_attend(f"chunk {c}", out, lse, emu_out, emu_lse, tol, pure_out)
+        if c == 1:                               # the Q scratch of this attend, before any refresh
+            qs = s.q_scratch_view().cpu().float().numpy().astype(np.float64).reshape(w.batch, w.heads, nc, -1)
+            qpure = pure_ring.staged(q, k, v)[0]
+            qin = np.transpose(q, (0, 2, 1, 3)).astype(np.float64)
+            _check_codes("Q scratch", qs, qpure, _pair_delta(qin))
+        s.kv_append()                            # commit the staged chunk
+        for o in (emu, pure_ring, hist):
+            o.append(k, v)
+        if c == w.sink_chunks + 1:               # cache codes of every committed chunk so far
+            kc = s.k_cache_view().cpu().float().numpy().astype(np.float64)
+            vt = s.vt_cache_view().cpu().float().numpy().astype(np.float64)
+            for slot in range(s.query()["n_slots"]):
+                info = s.slot(slot)
+                if info["kind"] not in (cwa.SA_SLOT_SINK, cwa.SA_SLOT_WINDOW):
+                    continue
+                cid = info["chunk_id"]
+                _, kraw, vraw = synth.chunk_qkv(w, cid)
+                rows = slice(slot * nc, (slot + 1) * nc)
+                kdev = kc[:, rows].reshape(w.batch, w.heads, nc, -1)
+                kin = np.transpose(kraw, (0, 2, 1, 3)).astype(np.float64)
+                _check_codes(f"K slot {slot} (chunk {cid})", kdev, pure_ring.stored_k(cid), _pair_delta(kin))
+                vdev = np.transpose(vt[:, :, rows], (0, 2, 1)).reshape(w.batch, w.heads, nc, -1)
+                vwant = pure_ring.stored_v(cid)
+                _check_codes(f"V slot {slot} (chunk {cid})", vdev, vwant, np.zeros_like(vwant))
+    s.close()
+
+
+def test_fp8_full_size_sampled():
+    """wan1.3b shape (H = 12, Nc = 4680, S = 1, W = 6) with an fp8 cache, after the ring
+    has wrapped: sampled rows of two heads against the storage-emulating oracle."""
+    w = synth.small_variant(synth.WORKLOADS["wan1.3b"], dtype="fp8")
+    nc = w.tokens_per_chunk
+    heads = [0, w.heads - 1]
+    say(f"fp8 wan1.3b full size: H {w.heads} Nc {nc}; heads {heads}")
+    s = cwa.Stream(config_for(w))
+    spec = spec_for(w, heads)
+    emu, hist = RingOracle(spec, storage="fp8"), HistoryOracle(spec)
+    n = w.sink_chunks + w.window_chunks + 2
+    for c in range(n):
+        q, k, v = synth.chunk_qkv(w, c)
+        if c < n - 1:
+            s.kv_append(dev(k, w.dtype), dev(v, w.dtype))
+            emu.append(k[:, :, heads], v[:, :, heads])
+            hist.append(k[:, :, heads], v[:, :, heads])
+    lse = torch.empty((w.batch, w.heads, nc), dtype=torch.float32, device="cuda")
+    out = s.chunk_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(nc - 8, nc), g.choice(nc, 40, replace=False)]))
+    qh, kh, vh = q[:, :, heads], k[:, :, heads], v[:, :, heads]
+    qrot, keys, vals = emu.operands(qh, kh, vh)
+    tol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale, rows=rows)
+    _, emu_lse = emu.attend(qh, kh, vh, rows=list(rows))
+    pure_out, _ = hist.attend(qh, kh, vh, rows=list(rows))
+    _check_attend("wan1.3b fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, pure_out[:, rows],
+                  rows=rows, heads=heads)
+    s.close()

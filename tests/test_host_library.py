@@ -407,3 +407,30 @@ def test_batch_attend_planning_semantics_and_errors():
     assert e.value.status == L.SA_ERR_POSITION_RANGE
     assert [s.query()["staged_valid"] for s in hs] == staged      # nothing changed
     assert [s.query()["t_next"] for s in hs[:3]] == t_before[:3]
+
+
+def test_fp8_config_and_planning():
+    """SA_FP8: head_dim 128 only; the cache and Q scratch take one byte per element; the
+    attention kernel is always the ping-pong one; planning matches the bf16 tiling."""
+    assert cwa.sa_config_check(_cfg(dtype="fp8", head_dim=64)) == L.SA_ERR_UNSUPPORTED
+    c8, c16 = _cfg(dtype="fp8", head_dim=128), _cfg(dtype="bf16", head_dim=128)
+    assert cwa.sa_config_check(c8) == 0
+    assert cwa.sa_workspace_bytes(c8) < cwa.sa_workspace_bytes(c16)
+    s8, s16 = cwa.Stream(c8, planning=True), cwa.Stream(c16, planning=True)
+    l8, l16 = s8.layout(), s16.layout()
+    assert l8["elem_bytes"] == 1 and l16["elem_bytes"] == 2
+    assert l8["k_bh_stride"] * 2 == l16["k_bh_stride"] and l8["vt_bh_stride"] * 2 == l16["vt_bh_stride"]
+    for v in (1, 2):
+        with pytest.raises(cwa.SaError) as e:
+            s8.set_option(cwa.SA_OPT_ATTN_VARIANT, v)
+        assert e.value.status == L.SA_ERR_INVALID_ARGUMENT
+    s8.set_option(cwa.SA_OPT_ATTN_VARIANT, 3)
+    for _ in range(5):
+        for s in (s8, s16):
+            s.chunk_attend(None, None, None)
+            s.kv_append()
+    a, b = s8.query(), s16.query()
+    for key in ("last_q_tiles", "last_key_tiles", "last_kv_splits", "visible_keys", "t_next"):
+        assert a[key] == b[key], key
+    s8.close()
+    s16.close()

@@ -634,6 +634,13 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
   f32x16 sacc[MT];
   Op pb[PSTEPS];
   float m = -__builtin_inff(), l = 0.f;
+  // fp8: the row sums of the rounded weights come from one more MFMA per tile (the
+  // MFMA unit has room, the VALU does not): its A operand is a constant matrix whose
+  // row 0 is all E4M3 ones (0x38), so row 0 of the product accumulates
+  // sum_k P[k][query]; it lands in element 0 of lanes 0-31 (query l % 32).
+  [[maybe_unused]] f32x16 osum = f32x16{};
+  [[maybe_unused]] const int ones4 = l32 == 0 ? 0x38383838 : 0;
+  [[maybe_unused]] const i32x8 ones_row = {ones4, ones4, ones4, ones4, ones4, ones4, ones4, ones4};
 
   auto qk = [&](int i) {
     const char* stage = smem + (i % STAGES) * G::BUF;
@@ -650,6 +657,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     for (int s = 0; s < PSTEPS; ++s)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] = mma(v_op(stage, s, dt), pb[s], o[dt]);
+    if constexpr (F8) osum = mfma_fp8(ones_row, pb[0], osum);
   };
   auto softmax = [&](int i) {
     int lo, hi;
@@ -674,23 +682,21 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
       l *= alpha;
+      if constexpr (F8) osum[0] *= alpha;        // the other elements hold zeros
 #pragma unroll
       for (int d = 0; d < DT; ++d) o[d] *= alpha;
     }
-    float rs = 0.f;
     if constexpr (F8) {                          // byte 16 a + j <- element j of accumulator a
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         float e4[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          e4[k] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + k], p.scale_log2, -m));
-          rs += e4[k];
-        }
+        for (int k = 0; k < 4; ++k) e4[k] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + k], p.scale_log2, -m));
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4[0], e4[1], 0, false);
         pb[0][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e4[2], e4[3], lo, true);
       }
     } else {
+      float rs = 0.f;
 #pragma unroll
       for (int s = 0; s < PSTEPS; ++s)
 #pragma unroll
@@ -699,8 +705,8 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
           rs += pvl;
           pb[s][e] = static_cast<__bf16>(pvl);
         }
+      l += rs;
     }
-    l += rs;
   };
 
   // QK(i) and PV(i-1) interleaved: step k issues the K operand read and the QK
@@ -722,6 +728,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
       sacc[mt] = mma(a, bq[s], sacc[mt]);
       o[dt] = mma(v, pb[sv], o[dt]);
     }
+    if constexpr (F8) osum = mfma_fp8(ones_row, pb[0], osum);
     constexpr int AHEAD = PP_READ_AHEAD;                   // steps of operand reads in flight
     constexpr int RD = F8 ? 4 : 2;                         // LDS reads per step
     __builtin_amdgcn_sched_group_barrier(0x100, RD * AHEAD, 0);  // operands of steps 0 .. AHEAD-1
@@ -730,6 +737,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
       if (k + AHEAD < KSTEPS * MT) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);  // step k+AHEAD reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // step k MFMAs
     }
+    if constexpr (F8) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the row-sum MFMA
   };
   // Both groups run the same block sequence; waves 4-7 pass one extra barrier
   // first (and waves 0-3 one at the end), which offsets them by one block.
@@ -739,6 +747,19 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
   auto wait_tile = [&](int i) {                  // tile i complete; tile i + 1 may be in flight
     if (i + 1 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_TILE));
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  // MFMAs touch no memory, so the compiler may sink them past the lagging group's wait
+  // branch and below the barrier that ends their block, which puts both groups' MFMAs
+  // into one phase; for the fp8 blocks it does. An empty asm that takes every
+  // accumulator as an operand makes the block's MFMAs issue before that branch.
+  auto block_end = [&] {
+    if constexpr (F8) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(sacc[mt]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(o[dt]));
+      asm volatile("" : "+v"(osum));
+    }
   };
   issue_tile(0);
   if (n > 1) issue_tile(1);
@@ -750,6 +771,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
   __syncthreads();
   if (n > 2) issue_tile(2);
   qk(0);                                         // M(0)
+  block_end();
   if (lag && n > 1) wait_tile(1);
   __syncthreads();
   softmax(0);                                    // V(0)
@@ -758,6 +780,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     __syncthreads();
     if (i + 2 < n) issue_tile(i + 2);
     qk_pv(i);                                    // M(i)
+    block_end();
     if (lag && i + 1 < n) wait_tile(i + 1);
     __syncthreads();
     softmax(i);                                  // V(i)
@@ -767,7 +790,13 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
   if (!lag) __syncthreads();
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l_tot = l + xor32(l);
+  float l_tot;
+  if constexpr (F8) {
+    const float t = xor32(osum[0]);
+    l_tot = g ? t : osum[0];
+  } else {
+    l_tot = l + xor32(l);
+  }
   const float inv = 1.f / l_tot;
   const float lse2 = m + __log2f(l_tot);
   if (mode == kPpStreamK) {                      // partial rows of this q-tile, all BM of them

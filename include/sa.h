@@ -79,9 +79,11 @@ typedef enum sa_status {
  * products run on the fp8 MFMA with fp32 accumulation, and the softmax weights
  * are rounded to E4M3 before the PV product (weights of a row are formed
  * relative to its running maximum minus 4 in log2 units, so they stay below
- * 2^8). A lower-precision variant of the same method (SANA-Streaming's
- * mixed-precision policy quantises attention query/key projections); its
- * error bound is derived from the E4M3 rounding of the weights.
+ * 2^8). Outputs are normalised by the sum of the rounded weights, and lse is
+ * the log of that sum (off the exact one by the weights' rounding: about
+ * 1e-3 for broad attention). A lower-precision variant of the same method
+ * (SANA-Streaming's mixed-precision policy quantises attention query/key
+ * projections); its error bound is derived from the E4M3 rounding.
  */
 typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_FP8 = 2 } sa_dtype;
 

@@ -7,16 +7,24 @@ neighbour only where the fp32 rotation error can reach an E4M3 rounding boundary
 
 Attention is compared with the storage-emulating oracle (RingOracle, storage 'fp8':
 exact softmax over the E4M3-rounded Q, K and V the device holds). The device also
-rounds the softmax weights to E4M3 before the PV product, which the oracle does not;
+rounds the softmax weights to E4M3 and normalises by the sum of the rounded weights
+(O_i = sum_j p~_ij v_j / sum_j p~_ij, LSE from the same sum), which the oracle does not;
 the tolerance is derived from that rounding. Weight j of row i, in units of the
-normalised weights P_ij, is rounded with an error of at most h_ij = max(2^-4 P_ij,
-2^-10 max_j P_ij / 2^4): a relative half-step of 2^-4 in E4M3's normal range, or half
-the subnormal step 2^-9 at the kernel's weight scale (the largest weight of a row is at
-least 2^4 there). The errors are independent and unbiased (round to nearest even), so
-output element (i, d) deviates with a standard deviation of at most
-sigma_id = sqrt(sum_j h_ij^2 v_jd^2 / 3). The test allows 6 sigma, plus 2^-8 |O| for
-the bf16 output rounding and 2e-3 for the fp32 / fp8-MFMA accumulation. The error
-against the pure fp64 oracle (dominated by the E4M3 rounding of Q and K) is printed.
+normalised weights P_ij, is rounded with an error e_ij of at most h_ij =
+max(2^-4 P_ij, 2^-10 max_j P_ij / 2^4): a relative half-step of 2^-4 in E4M3's normal
+range, or half the subnormal step 2^-9 at the kernel's weight scale (the largest weight
+of a row is at least 2^4 there). To first order O_i moves by sum_j e_ij (v_j - O_i) and
+LSE_i by sum_j e_ij. The errors are independent; with a uniform-error variance bound
+h^2 / 3 their standard deviations are at most sigma_id = sqrt(sum_j h_ij^2 (v_jd -
+O_id)^2 / 3) and sqrt(sum_j h_ij^2 / 3). Round to nearest even is unbiased only for a
+flat density across a rounding step; exponentials of smooth scores are denser at the
+low end of a step, which biases each normal-range weight low by about (step / value)^2
+/ 24 <= 2^-6 / 24 of itself: at most beta = 2^-6 / 24 on the LSE and beta sum_j P_ij
+|v_j - O_i| <= beta (P|V| + |O|) on an output. The test allows 6 sigma plus that bias,
+plus 2^-8 |O| for the bf16 output rounding and 2e-3 (outputs) or 1e-4 (LSE) for fp32
+accumulation and the fp8 MFMA's own (measured on N(0,1)-like E4M3 data: at most 5e-5
+of sum |products|, unbiased). The error against the pure fp64 oracle (dominated by the
+E4M3 rounding of Q and K) is printed.
 """
 import numpy as np
 import pytest
@@ -28,8 +36,6 @@ from gpu_util import config_for, dev, host, say, spec_for
 from oracle import HistoryOracle, RingOracle, attention_probs, round_e4m3
 
 pytestmark = pytest.mark.gpu
-
-LSE_ABS = 5e-3
 
 CASES = {
     # Nc = 180 and 70: key tiles straddle chunk boundaries, the last query tile is ragged
@@ -43,26 +49,31 @@ def _workload(**kw):
 
 
 def fp8_tolerance(qrot, keys, vals, scale, rows=None):
-    """Per-element tolerance [B, Nq, H, D] and the emulated output, from the stored
-    operands of one attend (see the module docstring)."""
+    """Per-element output tolerance [B, Nq, H, D], LSE tolerance [B, H, Nq] and the
+    emulated output, from the stored operands of one attend (see the module docstring)."""
     B, H, Nc, D = qrot.shape
     r = np.arange(Nc) if rows is None else np.asarray(rows)
     tol = np.zeros((B, len(r), H, D))
+    ltol = np.zeros((B, H, len(r)))
     out = np.zeros((B, len(r), H, D))
     for b in range(B):
         for h in range(H):
             K = np.concatenate([k[b, h] for k in keys], axis=0)
             V = np.concatenate([v[b, h] for v in vals], axis=0)
             P = attention_probs(qrot[b, h, r], K, scale)
-            hmax = np.maximum(2.0 ** -4 * P, 2.0 ** -10 * P.max(axis=1, keepdims=True) / 16.0)
-            sigma = np.sqrt((hmax ** 2) @ (V ** 2) / 3.0)
+            h2 = np.maximum(2.0 ** -4 * P, 2.0 ** -10 * P.max(axis=1, keepdims=True) / 16.0) ** 2
             o = P @ V
+            # sum_j h_ij^2 (v_jd - o_id)^2 expanded so no [Nq, Nk, D] array is formed
+            var = (h2 @ V ** 2 - 2.0 * o * (h2 @ V) + o ** 2 * h2.sum(axis=1, keepdims=True)) / 3.0
+            beta = 2.0 ** -6 / 24.0
             out[b, :, h] = o
-            tol[b, :, h] = 6.0 * sigma + 2.0 ** -8 * np.abs(o) + 2e-3
-    return tol, out
+            tol[b, :, h] = (6.0 * np.sqrt(np.maximum(var, 0.0)) + beta * (P @ np.abs(V) + np.abs(o))
+                            + 2.0 ** -8 * np.abs(o) + 2e-3)
+            ltol[b, h] = 6.0 * np.sqrt(h2.sum(axis=1) / 3.0) + beta + 1e-4
+    return tol, ltol, out
 
 
-def _check_attend(what, got, got_lse, emu_out, emu_lse, tol, pure_out=None, rows=None, heads=None):
+def _check_attend(what, got, got_lse, emu_out, emu_lse, tol, ltol, pure_out=None, rows=None, heads=None):
     g = host(got)
     gl = host(got_lse)
     if rows is not None:
@@ -70,12 +81,14 @@ def _check_attend(what, got, got_lse, emu_out, emu_lse, tol, pure_out=None, rows
         gl = gl[:, heads][:, :, rows]
     d = np.abs(g - emu_out)
     ratio = float((d / tol).max())
-    la = float(np.abs(gl - emu_lse).max())
-    msg = f"  {what}: max err {d.max():.2e}, max err/tol {ratio:.3f}, lse {la:.2e}"
+    ld = np.abs(gl - emu_lse)
+    lratio = float((ld / ltol).max())
+    msg = (f"  {what}: max err {d.max():.2e}, max err/tol {ratio:.3f}; lse max err {ld.max():.2e}, "
+           f"err/tol {lratio:.3f}")
     if pure_out is not None:
         msg += f"; vs pure fp64 max {np.abs(g - pure_out).max():.2e}"
     say(msg)
-    assert ratio <= 1.0 and la <= LSE_ABS, (what, ratio, la)
+    assert ratio <= 1.0 and lratio <= 1.0, (what, ratio, lratio)
 
 
 def _check_codes(what, got, want_fp64, delta):
@@ -119,10 +132,10 @@ def test_fp8_stream_matches_oracle(case):
         out = s.chunk_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
         torch.cuda.synchronize()
         qrot, keys, vals = emu.operands(q, k, v)
-        tol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale)
+        tol, ltol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale)
         _, emu_lse = emu.attend(q, k, v)
         pure_out, _ = hist.attend(q, k, v)
-        _check_attend(f"chunk {c}", out, lse, emu_out, emu_lse, tol, pure_out)
+        _check_attend(f"chunk {c}", out, lse, emu_out, emu_lse, tol, ltol, pure_out)
         if c == 1:                               # the Q scratch of this attend, before any refresh
             qs = s.q_scratch_view().cpu().float().numpy().astype(np.float64).reshape(w.batch, w.heads, nc, -1)
             qpure = pure_ring.staged(q, k, v)[0]
@@ -174,9 +187,9 @@ def test_fp8_full_size_sampled():
     rows = np.unique(np.concatenate([np.arange(4), np.arange(nc - 8, nc), g.choice(nc, 40, replace=False)]))
     qh, kh, vh = q[:, :, heads], k[:, :, heads], v[:, :, heads]
     qrot, keys, vals = emu.operands(qh, kh, vh)
-    tol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale, rows=rows)
+    tol, ltol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale, rows=rows)
     _, emu_lse = emu.attend(qh, kh, vh, rows=list(rows))
     pure_out, _ = hist.attend(qh, kh, vh, rows=list(rows))
-    _check_attend("wan1.3b fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, pure_out[:, rows],
+    _check_attend("wan1.3b fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, ltol, pure_out[:, rows],
                   rows=rows, heads=heads)
     s.close()

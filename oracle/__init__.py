@@ -37,11 +37,11 @@ from .bf16 import round_bf16, is_bf16_exact
 from .fp8 import round_e4m3, is_e4m3_exact
 from .rope import rope_split, token_coords, rope_freqs, rope3d, rotate_temporal
 from .attention import attend, attend_bruteforce, attention_probs
-from .stream import StreamSpec, HistoryOracle, RingOracle, SHIFT_SINK
+from .stream import StreamSpec, HistoryOracle, RingOracle, SHIFT_SINK, fp8_q_scale
 
 __all__ = [
     "round_bf16", "is_bf16_exact", "round_e4m3", "is_e4m3_exact",
     "rope_split", "token_coords", "rope_freqs", "rope3d", "rotate_temporal",
     "attend", "attend_bruteforce", "attention_probs",
-    "StreamSpec", "HistoryOracle", "RingOracle", "SHIFT_SINK",
+    "StreamSpec", "HistoryOracle", "RingOracle", "SHIFT_SINK", "fp8_q_scale",
 ]

@@ -280,12 +280,25 @@ class HistoryOracle(_Common):
         self.sink_fill = s.sink_chunks
 
 
+def fp8_q_scale(spec: StreamSpec) -> float:
+    """The factor the fp8 variant applies to rotated queries before E4M3 rounding:
+    c * 2^k with c = softmax_scale * log2(e) and the integer k that puts it in [1, 2)
+    (for D = 128: c = 0.1275, k = 3, factor 1.0202). Scores then come out of the
+    product in base-2 units once it multiplies by 2^-k, an exact power of two."""
+    c = spec.softmax_scale * math.log2(math.e)
+    k = -math.floor(math.log2(c))
+    return c * 2.0 ** k
+
+
 class RingOracle(_Common):
     """Rotated keys in S sink slots + W window slots; refresh re-rotates stored keys.
 
     storage: None (pure fp64), 'bf16', 'f32' or 'fp8' -- round every stored value
     (rotated Q, rotated K, V, re-rotated K) the way a device cache of that type holds
-    it ('fp8': E4M3, saturating).
+    it ('fp8': E4M3, saturating). The fp8 variant stores the rotated queries scaled by
+    fp8_q_scale(spec) before rounding (the softmax scale in base 2, brought into [1, 2)
+    by a power of two that the product takes back exactly); the stored Q here is that
+    rounded value divided by the same factor, so the scores keep their usual scale.
     """
 
     def __init__(self, spec: StreamSpec, storage: Optional[str] = None):
@@ -349,10 +362,16 @@ class RingOracle(_Common):
                 return self.ring_v[j]
         raise KeyError(chunk_id)
 
+    def _store_q(self, qrot: np.ndarray) -> np.ndarray:
+        if self.storage == "fp8":
+            kappa = fp8_q_scale(self.spec)
+            return round_e4m3(qrot * kappa) / kappa
+        return self._store(qrot)
+
     def staged(self, q, k, v):
         """What the attend call stores before the product: (Qrot, Kself, Vself), each [B,H,Nc,D]."""
         s = self.spec
-        return (self._store(_rotate_chunk(s, q, self.t_next)),
+        return (self._store_q(_rotate_chunk(s, q, self.t_next)),
                 self._store(_rotate_chunk(s, k, self.t_next)),
                 self._store(_heads_major(v)))
 

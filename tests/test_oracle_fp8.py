@@ -8,11 +8,14 @@ even code and values beside it to the nearer neighbour; saturation at +-448; agr
 with PyTorch's float8_e4m3fn cast (a library routine) on random in-range values; and
 the relative / absolute error bounds the fp8 parity tolerance is derived from.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
 
-from oracle import HistoryOracle, RingOracle, StreamSpec, is_e4m3_exact, rotate_temporal, round_e4m3
+from oracle import (HistoryOracle, RingOracle, StreamSpec, fp8_q_scale, is_e4m3_exact, rotate_temporal,
+                    round_e4m3)
 
 
 def _decode(code: int) -> float:
@@ -98,3 +101,28 @@ def test_ring_oracle_fp8_storage():
     o, _ = emu.attend(q, k, v)
     o_pure, _ = HistoryOracle(spec).attend(q, k, v)
     assert np.all(np.isfinite(o)) and np.abs(o - o_pure).max() > 0
+
+
+def test_fp8_q_scale_and_stored_queries():
+    """The query factor is softmax_scale * log2(e) times the power of two that brings it
+    into [1, 2); the stored queries are E4M3 of the scaled values, scaled back."""
+    for d, want in ((128, 1.0 / math.sqrt(128) * math.log2(math.e) * 8),
+                    (64, 1.0 / 8.0 * math.log2(math.e) * 8)):
+        spec = StreamSpec(batch=1, heads=1, head_dim=d, frame_h=2, frame_w=2, frames_per_chunk=1,
+                          sink_chunks=1, window_chunks=1)
+        kappa = fp8_q_scale(spec)
+        assert 1.0 <= kappa < 2.0 and kappa == pytest.approx(want, rel=1e-15)
+    assert fp8_q_scale(StreamSpec(batch=1, heads=1, head_dim=128, frame_h=2, frame_w=2,
+                                  frames_per_chunk=1, sink_chunks=1, window_chunks=1,
+                                  scale=1.0)) == pytest.approx(math.log2(math.e))   # k = 0
+    spec = StreamSpec(batch=1, heads=2, head_dim=128, frame_h=2, frame_w=3, frames_per_chunk=2,
+                      sink_chunks=1, window_chunks=2)
+    g = np.random.default_rng(9)
+    q, k, v = (g.standard_normal((1, spec.tokens_per_chunk, 2, 128)) for _ in range(3))
+    emu, pure = RingOracle(spec, storage="fp8"), RingOracle(spec)
+    qs, ks, vs = emu.staged(q, k, v)
+    qp, kp, vp = pure.staged(q, k, v)
+    kappa = fp8_q_scale(spec)
+    np.testing.assert_array_equal(qs, round_e4m3(qp * kappa) / kappa)
+    np.testing.assert_array_equal(ks, round_e4m3(kp))
+    assert not np.array_equal(qs, round_e4m3(qp))                     # the factor matters

@@ -627,29 +627,42 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     if constexpr (F8) return mfma_fp8(a, b, c);
     else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   };
+  // QK product. fp8: Q is stored times c * 2^k (c = softmax scale * log2 e), and the Q
+  // operand's E8M0 block scale 2^-k takes the power of two back, so scores come out in
+  // base-2 units; the accumulators start from -m (the C operand), so they hold s - m.
+  [[maybe_unused]] const int qk_scale = uniform(p.qk_scale_e8m0);
+  auto mma_qk = [&](const Op& a, const Op& b, const f32x16& c) -> f32x16 {
+    if constexpr (F8) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, qk_scale);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  };
 
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x16{};
   f32x16 sacc[MT];
   Op pb[PSTEPS];
-  float m = -__builtin_inff(), l = 0.f;
+  // running maximum (base 2): bf16 starts from -inf; fp8 from a 0 reference that its
+  // first tile moves (scores arrive already shifted by -m there)
+  float m = F8 ? 0.f : -__builtin_inff(), l = 0.f;
   // fp8: the row sums of the rounded weights come from one more MFMA per tile (the
   // MFMA unit has room, the VALU does not): its A operand is a constant matrix whose
   // row 0 is all E4M3 ones (0x38), so row 0 of the product accumulates
   // sum_k P[k][query]; it lands in element 0 of lanes 0-31 (query l % 32).
   [[maybe_unused]] f32x16 osum = f32x16{};
+  // fp8: -m in every element, the C operand of each tile's first QK step. m starts as a
+  // 0 reference; the first tile of a segment sets it.
+  [[maybe_unused]] f32x16 negm = f32x16{};
   [[maybe_unused]] const int ones4 = l32 == 0 ? 0x38383838 : 0;
   [[maybe_unused]] const i32x8 ones_row = {ones4, ones4, ones4, ones4, ones4, ones4, ones4, ones4};
 
   auto qk = [&](int i) {
     const char* stage = smem + (i % STAGES) * G::BUF;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = F8 ? negm : f32x16{};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) sacc[mt] = mma(k_op(stage, s, mt), bq[s], sacc[mt]);
+      for (int mt = 0; mt < MT; ++mt) sacc[mt] = mma_qk(k_op(stage, s, mt), bq[s], sacc[mt]);
   };
   auto pv = [&](int i) {
     const char* stage = smem + (i % STAGES) * G::BUF;
@@ -676,26 +689,45 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mt][j]);
-    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
-    if (__any(mx > m + kRescaleThreshold)) {
-      const float m_new = fmaxf(m, F8 ? mx - kP8Shift : mx);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      l *= alpha;
-      if constexpr (F8) osum[0] *= alpha;        // the other elements hold zeros
+    if constexpr (F8) {
+      // scores arrive as s - m in base 2; the first tile sets m (largest weight 2^4),
+      // later tiles raise it when a weight would pass 2^8
+      mx = fmaxf(mx, xor32(mx));
+      const bool first = i == 0;
+      if (first || __any(mx > kRescaleThreshold)) {
+        const float dlt = first ? mx - kP8Shift : fmaxf(0.f, mx - kP8Shift);
+        m += dlt;
+        if (!first) {                            // o and osum are still zero on the first tile
+          const float alpha = fast_exp2(-dlt);
+          osum[0] *= alpha;                      // the other elements hold zeros
 #pragma unroll
-      for (int d = 0; d < DT; ++d) o[d] *= alpha;
-    }
-    if constexpr (F8) {                          // byte 16 a + j <- element j of accumulator a
+          for (int d = 0; d < DT; ++d) o[d] *= alpha;
+        }
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sacc[mt][j] -= dlt;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) negm[j] = -m;
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {              // byte 16 a + j <- element j of accumulator a
         float e4[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) e4[k] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + k], p.scale_log2, -m));
+        for (int k = 0; k < 4; ++k) e4[k] = fast_exp2(sacc[w >> 2][4 * (w & 3) + k]);
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4[0], e4[1], 0, false);
         pb[0][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e4[2], e4[3], lo, true);
       }
     } else {
+      mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+      if (__any(mx > m + kRescaleThreshold)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) o[d] *= alpha;
+      }
       float rs = 0.f;
 #pragma unroll
       for (int s = 0; s < PSTEPS; ++s)
@@ -718,18 +750,18 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
     const char* ks = smem + (i % STAGES) * G::BUF;
     const char* vs = smem + ((i - 1) % STAGES) * G::BUF;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = F8 ? negm : f32x16{};
 #pragma unroll
     for (int k = 0; k < KSTEPS * MT; ++k) {
       const int s = k / MT, mt = k % MT;
       const int sv = k / DT, dt = k % DT;
       const Op a = k_op(ks, s, mt);
       const Op v = v_op(vs, sv, dt);
-      sacc[mt] = mma(a, bq[s], sacc[mt]);
+      sacc[mt] = mma_qk(a, bq[s], sacc[mt]);
       o[dt] = mma(v, pb[sv], o[dt]);
     }
     if constexpr (F8) osum = mfma_fp8(ones_row, pb[0], osum);
-    constexpr int AHEAD = PP_READ_AHEAD;                   // steps of operand reads in flight
+    constexpr int AHEAD = F8 ? 1 : PP_READ_AHEAD;          // steps of operand reads in flight
     constexpr int RD = F8 ? 4 : 2;                         // LDS reads per step
     __builtin_amdgcn_sched_group_barrier(0x100, RD * AHEAD, 0);  // operands of steps 0 .. AHEAD-1
 #pragma unroll
@@ -759,6 +791,7 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(o[dt]));
       asm volatile("" : "+v"(osum));
+      asm volatile("" : "+v"(negm));
     }
   };
   issue_tile(0);

@@ -22,6 +22,8 @@
 // 16-byte vectors along the key axis when the slot offset is 16-byte aligned.
 #include "sa_internal.h"
 
+#include <type_traits>
+
 namespace sa {
 namespace {
 
@@ -57,17 +59,24 @@ __device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const RopeWritePa
   return p.w_cs[x * (p.dw >> 1) + (ch >> 1)];
 }
 
-// Rotated pairs of one 16-byte input vector, rounded to the storage type TS.
-template <typename TI, typename TS>
+// Rotated pairs of one 16-byte input vector, rounded to the storage type TS. SCALED:
+// the rotated values are multiplied by `post` before rounding (fp8 queries).
+template <typename TI, typename TS, bool SCALED = false>
 __device__ __forceinline__ VecN<TS, 16 / sizeof(TI)> rotate(const Vec16<TI>& in,
-                                                           const float2 (&cs)[16 / sizeof(TI) / 2]) {
+                                                           const float2 (&cs)[16 / sizeof(TI) / 2],
+                                                           float post = 1.f) {
   constexpr int NP = 16 / sizeof(TI) / 2;
   VecN<TS, 2 * NP> out;
 #pragma unroll
   for (int e = 0; e < NP; ++e) {
     const float u0 = to_f(in.e[2 * e]), u1 = to_f(in.e[2 * e + 1]);
-    out.e[2 * e] = from_f<TS>(u0 * cs[e].x - u1 * cs[e].y);
-    out.e[2 * e + 1] = from_f<TS>(u0 * cs[e].y + u1 * cs[e].x);
+    float r0 = u0 * cs[e].x - u1 * cs[e].y, r1 = u0 * cs[e].y + u1 * cs[e].x;
+    if constexpr (SCALED) {
+      r0 *= post;
+      r1 *= post;
+    }
+    out.e[2 * e] = from_f<TS>(r0);
+    out.e[2 * e + 1] = from_f<TS>(r1);
   }
   return out;
 }
@@ -189,8 +198,10 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
 #pragma unroll
       for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, p, c0 + 2 * e, s_fyx[tl][0], s_fyx[tl][1], s_fyx[tl][2]);
       *reinterpret_cast<VecS*>(kc + static_cast<size_t>(p.row0 + n) * p.D + c0) = rotate<TI, TS>(kv[j], cs);
+      // fp8 queries are stored times q_scale (the base-2 softmax scale brought into [1, 2))
       if constexpr (HAS_Q)
-        *reinterpret_cast<VecS*>(qo + static_cast<size_t>(n) * p.D + c0) = rotate<TI, TS>(qv[j], cs);
+        *reinterpret_cast<VecS*>(qo + static_cast<size_t>(n) * p.D + c0) =
+            rotate<TI, TS, std::is_same_v<TS, fp8e4m3>>(qv[j], cs, p.q_scale);
     }
   }
 

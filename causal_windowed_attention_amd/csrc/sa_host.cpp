@@ -45,6 +45,8 @@ struct Derived {
   int32_t key_stride, q_tiles, max_splits;
   double theta;
   float scale;
+  float q_scale;             // fp8: scale * log2(e) * 2^k in [1, 2), applied to rotated Q
+  int32_t qk_scale_e8m0;     // fp8: 127 - k, the E8M0 block scale that takes 2^k back
   size_t k_off, k_bytes, vt_off, vt_bytes, q_off, q_bytes, part_off, part_bytes, sk_off, sk_bytes, tab_off,
       tab_bytes, total;
 };
@@ -93,6 +95,17 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->theta = c->rope_theta == 0.0 ? 10000.0 : c->rope_theta;
   d->scale = c->softmax_scale == 0.f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->D)))
                                      : c->softmax_scale;
+  d->q_scale = 1.f;
+  d->qk_scale_e8m0 = 127;
+  if (d->dtype == SA_FP8) {
+    // scores leave the fp8 product in base-2 units: Q is stored times c * 2^k (in [1, 2))
+    // and the product multiplies by 2^-k through the Q operand's E8M0 block scale
+    const double c = static_cast<double>(d->scale) * 1.4426950408889634;
+    const int k = -static_cast<int>(std::floor(std::log2(c)));
+    if (k < -126 || k > 126) return SA_ERR_UNSUPPORTED;
+    d->q_scale = static_cast<float>(c * std::ldexp(1.0, k));
+    d->qk_scale_e8m0 = 127 - k;
+  }
   d->key_stride = static_cast<int32_t>(align_up(static_cast<size_t>(keys), 64));
   // bf16 tile copies address one (b, h) region through a buffer resource (32-bit offsets)
   if (static_cast<int64_t>(d->key_stride) * d->D * d->elem >= (int64_t{1} << 31)) return SA_ERR_UNSUPPORTED;
@@ -202,6 +215,7 @@ void fill_temporal(const Derived& d, int64_t t0, int n_frames, float2* out) {
 void base_write_params(const sa_stream* s, RopeWriteParams* p) {
   std::memset(p, 0, sizeof(*p));
   const Derived& d = s->d;
+  p->q_scale = d.q_scale;
   p->kcache = s->kcache();
   p->vtcache = s->vtcache();
   p->h_cs = s->h_cs();
@@ -520,6 +534,7 @@ sa_status sa_chunk_attend(sa_stream* s, const void* q, const void* k, const void
     ap.kv_splits = splits;
     ap.key_tiles = key_tiles;
     ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    ap.qk_scale_e8m0 = d.qk_scale_e8m0;
     ap.sk_groups = sk_groups;
     ap.sk_part_o = reinterpret_cast<float*>(s->ws + d.sk_off);
     ap.sk_part_lse = ap.sk_part_o + static_cast<size_t>(2 * kSkGroups) * sa::kBf16BlockMWide * d.D;
@@ -842,6 +857,7 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
     ap.kv_splits = 1;
     ap.key_tiles = max_tiles;
     ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    ap.qk_scale_e8m0 = d.qk_scale_e8m0;
     ap.n_groups = n_chunks;
     ap.group_rows = d.Nc;
     ap.group_qtiles = group_qtiles;
@@ -927,6 +943,7 @@ sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* cons
     ap.q_tiles = n * group_qtiles;
     ap.kv_splits = 1;
     ap.scale_log2 = static_cast<float>(static_cast<double>(d.scale) * 1.4426950408889634);
+    ap.qk_scale_e8m0 = d.qk_scale_e8m0;
     ap.n_groups = n;
     ap.group_rows = d.Nc;
     ap.group_qtiles = group_qtiles;

@@ -48,6 +48,7 @@ struct RopeWriteParams {
   int32_t n_frames;     // frames covered by t_cs (F)
   int32_t q_rows;       // rows per (b, h) of the Q scratch
   int32_t q_row0;       // first Q scratch row written by this launch
+  float q_scale;        // fp8 cache: factor on rotated Q before rounding (else unused)
   float2 t_cs[kMaxTemporalPairs];  // [frame][d_t/2]: (cos, sin) of (t0 + frame) * theta_t,j
 };
 
@@ -81,6 +82,7 @@ struct AttnParams {
   int32_t kv_splits;    // >= 1
   int32_t key_tiles;    // ceil(n_keys / BlockN)
   float scale_log2;     // softmax_scale * log2(e)
+  int32_t qk_scale_e8m0;  // fp8: E8M0 block scale 2^-k on the Q operand (Q stored times scale_log2 * 2^k)
   int32_t sk_groups;    // > 0: stream-K schedule with this many persistent workgroups (variant 3)
   float* sk_part_o;     // [2 * sk_groups][BlockM][D] stream-K partial outputs
   float* sk_part_lse;   // [2 * sk_groups][BlockM] stream-K partial log2-sum-exp

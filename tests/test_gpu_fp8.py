@@ -1,9 +1,10 @@
 """GPU parity of the fp8 cache variant (SA_FP8) against the fp64 oracle.
 
 What the device stores is checked code by code: V is a plain bf16 -> E4M3 rounding and
-must match the oracle's E4M3 rounding exactly; rotated K and Q come from an fp32
-rotation on the device and an fp64 one in the oracle, so an element may take the other
-neighbour only where the fp32 rotation error can reach an E4M3 rounding boundary.
+must match the oracle's E4M3 rounding exactly; rotated K and Q (Q times the factor
+fp8_q_scale) come from fp32 arithmetic on the device and fp64 in the oracle, so an
+element may take the other neighbour only where the fp32 error can reach an E4M3
+rounding boundary.
 
 Attention is compared with the storage-emulating oracle (RingOracle, storage 'fp8':
 exact softmax over the E4M3-rounded Q, K and V the device holds). The device also
@@ -33,7 +34,7 @@ import torch
 import causal_windowed_attention_amd as cwa
 import synth
 from gpu_util import config_for, dev, host, say, spec_for
-from oracle import HistoryOracle, RingOracle, attention_probs, round_e4m3
+from oracle import HistoryOracle, RingOracle, attention_probs, fp8_q_scale, round_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -138,9 +139,11 @@ def test_fp8_stream_matches_oracle(case):
         _check_attend(f"chunk {c}", out, lse, emu_out, emu_lse, tol, ltol, pure_out)
         if c == 1:                               # the Q scratch of this attend, before any refresh
             qs = s.q_scratch_view().cpu().float().numpy().astype(np.float64).reshape(w.batch, w.heads, nc, -1)
-            qpure = pure_ring.staged(q, k, v)[0]
+            kappa = fp8_q_scale(spec)
+            qwant = kappa * pure_ring.staged(q, k, v)[0]
             qin = np.transpose(q, (0, 2, 1, 3)).astype(np.float64)
-            _check_codes("Q scratch", qs, qpure, _pair_delta(qin))
+            # rotation error times the factor, plus the fp32 product and the fp32 factor itself
+            _check_codes("Q scratch", qs, qwant, kappa * _pair_delta(qin) + 2.0 ** -22 * np.abs(qwant))
         s.kv_append()                            # commit the staged chunk
         for o in (emu, pure_ring, hist):
             o.append(k, v)

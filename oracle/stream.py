@@ -164,30 +164,39 @@ class _Common:
         Returns O [B, n*Nc, H, D], LSE [B, H, n*Nc]."""
         s = self.spec
         nc = s.tokens_per_chunk
-        if q.ndim != 4 or q.shape[1] == 0 or q.shape[1] % nc:
-            raise StreamError("invalid", f"buffer of {q.shape[1] if q.ndim == 4 else '?'} tokens is not whole chunks")
-        n = q.shape[1] // nc
-        self._check_chunk(q, k, v, n_tokens=n * nc)
-        if not steps and self.sink_fill < s.sink_chunks:
-            raise StreamError("bad_state", "a moving-buffer attend needs a full sink")
+        n = q.shape[1] // nc if q.ndim == 4 else 0
         B, H, D = s.batch, s.heads, s.head_dim
         out = np.full((B, n * nc, H, D), np.nan)
         lse = np.full((B, H, n * nc), np.nan)
-        tmp = copy.deepcopy(self)
-        for j in range(n):
-            sl = slice(j * nc, (j + 1) * nc)
-            if steps:                                # same committed context, j chunks further on
-                tmp = copy.deepcopy(self)
-                tmp.t_next = self.t_next + j * s.frames_per_chunk
+        for j, sl, tmp in self._buffer_states(q, k, v, steps):
             r = None if rows is None else [x - j * nc for x in rows if j * nc <= x < (j + 1) * nc]
             if r is None or r:
                 o, lj = tmp.attend(q[:, sl], k[:, sl], v[:, sl], rows=r, heads=heads)
                 out[:, sl], lse[:, :, sl] = o, lj
             else:
                 tmp._check_positions()
+        return out, lse
+
+    def _buffer_states(self, q, k, v, steps):
+        """(j, token slice of chunk j, a copy of the stream in the state chunk j is attended
+        in), for each buffer chunk in order (see buffer_attend); validates the call first."""
+        s = self.spec
+        nc = s.tokens_per_chunk
+        if q.ndim != 4 or q.shape[1] == 0 or q.shape[1] % nc:
+            raise StreamError("invalid", f"buffer of {q.shape[1] if q.ndim == 4 else '?'} tokens is not whole chunks")
+        n = q.shape[1] // nc
+        self._check_chunk(q, k, v, n_tokens=n * nc)
+        if not steps and self.sink_fill < s.sink_chunks:
+            raise StreamError("bad_state", "a moving-buffer attend needs a full sink")
+        tmp = copy.deepcopy(self)
+        for j in range(n):
+            sl = slice(j * nc, (j + 1) * nc)
+            if steps:                                # same committed context, j chunks further on
+                tmp = copy.deepcopy(self)
+                tmp.t_next = self.t_next + j * s.frames_per_chunk
+            yield j, sl, tmp
             if not steps and j + 1 < n:
                 tmp.append(k[:, sl], v[:, sl])
-        return out, lse
 
     def _base(self, new_base):
         if new_base is None or new_base == -1:
@@ -377,7 +386,8 @@ class RingOracle(_Common):
 
     def operands(self, q, k, v):
         """(Qrot, keys, vals) of the attend call: the stored rotated queries [B,H,Nc,D] and
-        the stored visible keys and values, lists of [B,H,Nc,D] in sink, window, self order."""
+        the stored visible keys and values, lists of [B,H,Nc,D] in sink, window, self order
+        (views of the stored slots: a later commit may overwrite them)."""
         qrot, kself, vself = self.staged(q, k, v)
         keys = [self.sink_k[j] for j, m in enumerate(self.sink_meta) if m[0]]
         vals = [self.sink_v[j] for j, m in enumerate(self.sink_meta) if m[0]]
@@ -387,6 +397,16 @@ class RingOracle(_Common):
         keys.append(kself)
         vals.append(vself)
         return qrot, keys, vals
+
+    def buffer_operands(self, q, k, v, steps=False):
+        """operands() of every chunk of a buffer attend, in order (see buffer_attend)."""
+        res = []
+        for _, sl, tmp in self._buffer_states(q, k, v, steps):
+            tmp._check_positions()
+            qrot, keys, vals = tmp.operands(q[:, sl], k[:, sl], v[:, sl])
+            # copies: the slot arrays are overwritten by the next chunk's commit
+            res.append((qrot.copy(), [x.copy() for x in keys], [x.copy() for x in vals]))
+        return res
 
     def attend(self, q, k, v, rows=None, heads=None):
         self._check_chunk(q, k, v)

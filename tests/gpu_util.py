@@ -11,7 +11,7 @@ import torch
 
 import causal_windowed_attention_amd as cwa
 import synth
-from oracle import StreamSpec
+from oracle import StreamSpec, attention_probs
 
 
 def say(*a):
@@ -66,3 +66,58 @@ def bf16_ulp_distance(a: torch.Tensor, b: np.ndarray) -> int:
 # bf16 tolerances (fp32 accumulation): max abs and relative L2 must both hold
 BF16_ABS, BF16_REL = 2e-2, 1e-2
 F32_ABS = 1e-4
+
+
+def fp8_tolerance(qrot, keys, vals, scale, rows=None):
+    """Per-element output tolerance [B, Nq, H, D], LSE tolerance [B, H, Nq] and the
+    emulated output, from the stored operands of one attend of an fp8 stream.
+
+    Derivation (the device rounds the softmax weights to E4M3 and normalises by the sum
+    of the rounded weights, which the storage-emulating oracle does not): weight j of
+    row i, in units of the normalised weights P_ij, is off by e_ij with |e_ij| <= h_ij =
+    max(2^-4 P_ij, 2^-10 max_j P_ij / 2^4) (relative half-step of E4M3's normal range;
+    half the subnormal step at the kernel's weight scale, where a row's largest weight
+    is at least 2^4). To first order O_i moves by sum_j e_ij (v_j - O_i) and LSE_i by
+    sum_j e_ij; independent errors with variance <= h^2 / 3 give 6-sigma bounds. Round
+    to nearest is biased low on the falling density of exponentials by at most
+    beta = 2^-6 / 24 per weight (relative), added as beta (P|V| + |O|) and beta. Plus
+    2^-8 |O| for the bf16 output and 2e-3 / 1e-4 for fp32 accumulation and the fp8
+    MFMA's own (at most 5e-5 of sum |products| on N(0,1)-like E4M3 data, unbiased)."""
+    B, H, Nc, D = qrot.shape
+    r = np.arange(Nc) if rows is None else np.asarray(rows)
+    tol = np.zeros((B, len(r), H, D))
+    ltol = np.zeros((B, H, len(r)))
+    out = np.zeros((B, len(r), H, D))
+    for b in range(B):
+        for h in range(H):
+            K = np.concatenate([k[b, h] for k in keys], axis=0)
+            V = np.concatenate([v[b, h] for v in vals], axis=0)
+            P = attention_probs(qrot[b, h, r], K, scale)
+            h2 = np.maximum(2.0 ** -4 * P, 2.0 ** -10 * P.max(axis=1, keepdims=True) / 16.0) ** 2
+            o = P @ V
+            # sum_j h_ij^2 (v_jd - o_id)^2 expanded so no [Nq, Nk, D] array is formed
+            var = (h2 @ V ** 2 - 2.0 * o * (h2 @ V) + o ** 2 * h2.sum(axis=1, keepdims=True)) / 3.0
+            beta = 2.0 ** -6 / 24.0
+            out[b, :, h] = o
+            tol[b, :, h] = (6.0 * np.sqrt(np.maximum(var, 0.0)) + beta * (P @ np.abs(V) + np.abs(o))
+                            + 2.0 ** -8 * np.abs(o) + 2e-3)
+            ltol[b, h] = 6.0 * np.sqrt(h2.sum(axis=1) / 3.0) + beta + 1e-4
+    return tol, ltol, out
+
+
+def check_fp8_attend(what, got, got_lse, emu_out, emu_lse, tol, ltol, pure_out=None, rows=None, heads=None):
+    g = host(got)
+    gl = host(got_lse)
+    if rows is not None:
+        g = g[:, rows][:, :, heads]
+        gl = gl[:, heads][:, :, rows]
+    d = np.abs(g - emu_out)
+    ratio = float((d / tol).max())
+    ld = np.abs(gl - emu_lse)
+    lratio = float((ld / ltol).max())
+    msg = (f"  {what}: max err {d.max():.2e}, max err/tol {ratio:.3f}; lse max err {ld.max():.2e}, "
+           f"err/tol {lratio:.3f}")
+    if pure_out is not None:
+        msg += f"; vs pure fp64 max {np.abs(g - pure_out).max():.2e}"
+    say(msg)
+    assert ratio <= 1.0 and lratio <= 1.0, (what, ratio, lratio)

@@ -10,14 +10,18 @@ import torch
 
 import causal_windowed_attention_amd as cwa
 import synth
-from gpu_util import BF16_ABS, BF16_REL, F32_ABS, config_for, dev, err, host, say, spec_for
-from oracle import HistoryOracle
+from gpu_util import (BF16_ABS, BF16_REL, F32_ABS, check_fp8_attend, config_for, dev, err, fp8_tolerance, host,
+                      say, spec_for)
+from oracle import HistoryOracle, RingOracle
 
 CASES = {
     "f32_tiny": ("tiny_f32", {}),
     "bf16_d128": ("wan1.3b", dict(heads=2, frame_h=6, frame_w=10, frames_per_chunk=3, window_chunks=3)),
     "bf16_d64_b2": ("wan1.3b", dict(batch=2, heads=2, head_dim=64, frame_h=5, frame_w=7, frames_per_chunk=2,
                                     sink_chunks=2, window_chunks=2)),
+    # fp8 cache: each entry against its own fp8 storage-emulating oracle (derived tolerance)
+    "fp8_d128_b2": ("wan1.3b", dict(batch=2, heads=2, frame_h=5, frame_w=7, frames_per_chunk=2,
+                                    sink_chunks=1, window_chunks=2, dtype="fp8")),
 }
 
 
@@ -31,7 +35,8 @@ def test_batch_attend_matches_per_stream_oracles(case):
         "S", w.sink_chunks, "W", w.window_chunks, "streams", n)
     cfg = config_for(w)
     streams = [cwa.Stream(cfg) for _ in range(n)]
-    hists = [HistoryOracle(spec_for(w)) for _ in range(n)]
+    fp8 = w.dtype == "fp8"
+    hists = [RingOracle(spec_for(w), storage="fp8") if fp8 else HistoryOracle(spec_for(w)) for _ in range(n)]
     seq = [0] * n
 
     def chunk(i):
@@ -51,8 +56,13 @@ def test_batch_attend_matches_per_stream_oracles(case):
         lses = [torch.empty((w.batch, w.heads, w.tokens_per_chunk), dtype=torch.float32, device="cuda")
                 for _ in range(n)]
         cwa.sa_batch_attend(streams, qs, ks, vs, outs, lses)
+        torch.cuda.synchronize()
         for i in range(n):
             want, want_lse = hists[i].attend(*data[i])
+            if fp8:
+                tol, ltol, emu_out = fp8_tolerance(*hists[i].operands(*data[i]), spec_for(w).softmax_scale)
+                check_fp8_attend(f"  round {rnd} stream {i}", outs[i], lses[i], emu_out, want_lse, tol, ltol)
+                continue
             a, r = err(host(outs[i]), want)
             la, _ = err(host(lses[i]), want_lse)
             say(f"  round {rnd} stream {i} ({streams[i].query()['visible_keys']} keys): "

@@ -14,8 +14,9 @@ import torch
 
 import causal_windowed_attention_amd as cwa
 import synth
-from gpu_util import BF16_ABS, BF16_REL, F32_ABS, config_for, dev, err, host, say, spec_for
-from oracle import HistoryOracle
+from gpu_util import (BF16_ABS, BF16_REL, F32_ABS, check_fp8_attend, config_for, dev, err, fp8_tolerance, host,
+                      say, spec_for)
+from oracle import HistoryOracle, RingOracle
 
 CASES = {
     # name: (base workload, overrides, max_buffer_chunks)
@@ -26,6 +27,9 @@ CASES = {
     "bf16_w0": ("wan1.3b", dict(heads=1, frame_h=4, frame_w=9, frames_per_chunk=2, window_chunks=0), 3),
     "bf16_s0": ("wan1.3b", dict(heads=1, frame_h=4, frame_w=9, frames_per_chunk=2, sink_chunks=0,
                                 window_chunks=2), 3),
+    # fp8 cache: judged against the fp8 storage-emulating oracle with the derived tolerance
+    "fp8_d128": ("wan1.3b", dict(heads=2, frame_h=6, frame_w=10, frames_per_chunk=3, window_chunks=3,
+                                 dtype="fp8"), 5),
 }
 
 
@@ -53,7 +57,9 @@ def test_buffer_attend_matches_oracle(case, steps):
     say("buffer", case, "steps" if steps else "banded", w.dtype, "H", w.heads, "D", w.head_dim, "Nc", w.tokens_per_chunk,
         "S", w.sink_chunks, "W", w.window_chunks, "NB", nb)
     s = cwa.Stream(config_for(w, max_buffer_chunks=nb))
-    hist = HistoryOracle(spec_for(w))
+    spec = spec_for(w)
+    hist = HistoryOracle(spec)
+    emu = RingOracle(spec, storage="fp8") if w.dtype == "fp8" else None
     state = {"c": 0}
 
     def commit(k_times):
@@ -61,7 +67,22 @@ def test_buffer_attend_matches_oracle(case, steps):
             _, k, v = synth.chunk_qkv(w, state["c"])
             s.kv_append(dev(k, w.dtype), dev(v, w.dtype))
             hist.append(k, v)
+            if emu is not None:
+                emu.append(k, v)
             state["c"] += 1
+
+    def check(out, lse, q, k, v, what, steps_mode, n):
+        if emu is None:
+            want, want_lse = hist.buffer_attend(q, k, v, steps=steps_mode)
+            _check(w, out, want, lse, want_lse, what)
+            return
+        nc = w.tokens_per_chunk
+        want_lse = emu.buffer_attend(q, k, v, steps=steps_mode)[1]
+        for j, (qrot, keys, vals) in enumerate(emu.buffer_operands(q, k, v, steps=steps_mode)):
+            tol, ltol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale)
+            sl = slice(j * nc, (j + 1) * nc)
+            check_fp8_attend(f"{what}, chunk {j}", out[:, sl], lse[:, :, sl], emu_out, want_lse[:, :, sl],
+                             tol, ltol)
 
     # a moving-buffer attend needs a full sink; steps start with nothing committed
     schedule = [(0 if steps else w.sink_chunks, 1), (0, nb), (1, 2), ("refresh", None), (1, nb),
@@ -69,20 +90,22 @@ def test_buffer_attend_matches_oracle(case, steps):
     for i, (commits, n) in enumerate(schedule):
         if commits == "refresh":
             assert s.rope_refresh(-1, 0) == hist.refresh(None, 0)
+            if emu is not None:
+                emu.refresh(None, 0)
             continue
         commit(commits)
         q, k, v = _buffer(w, 500 + 10 * i, n)
         lse = torch.empty((w.batch, w.heads, n * w.tokens_per_chunk), dtype=torch.float32, device="cuda")
         out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse, steps=steps)
-        want, want_lse = hist.buffer_attend(q, k, v, steps=steps)
-        _check(w, out, want, lse, want_lse, f"step {i}: {commits} commits then a buffer of {n}")
+        torch.cuda.synchronize()
+        check(out, lse, q, k, v, f"step {i}: {commits} commits then a buffer of {n}", steps, n)
         assert s.query()["staged_valid"] == 0
     # an ordinary attend afterwards is unaffected by the buffer slots
     q, k, v = synth.chunk_qkv(w, 900)
     lse = torch.empty((w.batch, w.heads, w.tokens_per_chunk), dtype=torch.float32, device="cuda")
     out = s.chunk_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), lse=lse)
-    want, want_lse = hist.attend(q, k, v)
-    _check(w, out, want, lse, want_lse, "chunk attend after the buffers")
+    torch.cuda.synchronize()
+    check(out, lse, q, k, v, "chunk attend after the buffers", False, 1)
     s.close()
 
 

@@ -33,8 +33,8 @@ import torch
 
 import causal_windowed_attention_amd as cwa
 import synth
-from gpu_util import config_for, dev, host, say, spec_for
-from oracle import HistoryOracle, RingOracle, attention_probs, fp8_q_scale, round_e4m3
+from gpu_util import check_fp8_attend, config_for, dev, fp8_tolerance, host, say, spec_for
+from oracle import HistoryOracle, RingOracle, fp8_q_scale, round_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -47,49 +47,6 @@ CASES = {
 
 def _workload(**kw):
     return synth.small_variant(synth.WORKLOADS["wan1.3b"], dtype="fp8", **kw)
-
-
-def fp8_tolerance(qrot, keys, vals, scale, rows=None):
-    """Per-element output tolerance [B, Nq, H, D], LSE tolerance [B, H, Nq] and the
-    emulated output, from the stored operands of one attend (see the module docstring)."""
-    B, H, Nc, D = qrot.shape
-    r = np.arange(Nc) if rows is None else np.asarray(rows)
-    tol = np.zeros((B, len(r), H, D))
-    ltol = np.zeros((B, H, len(r)))
-    out = np.zeros((B, len(r), H, D))
-    for b in range(B):
-        for h in range(H):
-            K = np.concatenate([k[b, h] for k in keys], axis=0)
-            V = np.concatenate([v[b, h] for v in vals], axis=0)
-            P = attention_probs(qrot[b, h, r], K, scale)
-            h2 = np.maximum(2.0 ** -4 * P, 2.0 ** -10 * P.max(axis=1, keepdims=True) / 16.0) ** 2
-            o = P @ V
-            # sum_j h_ij^2 (v_jd - o_id)^2 expanded so no [Nq, Nk, D] array is formed
-            var = (h2 @ V ** 2 - 2.0 * o * (h2 @ V) + o ** 2 * h2.sum(axis=1, keepdims=True)) / 3.0
-            beta = 2.0 ** -6 / 24.0
-            out[b, :, h] = o
-            tol[b, :, h] = (6.0 * np.sqrt(np.maximum(var, 0.0)) + beta * (P @ np.abs(V) + np.abs(o))
-                            + 2.0 ** -8 * np.abs(o) + 2e-3)
-            ltol[b, h] = 6.0 * np.sqrt(h2.sum(axis=1) / 3.0) + beta + 1e-4
-    return tol, ltol, out
-
-
-def _check_attend(what, got, got_lse, emu_out, emu_lse, tol, ltol, pure_out=None, rows=None, heads=None):
-    g = host(got)
-    gl = host(got_lse)
-    if rows is not None:
-        g = g[:, rows][:, :, heads]
-        gl = gl[:, heads][:, :, rows]
-    d = np.abs(g - emu_out)
-    ratio = float((d / tol).max())
-    ld = np.abs(gl - emu_lse)
-    lratio = float((ld / ltol).max())
-    msg = (f"  {what}: max err {d.max():.2e}, max err/tol {ratio:.3f}; lse max err {ld.max():.2e}, "
-           f"err/tol {lratio:.3f}")
-    if pure_out is not None:
-        msg += f"; vs pure fp64 max {np.abs(g - pure_out).max():.2e}"
-    say(msg)
-    assert ratio <= 1.0 and lratio <= 1.0, (what, ratio, lratio)
 
 
 def _check_codes(what, got, want_fp64, delta):
@@ -136,7 +93,7 @@ def test_fp8_stream_matches_oracle(case):
         tol, ltol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale)
         _, emu_lse = emu.attend(q, k, v)
         pure_out, _ = hist.attend(q, k, v)
-        _check_attend(f"chunk {c}", out, lse, emu_out, emu_lse, tol, ltol, pure_out)
+        check_fp8_attend(f"chunk {c}", out, lse, emu_out, emu_lse, tol, ltol, pure_out)
         if c == 1:                               # the Q scratch of this attend, before any refresh
             qs = s.q_scratch_view().cpu().float().numpy().astype(np.float64).reshape(w.batch, w.heads, nc, -1)
             kappa = fp8_q_scale(spec)
@@ -193,6 +150,6 @@ def test_fp8_full_size_sampled():
     tol, ltol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale, rows=rows)
     _, emu_lse = emu.attend(qh, kh, vh, rows=list(rows))
     pure_out, _ = hist.attend(qh, kh, vh, rows=list(rows))
-    _check_attend("wan1.3b fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, ltol, pure_out[:, rows],
+    check_fp8_attend("wan1.3b fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, ltol, pure_out[:, rows],
                   rows=rows, heads=heads)
     s.close()

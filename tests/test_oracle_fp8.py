@@ -126,3 +126,29 @@ def test_fp8_q_scale_and_stored_queries():
     np.testing.assert_array_equal(qs, round_e4m3(qp * kappa) / kappa)
     np.testing.assert_array_equal(ks, round_e4m3(kp))
     assert not np.array_equal(qs, round_e4m3(qp))                     # the factor matters
+
+
+@pytest.mark.parametrize("steps", [False, True])
+def test_buffer_operands_reproduce_buffer_attend(steps):
+    """The per-chunk operands of a buffer attend (used to derive fp8 tolerances) give back
+    the buffer attend's own outputs when attended."""
+    from oracle import attend
+    spec = StreamSpec(batch=1, heads=2, head_dim=16, frame_h=2, frame_w=3, frames_per_chunk=2,
+                      sink_chunks=1, window_chunks=2)
+    g = np.random.default_rng(11)
+    nc = spec.tokens_per_chunk
+    emu = RingOracle(spec, storage="fp8")
+    for _ in range(3):
+        emu.append(g.standard_normal((1, nc, 2, 16)), g.standard_normal((1, nc, 2, 16)))
+    q, k, v = (g.standard_normal((1, 3 * nc, 2, 16)) for _ in range(3))
+    out, lse = emu.buffer_attend(q, k, v, steps=steps)
+    ops = emu.buffer_operands(q, k, v, steps=steps)
+    assert len(ops) == 3
+    for j, (qrot, keys, vals) in enumerate(ops):
+        for h in range(2):
+            K = np.concatenate([x[0, h] for x in keys])
+            V = np.concatenate([x[0, h] for x in vals])
+            o, l = attend(qrot[0, h], K, V, spec.softmax_scale)
+            np.testing.assert_allclose(o, out[0, j * nc:(j + 1) * nc, h], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l, lse[0, h, j * nc:(j + 1) * nc], rtol=0, atol=1e-12)
+    assert len(ops[2][1]) == 4                        # sink, two window chunks, itself

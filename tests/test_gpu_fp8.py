@@ -123,13 +123,16 @@ def test_fp8_stream_matches_oracle(case):
     s.close()
 
 
-def test_fp8_full_size_sampled():
-    """wan1.3b shape (H = 12, Nc = 4680, S = 1, W = 6) with an fp8 cache, after the ring
-    has wrapped: sampled rows of two heads against the storage-emulating oracle."""
-    w = synth.small_variant(synth.WORKLOADS["wan1.3b"], dtype="fp8")
+@pytest.mark.parametrize("name", ["wan1.3b", "wan14b_b2", "hybrid1280x704", "long512p"])
+def test_fp8_full_size_sampled(name):
+    """Full workload shapes with an fp8 cache (wan1.3b: H = 12, Nc = 4680, S = 1, W = 6;
+    wan14b_b2: two streams of 40 heads; hybrid1280x704: outlier channels scaled x8 in Q and
+    K; long512p: H = 24, Nc = 2048), after the ring has wrapped: sampled rows of two heads
+    against the storage-emulating oracle."""
+    w = synth.small_variant(synth.WORKLOADS[name], dtype="fp8")
     nc = w.tokens_per_chunk
     heads = [0, w.heads - 1]
-    say(f"fp8 wan1.3b full size: H {w.heads} Nc {nc}; heads {heads}")
+    say(f"fp8 {name} full size: B {w.batch} H {w.heads} Nc {nc}; heads {heads}")
     s = cwa.Stream(config_for(w))
     spec = spec_for(w, heads)
     emu, hist = RingOracle(spec, storage="fp8"), HistoryOracle(spec)
@@ -150,6 +153,6 @@ def test_fp8_full_size_sampled():
     tol, ltol, emu_out = fp8_tolerance(qrot, keys, vals, spec.softmax_scale, rows=rows)
     _, emu_lse = emu.attend(qh, kh, vh, rows=list(rows))
     pure_out, _ = hist.attend(qh, kh, vh, rows=list(rows))
-    check_fp8_attend("wan1.3b fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, ltol, pure_out[:, rows],
+    check_fp8_attend(f"{name} fp8 sampled", out, lse, emu_out, emu_lse[:, :, rows], tol, ltol, pure_out[:, rows],
                   rows=rows, heads=heads)
     s.close()

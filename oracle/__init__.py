@@ -16,6 +16,8 @@ Plain, slow, obviously correct NumPy code for what the GPU path computes:
                    bounded ring, re-rotated on refresh, optionally rounding every
                    stored value to bfloat16 the way a bf16 device cache does).
 * ``bf16``      -- direct float64 -> bfloat16 round-to-nearest-even.
+* ``gdn``       -- the gated delta rule (GDN linear attention) as the plain token loop
+                   (published Gated DeltaNet recurrence; the pages name the block only).
 * ``fp8``       -- direct float64 -> E4M3 (OCP 8-bit float) round-to-nearest-even,
                    saturating at +-448, for the storage-emulating oracle of the
                    fp8 cache variant.
@@ -35,12 +37,13 @@ number for this path.
 """
 from .bf16 import round_bf16, is_bf16_exact
 from .fp8 import round_e4m3, is_e4m3_exact
+from .gdn import gdn_recurrent
 from .rope import rope_split, token_coords, rope_freqs, rope3d, rotate_temporal
 from .attention import attend, attend_bruteforce, attention_probs
 from .stream import StreamSpec, HistoryOracle, RingOracle, SHIFT_SINK, fp8_q_scale
 
 __all__ = [
-    "round_bf16", "is_bf16_exact", "round_e4m3", "is_e4m3_exact",
+    "round_bf16", "is_bf16_exact", "round_e4m3", "is_e4m3_exact", "gdn_recurrent",
     "rope_split", "token_coords", "rope_freqs", "rope3d", "rotate_temporal",
     "attend", "attend_bruteforce", "attention_probs",
     "StreamSpec", "HistoryOracle", "RingOracle", "SHIFT_SINK", "fp8_q_scale",

@@ -26,6 +26,7 @@ __all__ = [
     "sa_stream_create", "sa_stream_destroy", "sa_chunk_attend", "sa_kv_append",
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
     "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16",
+    "sa_gdn_workspace_bytes", "sa_gdn_forward", "gdn_forward",
     "sa_buffer_attend", "sa_buffer_plan", "sa_batch_attend", "Stream",
     "SA_F32", "SA_BF16", "SA_FP8", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
     "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
@@ -187,6 +188,45 @@ def sa_batch_attend(handles, qs, ks, vs, outs, lses=None, stream=None) -> None:
 def sa_probe_mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
     """Launch the pure-MFMA measurement kernel (out: float32 device tensor of blocks*256)."""
     _check(L.load().sa_probe_mfma_bf16(_ptr(out), blocks, iters, _stream_ptr(stream)), "sa_probe_mfma_bf16")
+
+
+def sa_gdn_workspace_bytes(batch: int, tokens: int, heads: int, head_dim: int) -> int:
+    return int(L.load().sa_gdn_workspace_bytes(batch, tokens, heads, head_dim))
+
+
+def sa_gdn_forward(batch, tokens, heads, head_dim, q, k, v, alpha, beta, state_in, state_out, out, workspace,
+                   workspace_bytes, stream=None) -> None:
+    _check(L.load().sa_gdn_forward(batch, tokens, heads, head_dim, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(workspace),
+                                   workspace_bytes, _stream_ptr(stream)), "sa_gdn_forward")
+
+
+def gdn_forward(q, k, v, alpha, beta, state=None, out=None, state_out=None, workspace=None, stream=None):
+    """Gated delta rule forward (see sa_gdn_forward): q, k, v [B, N, H, D] bf16 CUDA tensors,
+    alpha, beta [B, H, N] float32, state [B, H, D, D] float32 or None. Returns (out, state_out);
+    state_out may be the state tensor itself (updated in place)."""
+    import torch
+    B, N, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if tuple(t.shape) != (B, N, H, D) or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{n}: expected contiguous bf16 CUDA [B, N, H, D], got {t.dtype} {tuple(t.shape)}")
+    for t, n in ((alpha, "alpha"), (beta, "beta")):
+        if tuple(t.shape) != (B, H, N) or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{n}: expected contiguous float32 CUDA [B, H, N]")
+    for t, n in ((state, "state"), (state_out, "state_out")):
+        if t is not None and (tuple(t.shape) != (B, H, D, D) or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{n}: expected contiguous float32 [B, H, D, D]")
+    if out is None:
+        out = torch.empty_like(v)
+    if state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    need = sa_gdn_workspace_bytes(B, N, H, D)
+    if need == 0:
+        raise SaError(L.SA_ERR_UNSUPPORTED, "gdn_forward: unsupported sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    sa_gdn_forward(B, N, H, D, q, k, v, alpha, beta, state, state_out, out, workspace, workspace.numel(), stream)
+    return out, state_out
 
 
 class Stream:

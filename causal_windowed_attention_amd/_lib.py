@@ -97,6 +97,8 @@ SIGNATURES = {
                                       ctypes.POINTER(_I32)]),
     "sa_batch_attend": (ctypes.c_int, [_I32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                                        ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
+    "sa_gdn_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "sa_gdn_forward": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib = None

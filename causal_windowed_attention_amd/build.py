@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsa.so")
-SOURCES = ["sa_host.cpp", "rope_kernels.hip", "attention_kernels.hip"]
+SOURCES = ["sa_host.cpp", "rope_kernels.hip", "attention_kernels.hip", "gdn_kernels.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

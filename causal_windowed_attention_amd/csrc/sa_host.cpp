@@ -975,3 +975,78 @@ sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* 
 }
 
 }  // extern "C"
+
+// ---- gated delta rule (GDN) forward ----------------------------------------------------------
+
+namespace {
+
+struct GdnLayout {
+  size_t g, W, Up, U, Sst, total;
+  int32_t nb;
+};
+
+sa_status gdn_layout(int32_t B, int32_t N, int32_t H, int32_t D, GdnLayout* L) {
+  if (B < 1 || H < 1 || N < 0) return SA_ERR_INVALID_ARGUMENT;
+  if (D != 64 && D != 128) return SA_ERR_UNSUPPORTED;
+  if (B > 32767 || H > 32767 || N > (1 << 24)) return SA_ERR_UNSUPPORTED;
+  const int64_t nb = (static_cast<int64_t>(N) + sa::kGdnBlock - 1) / sa::kGdnBlock;
+  const size_t bhb = static_cast<size_t>(B) * H * static_cast<size_t>(nb);
+  size_t off = 0;
+  L->nb = static_cast<int32_t>(nb);
+  L->g = off; off = align_up(off + bhb * sa::kGdnBlock * 4, kAlign);
+  L->W = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
+  L->Up = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
+  L->U = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
+  L->Sst = off; off = align_up(off + bhb * static_cast<size_t>(D) * D * 4, kAlign);
+  L->total = off > kAlign ? off : kAlign;        // never 0: 0 means unsupported sizes
+  return SA_OK;
+}
+
+}  // namespace
+
+size_t sa_gdn_workspace_bytes(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim) {
+  GdnLayout L;
+  return gdn_layout(batch, tokens, heads, head_dim, &L) == SA_OK ? L.total : 0;
+}
+
+sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const float* state_in, float* state_out, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  GdnLayout L;
+  const sa_status st = gdn_layout(batch, tokens, heads, head_dim, &L);
+  if (st != SA_OK) return st;
+  auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (state_out == nullptr || !a4(state_out) || (state_in != nullptr && !a4(state_in))) return SA_ERR_INVALID_ARGUMENT;
+  if (tokens > 0) {                              // with no tokens only the state is touched
+    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || out == nullptr ||
+        workspace == nullptr)
+      return SA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) || !a4(alpha) ||
+        !a4(beta))
+      return SA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < L.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  char* ws = static_cast<char*>(workspace);
+  sa::GdnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q; p.k = k; p.v = v;
+  p.alpha = alpha; p.beta = beta;
+  p.state_in = state_in; p.state_out = state_out;
+  p.out = out;
+  p.g = reinterpret_cast<float*>(ws + L.g);
+  p.W = reinterpret_cast<float*>(ws + L.W);
+  p.Up = reinterpret_cast<float*>(ws + L.Up);
+  p.U = reinterpret_cast<float*>(ws + L.U);
+  p.Sst = reinterpret_cast<float*>(ws + L.Sst);
+  p.B = batch; p.N = tokens; p.H = heads; p.D = head_dim; p.nb = L.nb;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (tokens == 0) {                             // no tokens: the state passes through
+    const size_t n = static_cast<size_t>(batch) * heads * head_dim * head_dim * 4;
+    if (state_in == nullptr) return hipMemsetAsync(state_out, 0, n, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
+    if (state_in == state_out) return SA_OK;
+    return hipMemcpyAsync(state_out, state_in, n, hipMemcpyDeviceToDevice, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
+  }
+  return sa::launch_gdn_forward(p, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
+}
+

@@ -107,6 +107,29 @@ struct AttnParams {
 
 constexpr int kMaxSkGroups = 512;
 
+// Gated delta rule (GDN) forward, chunkwise: tokens in blocks of kGdnBlock; the state scan
+// runs kGdnScanRows rows of each (b, h) state per workgroup.
+constexpr int kGdnBlock = 64;
+constexpr int kGdnScanRows = 16;
+
+struct GdnParams {
+  const void* q;          // [B, N, H, D] bf16
+  const void* k;          // [B, N, H, D] bf16
+  const void* v;          // [B, N, H, D] bf16
+  const float* alpha;     // [B, H, N] decay gates in (0, 1]
+  const float* beta;      // [B, H, N] write strengths in [0, 1]
+  const float* state_in;  // [B, H, D, D] (Dv x Dk), or null for zeros
+  float* state_out;       // [B, H, D, D]; may equal state_in
+  void* out;              // [B, N, H, D] bf16
+  // workspace (nb = ceil(N / kGdnBlock) blocks per (b, h))
+  float* g;               // [B*H][nb*64] log of the cumulative gate within each block
+  float* W;               // [B*H][nb][64][D] T diag(gam) K
+  float* Up;              // [B*H][nb][64][D] T V
+  float* U;               // [B*H][nb][64][D] pseudo-values
+  float* Sst;             // [B*H][nb][D][D] state at each block start
+  int32_t B, N, H, D, nb;
+};
+
 struct CombineParams {
   const float* part_o;
   const float* part_lse;
@@ -124,5 +147,6 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
 hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st);
 hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
+hipError_t launch_gdn_forward(const GdnParams& p, hipStream_t st);
 
 }  // namespace sa

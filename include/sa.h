@@ -352,6 +352,39 @@ sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int
  */
 sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* stream);
 
+/*
+ * Gated delta rule (GDN linear attention; SANA-Streaming, "Transformer a diffusione
+ * ibrido": most blocks keep a fixed-size recurrent state per head, updated as the
+ * stream advances, and only the final state is kept between chunks). The pages give no
+ * equations; this is the published gated delta rule (Yang, Kautz and Hatamizadeh,
+ * "Gated Delta Networks", ICLR 2025), token by token in (frame, y, x) order:
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t,
+ * S of size D x D (value rows, key columns) per (b, h).
+ *
+ * sa_gdn_workspace_bytes: device workspace sa_gdn_forward needs for these sizes (0 for
+ * unsupported sizes): per 64-token block of each (b, h), fp32 gates, two 64 x D
+ * products, the pseudo-values and the block's starting state (D x D).
+ *
+ * sa_gdn_forward: q, k, v: [B, N, H, D] bf16 (token-major, like sa_chunk_attend's
+ * inputs; q and k as the caller prepared them, GDN normalises them to unit length);
+ * alpha, beta: [B, H, N] float32 (alpha in (0, 1], beta in [0, 1]); state_in:
+ * [B, H, D, D] float32 or NULL for zeros; state_out: [B, H, D, D] float32, may equal
+ * state_in; out: [B, N, H, D] bf16. N may be any count >= 0 (a ragged last block is
+ * padded with alpha = 1, beta = 0). Arithmetic is fp32 (chunkwise: 64-token blocks,
+ * a triangular solve per block, the state carried block to block). All buffers are
+ * the caller's; nothing is allocated. With N = 0 only state_in / state_out are used
+ * (the state passes through; the others may be NULL). Errors: SA_ERR_INVALID_ARGUMENT
+ * for NULL or misaligned pointers (16 bytes for bf16 tensors and the workspace, 4 for
+ * float32) or sizes < 1 (N < 0);
+ * SA_ERR_UNSUPPORTED for D not 64 or 128, H or B beyond 32767, N beyond 2^24;
+ * SA_ERR_WORKSPACE_TOO_SMALL; SA_ERR_DEVICE if a launch fails.
+ */
+size_t sa_gdn_workspace_bytes(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim);
+sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const float* state_in, float* state_out, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,3 +215,28 @@ def distinct_set_for(w: Workload, checked) -> frozenset:
             s.add(j)
     return frozenset(s)
 
+
+
+# tensor ids of the gated delta rule (GDN) inputs
+T_GDN = 16
+
+
+def gdn_inputs(batch: int, tokens: int, heads: int, head_dim: int, seed: int, state: bool = True):
+    """Seeded inputs of the gated delta rule (GDN linear attention) block, as the layer would
+    hand them over: q and k drawn N(0, 1), scaled to unit length per token and head (GDN's
+    own normalisation, input preparation here) and rounded to bf16; v N(0, 1) in bf16;
+    decay gates alpha ~ U[0.9, 1] and write strengths beta ~ U[0, 1] in float32 ([B, H, N]);
+    an initial state [B, H, D, D] drawn N(0, 1/D) (or None). Returns float32 arrays (the
+    bf16 tensors bf16-exact): q, k, v [B, N, H, D], alpha, beta, state."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, T_GDN, seed])))
+    shape = (batch, tokens, heads, head_dim)
+    q = g.standard_normal(shape, dtype=np.float32)
+    k = g.standard_normal(shape, dtype=np.float32)
+    q = to_bf16_exact(q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-6))
+    k = to_bf16_exact(k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-6))
+    v = to_bf16_exact(g.standard_normal(shape, dtype=np.float32))
+    alpha = g.uniform(0.9, 1.0, (batch, heads, tokens)).astype(np.float32)
+    beta = g.uniform(0.0, 1.0, (batch, heads, tokens)).astype(np.float32)
+    s0 = (g.standard_normal((batch, heads, head_dim, head_dim), dtype=np.float32) / np.sqrt(head_dim)
+          if state else None)
+    return q, k, v, alpha, beta, s0

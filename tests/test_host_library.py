@@ -434,3 +434,29 @@ def test_fp8_config_and_planning():
         assert a[key] == b[key], key
     s8.close()
     s16.close()
+
+
+def test_gdn_sizes_and_errors():
+    """The GDN entry points validate on the host before any device work."""
+    need = cwa.sa_gdn_workspace_bytes(1, 3520, 16, 128)
+    nb = 55
+    floor = 16 * nb * (64 * 4 + 3 * 64 * 128 * 4 + 128 * 128 * 4)
+    assert floor <= need <= floor + 5 * 256
+    assert cwa.sa_gdn_workspace_bytes(1, 3520, 16, 96) == 0          # D must be 64 or 128
+    assert cwa.sa_gdn_workspace_bytes(0, 10, 1, 64) == 0
+    assert cwa.sa_gdn_workspace_bytes(1, 0, 1, 64) > 0                # no tokens is valid
+    assert cwa.sa_gdn_workspace_bytes(1, (1 << 24) + 1, 1, 64) == 0
+    fake = 1 << 20                                                    # never dereferenced
+    args = dict(q=fake, k=fake, v=fake, alpha=fake, beta=fake, state_in=None, state_out=fake, out=fake,
+                workspace=fake, workspace_bytes=need)
+    for kw, code in [(dict(q=None), L.SA_ERR_INVALID_ARGUMENT), (dict(out=fake + 8), L.SA_ERR_INVALID_ARGUMENT),
+                     (dict(alpha=fake + 2), L.SA_ERR_INVALID_ARGUMENT),
+                     (dict(workspace_bytes=need - 1), L.SA_ERR_WORKSPACE_TOO_SMALL)]:
+        a = dict(args, **kw)
+        with pytest.raises(cwa.SaError) as e:
+            cwa.sa_gdn_forward(1, 3520, 16, 128, a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["state_in"],
+                               a["state_out"], a["out"], a["workspace"], a["workspace_bytes"])
+        assert e.value.status == code, kw
+    with pytest.raises(cwa.SaError) as e:
+        cwa.sa_gdn_forward(1, 10, 1, 80, fake, fake, fake, fake, fake, None, fake, fake, fake, need)
+    assert e.value.status == L.SA_ERR_UNSUPPORTED

@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "attended query tokens/sec + ms/chunk; % bf16 MFMA peak (1 MI355X)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -247,6 +248,45 @@ def bench_fp8(torch, cwa, synth, name="wan1.3b", steps=30):
             "tflops": tf, "frac_of_fp8_peak": tf / PEAK_FP8_TFLOPS, "kernel": "chunk_attention_fp8_d128_pp"}
 
 
+def gdn_flops(N, H, D, B=1, C=64):
+    """Algorithmic FLOPs of the chunkwise gated delta rule per call: per 64-token block and
+    head, K K^T (C^2 D), the triangular solve (C^3 / 6), T V and T diag(gam) K (2 C^2 D),
+    U = Up - W S^T and the state update (2 C D^2), Q S^T (C D^2), Q K^T and P U (2 C^2 D);
+    two FLOPs per multiply-add."""
+    nb = -(-N // C)
+    mac = 5 * C * C * D + C ** 3 / 6 + 3 * C * D * D
+    return 2.0 * B * H * nb * mac
+
+
+def bench_gdn(torch, cwa, synth, name="hybrid1280x704", steps=20):
+    """GDN block (gated delta rule) forward over one video chunk of a workload shape with a
+    carried state: call time and FLOP rate (chunkwise count) against the fp32 vector peak."""
+    w = synth.WORKLOADS[name]
+    B, N, H, D = w.batch, w.tokens_per_chunk, w.heads, w.head_dim
+    q, k, v, a, b, s0 = synth.gdn_inputs(B, N, H, D, seed=1)
+    d16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    d32 = lambda x: torch.from_numpy(x).cuda()
+    q, k, v, a, b, state = d16(q), d16(k), d16(v), d32(a), d32(b), d32(s0)
+    out = torch.empty_like(v)
+    ws = torch.empty(cwa.sa_gdn_workspace_bytes(B, N, H, D), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        cwa.gdn_forward(q, k, v, a, b, state=state, out=out, state_out=state, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        cwa.gdn_forward(q, k, v, a, b, state=state, out=out, state_out=state, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = gdn_flops(N, H, D, B)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": name, "tokens_per_call": B * N, "heads": H, "head_dim": D, "ms_per_call": ms,
+            "tokens_per_s": B * N / (ms * 1e-3), "flops_per_call": fl, "tflops": tf,
+            "frac_of_fp32_valu_peak": tf / PEAK_FP32_VALU_TFLOPS,
+            "kernels": ["gdn_prep", "gdn_scan", "gdn_out"]}
+
+
 def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), steps=20, deadline_ms=1.0,
                 calls=200):
     """Ragged batch: n steady-state streams (each its own cache and position) attended in one
@@ -420,6 +460,7 @@ def main():
     mfma_probe = probe_mfma(torch, cwa)
     buffer_res = bench_buffer(torch, cwa, synth)
     fp8_res = bench_fp8(torch, cwa, synth)
+    gdn_res = bench_gdn(torch, cwa, synth)
     steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
     batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
 
@@ -488,6 +529,7 @@ def main():
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
         "fp8_attend": fp8_res,
+        "gdn_forward": gdn_res,
         "buffer_attend": buffer_res,
         "steps_attend": steps_res,
         "batch_attend": batch_res,

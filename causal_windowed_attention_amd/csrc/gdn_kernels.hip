@@ -11,12 +11,14 @@
 //   T  = (I + diag(beta) A)^-1 diag(beta),  A_ij = (gam_i / gam_j) k_i.k_j  (j < i)
 //   U  = T V - (T diag(gam) K) S0^T = Up - W S0^T
 //   O  = diag(gam) Q S0^T + ((Q K^T) o M) U,  M_ij = gam_i / gam_j  (j <= i)
-//   S' = gam_C S0 + U^T diag(gam_C / gam) K
+//   S' = gam_C S0 + U^T Kt,  Kt = diag(gam_C / gam) K
 // Three kernels: gdn_prep (every block independently: gates, T by forward substitution,
-// W and Up), gdn_scan (the only sequential part: the state through the blocks, in row
-// slices of S, which evolve independently; records each block's starting state and U),
-// gdn_out (every block independently: the outputs). All arithmetic is fp32 on the VALU
-// through LDS tiles; inputs and outputs are bf16, the state fp32.
+// W, Up and Kt), gdn_scan (the only sequential part: the state through the blocks, in
+// row slices of S, which evolve independently; records each block's starting state and
+// U), gdn_out (every block independently: the outputs). Arithmetic is fp32 on the VALU:
+// register tiles fed by 16-byte LDS reads from rows padded by 4 floats (aligned and
+// conflict-free), and in the scan operands prefetched from global memory into registers
+// and LDS broadcasts; inputs and outputs bf16, the state fp32.
 #include "sa_internal.h"
 
 namespace sa {
@@ -24,206 +26,322 @@ namespace {
 
 constexpr int kC = kGdnBlock;        // tokens per block
 constexpr int kThr = 256;
+constexpr int kCL = kC + 4;          // padded row of a 64-wide LDS tile
 
-__device__ __forceinline__ float bf(const __bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ float at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
-// acc[i][j] += sum_k A(r0 + i, k) * B(k, c0 + j) over k < K, with A(i, k) = a[i * ai + k * ak]
-// and B(k, j) = b[k * bk + j * bj] (LDS arrays with padded strides).
-template <int RM, int RN>
-__device__ __forceinline__ void mm_acc(float (&acc)[RM][RN], const float* a, int ai, int ak, const float* b, int bk,
-                                       int bj, int r0, int c0, int K) {
-  for (int k = 0; k < K; ++k) {
-    float av[RM], bv[RN];
+// acc[i][j] += sum_{k < K} A[r0 + i][k] * B(k, c0 + j), A row-major (a + r * lda + k).
+// BT: B(k, c) = b[c * ldb + k] (rows of b contiguous in k); else B(k, c) = b[k * ldb + c].
+// RN is a multiple of 4 when !BT; lda, ldb multiples of 4, bases 16-byte aligned.
+template <int RM, int RN, int K, bool BT>
+__device__ __forceinline__ void gemm(float (&acc)[RM][RN], const float* a, int lda, const float* b, int ldb, int r0,
+                                     int c0) {
+#pragma unroll 4
+  for (int k = 0; k < K; k += 4) {
+    float4 av[RM];
 #pragma unroll
-    for (int i = 0; i < RM; ++i) av[i] = a[(r0 + i) * ai + k * ak];
+    for (int i = 0; i < RM; ++i) av[i] = ld4(a + (r0 + i) * lda + k);
+    if constexpr (BT) {
+      float4 bv[RN];
 #pragma unroll
-    for (int j = 0; j < RN; ++j) bv[j] = b[k * bk + (c0 + j) * bj];
+      for (int j = 0; j < RN; ++j) bv[j] = ld4(b + (c0 + j) * ldb + k);
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
+      for (int i = 0; i < RM; ++i)
 #pragma unroll
-      for (int j = 0; j < RN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < RN; ++j) {
+          acc[i][j] = fmaf(av[i].x, bv[j].x, acc[i][j]);
+          acc[i][j] = fmaf(av[i].y, bv[j].y, acc[i][j]);
+          acc[i][j] = fmaf(av[i].z, bv[j].z, acc[i][j]);
+          acc[i][j] = fmaf(av[i].w, bv[j].w, acc[i][j]);
+        }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        float4 bv[RN / 4];
+#pragma unroll
+        for (int j4 = 0; j4 < RN / 4; ++j4) bv[j4] = ld4(b + (k + kk) * ldb + c0 + 4 * j4);
+#pragma unroll
+        for (int i = 0; i < RM; ++i) {
+          const float x = at(av[i], kk);
+#pragma unroll
+          for (int j4 = 0; j4 < RN / 4; ++j4) {
+            acc[i][4 * j4 + 0] = fmaf(x, bv[j4].x, acc[i][4 * j4 + 0]);
+            acc[i][4 * j4 + 1] = fmaf(x, bv[j4].y, acc[i][4 * j4 + 1]);
+            acc[i][4 * j4 + 2] = fmaf(x, bv[j4].z, acc[i][4 * j4 + 2]);
+            acc[i][4 * j4 + 3] = fmaf(x, bv[j4].w, acc[i][4 * j4 + 3]);
+          }
+        }
+      }
+    }
   }
 }
 
-// Rows [0, 64) x D of a token-major [B, N, H, D] bf16 tensor into an fp32 LDS tile
-// (stride D + 1); tokens at or past n_valid read as zeros.
+// Rows [0, 64) x D of a token-major [B, N, H, D] bf16 tensor into an fp32 LDS tile with
+// row stride ld; tokens at or past n_valid read as zeros.
 template <int D>
-__device__ __forceinline__ void load_rows(float* dst, const __bf16* src, const GdnParams& p, int b, int h, int t0,
-                                          int n_valid) {
+__device__ __forceinline__ void load_rows(float* dst, int ld, const __bf16* src, const GdnParams& p, int b, int h,
+                                          int t0, int n_valid) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
   for (int e = threadIdx.x; e < kC * D / 8; e += kThr) {
     const int i = e / (D / 8), c = (e % (D / 8)) * 8;
     bf16x8 x = {};
     if (i < n_valid)
       x = *reinterpret_cast<const bf16x8*>(src + ((static_cast<size_t>(b) * p.N + t0 + i) * p.H + h) * D + c);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) dst[i * (D + 1) + c + u] = bf(x[u]);
+    st4(dst + i * ld + c, make_float4(static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                                      static_cast<float>(x[3])));
+    st4(dst + i * ld + c + 4, make_float4(static_cast<float>(x[4]), static_cast<float>(x[5]),
+                                          static_cast<float>(x[6]), static_cast<float>(x[7])));
   }
 }
 
-// ---- gdn_prep: per block, log gates, T, W = T diag(gam) K and Up = T V -------------------
+// ---- gdn_prep: per block, log gates, T, W = T diag(gam) K, Up = T V, Kt ---------------------
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  float* Ks = sm;                                // [64][D + 1]
-  float* Vs = Ks + kC * (D + 1);                 // [64][D + 1]
-  float* L = Vs + kC * (D + 1);                  // [64][65]: beta_i A_ij (j < i)
-  float* X = L + kC * 65;                        // [64][65]: L^-1, then T
-  float* g = X + kC * 65;                        // [64] log cumulative gates
+  constexpr int LD = D + 4;
+  float* Ks = sm;                                // [64][LD]
+  float* Vs = Ks + kC * LD;                      // [64][LD]
+  float* L = Vs + kC * LD;                       // [64][kCL]: beta_i A_ij (j < i)
+  float* X = L + kC * kCL;                       // [64][kCL]: T
+  float* g = X + kC * kCL;                       // [64] log cumulative gates
   float* bet = g + kC;                           // [64]
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int t0 = blk * kC, n_valid = min(kC, p.N - t0);
   const size_t bh = static_cast<size_t>(b) * p.H + h;
+  const size_t boff = (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
 
-  load_rows<D>(Ks, static_cast<const __bf16*>(p.k), p, b, h, t0, n_valid);
-  load_rows<D>(Vs, static_cast<const __bf16*>(p.v), p, b, h, t0, n_valid);
+  load_rows<D>(Ks, LD, static_cast<const __bf16*>(p.k), p, b, h, t0, n_valid);
+  load_rows<D>(Vs, LD, static_cast<const __bf16*>(p.v), p, b, h, t0, n_valid);
   if (tid < kC) {                                // padded tokens: alpha = 1, beta = 0 (no effect)
     const bool ok = tid < n_valid;
-    g[tid] = ok ? __logf(p.alpha[bh * p.N + t0 + tid]) : 0.f;
+    float s = ok ? __logf(p.alpha[bh * p.N + t0 + tid]) : 0.f;
     bet[tid] = ok ? p.beta[bh * p.N + t0 + tid] : 0.f;
-  }
-  __syncthreads();
-  if (tid == 0) {                                // prefix sum of 64 logs
-    float s = 0.f;
-    for (int i = 0; i < kC; ++i) {
-      s += g[i];
-      g[i] = s;
+#pragma unroll
+    for (int o = 1; o < kC; o <<= 1) {           // prefix sum over the first wave
+      const float t = __shfl_up(s, o, 64);
+      if (tid >= o) s += t;
     }
+    g[tid] = s;
+    p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid] = s;
   }
   __syncthreads();
-  if (tid < kC) p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid] = g[tid];
 
-  // L_ij = beta_i exp(g_i - g_j) k_i.k_j for j < i: 64 x 64, a 4 x 4 tile per thread
+  // L_ij = beta_i exp(g_i - g_j) k_i.k_j for j < i: a 4 x 4 tile per thread
   {
     const int r0 = (tid / 16) * 4, c0 = (tid % 16) * 4;
     float acc[4][4] = {};
-    mm_acc<4, 4>(acc, Ks, D + 1, 1, Ks, 1, D + 1, r0, c0, D);
+    gemm<4, 4, D, true>(acc, Ks, LD, Ks, LD, r0, c0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = r0 + i, c = c0 + j;
-        L[r * 65 + c] = c < r ? bet[r] * __expf(g[r] - g[c]) * acc[i][j] : 0.f;
+        L[r * kCL + c] = c < r ? bet[r] * __expf(g[r] - g[c]) * acc[i][j] : 0.f;
       }
   }
   __syncthreads();
-  // X = (I + L)^-1 by forward substitution. Column j depends only on itself:
-  // X_jj = 1, X_ij = -sum_{j <= k < i} L_ik X_kj (i > j), so thread j solves column j.
+  // X = (I + L)^-1 by forward substitution. Column j depends only on itself
+  // (X_jj = 1, X_ij = -sum_{k < i} L_ik X_kj), so lane j of the first wave solves it in
+  // registers; L_ik is the same address for every lane (an LDS broadcast). T = X diag(beta).
   if (tid < kC) {
     const int j = tid;
-    for (int r = 0; r <= j; ++r) X[r * 65 + j] = r == j ? 1.f : 0.f;
-    for (int i = j + 1; i < kC; ++i) {
-      float s = 0.f;
-      for (int k = j; k < i; ++k) s = fmaf(L[i * 65 + k], X[k * 65 + j], s);
-      X[i * 65 + j] = -s;
+    float x[kC];
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int k = 0; k + 3 < i; k += 4) {
+        const float4 l = ld4(L + i * kCL + k);
+        s0 = fmaf(l.x, x[k], s0);
+        s1 = fmaf(l.y, x[k + 1], s1);
+        s2 = fmaf(l.z, x[k + 2], s2);
+        s3 = fmaf(l.w, x[k + 3], s3);
+      }
+#pragma unroll
+      for (int k = i & ~3; k < i; ++k) s0 = fmaf(L[i * kCL + k], x[k], s0);
+      x[i] = i == j ? 1.f : (i < j ? 0.f : -((s0 + s1) + (s2 + s3)));
+    }
+    const float bj = bet[j];
+#pragma unroll
+    for (int i = 0; i < kC; ++i) X[i * kCL + j] = x[i] * bj;
+  }
+  __syncthreads();
+  // Up = T V; Kt = diag(exp(g_C - g)) K; W = T diag(exp g) K: 64 x D, 4 x RN per thread
+  constexpr int RN = D / 16;
+  const int r0 = (tid / 16) * 4, c0 = (tid % 16) * RN;
+  {
+    float acc[4][RN] = {};
+    gemm<4, RN, kC, false>(acc, X, kCL, Vs, LD, r0, c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; j += 4)
+        st4(p.Up + boff + (r0 + i) * D + c0 + j, make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]));
+  }
+  const float gC = g[kC - 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {                  // this thread's Kt entries, from the unscaled K
+    const float e = __expf(gC - g[r0 + i]);
+#pragma unroll
+    for (int j = 0; j < RN; j += 4) {
+      const float4 kk = ld4(Ks + (r0 + i) * LD + c0 + j);
+      st4(p.Kt + boff + (r0 + i) * D + c0 + j, make_float4(e * kk.x, e * kk.y, e * kk.z, e * kk.w));
     }
   }
   __syncthreads();
-  // T = X diag(beta)
-  for (int e = tid; e < kC * kC; e += kThr) {
-    const int r = e / kC, c = e % kC;
-    X[r * 65 + c] *= bet[c];
-  }
-  __syncthreads();
-  // W = T diag(exp g) K and Up = T V: 64 x D each, rows r0..r0+3, columns c0..c0+RN-1
-  constexpr int RN = D / 16;
-  const int r0 = (tid / 16) * 4, c0 = (tid % 16) * RN;
-  float* W = p.W + (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
-  float* Up = p.Up + (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
-  {
-    float acc[4][RN] = {};
-    mm_acc<4, RN>(acc, X, 65, 1, Vs, D + 1, 1, r0, c0, kC);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < RN; ++j) Up[(r0 + i) * D + c0 + j] = acc[i][j];
-  }
-  __syncthreads();
-  for (int e = tid; e < kC * D; e += kThr) {     // K rows scaled by gam_j (in place)
-    const int r = e / D, c = e % D;
-    Ks[r * (D + 1) + c] *= __expf(g[r]);
+  for (int e = tid; e < kC * D / 4; e += kThr) { // K rows scaled by gam_i, in place
+    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+    const float s = __expf(g[r]);
+    const float4 kk = ld4(Ks + r * LD + c);
+    st4(Ks + r * LD + c, make_float4(s * kk.x, s * kk.y, s * kk.z, s * kk.w));
   }
   __syncthreads();
   {
     float acc[4][RN] = {};
-    mm_acc<4, RN>(acc, X, 65, 1, Ks, D + 1, 1, r0, c0, kC);
+    gemm<4, RN, kC, false>(acc, X, kCL, Ks, LD, r0, c0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < RN; ++j) W[(r0 + i) * D + c0 + j] = acc[i][j];
+      for (int j = 0; j < RN; j += 4)
+        st4(p.W + boff + (r0 + i) * D + c0 + j, make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]));
   }
 }
 
-// ---- gdn_scan: the state through the blocks, rows [r0, r0 + 16) of S per workgroup ---------
+// ---- gdn_scan: the state through the blocks, rows [rs, rs + R) of S per workgroup ----------
+// Per block: U = Up - W S^T (64 x R), then S = exp(g_C) S + U^T Kt (R x D).
+// Thread (lane l, wave w): for U, row i = l of W over the key quarter [w D/4, (w+1) D/4),
+// straight from global memory into registers (prefetched one block ahead), against state
+// rows read as LDS broadcasts; the four quarters' partial sums meet in LDS. For the update
+// it owns S[RW w + j][SC l + e] (j < RW = R / 4, e < SC = D / 64) in registers, reading U
+// as broadcasts and Kt rows from LDS.
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   constexpr int R = kGdnScanRows;
-  float* Ss = sm;                                // [R][D + 1]   state rows
-  float* Ws = Ss + R * (D + 1);                  // [64][D + 1]  W of the block
-  float* Ks = Ws + kC * (D + 1);                 // [64][D + 1]  K scaled by exp(g_C - g_i)
-  float* Us = Ks + kC * (D + 1);                 // [64][R + 1]  U rows of this slice
-  float* g = Us + kC * (R + 1);                  // [64]
+  constexpr int RW = R / 4;                      // state rows per wave
+  constexpr int LD = D + 4;
+  constexpr int RL = R + 4;
+  constexpr int KQ = D / 4;                      // key quarter per wave
+  constexpr int SC = D / 64;                     // state columns per lane
+  constexpr int NV = kC * D / 4 / kThr;          // float4 of Kt per thread
+  float* Ss = sm;                                // [R][LD]      state rows (broadcast reads)
+  float* Kts = Ss + R * LD;                      // [64][LD]     Kt of the block
+  float* part = Kts + kC * LD;                   // [4][64][RL]  per-quarter partial U
+  float* Us = part + 4 * kC * RL;                // [64][RL]     U columns of this slice
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int l = tid & 63, w = tid >> 6;
   const int rs = split * R;
   const size_t bh = static_cast<size_t>(b) * p.H + h;
+  auto boff = [&](int blk) { return (bh * p.nb + blk) * static_cast<size_t>(kC) * D; };
 
-  for (int e = tid; e < R * D; e += kThr) {
-    const int r = e / D, c = e % D;
-    Ss[r * (D + 1) + c] = p.state_in != nullptr ? p.state_in[(bh * D + rs + r) * D + c] : 0.f;
-  }
-  for (int blk = 0; blk < p.nb; ++blk) {
-    const int t0 = blk * kC, n_valid = min(kC, p.N - t0);
-    __syncthreads();                             // Ss final for this block; LDS tiles free
-    float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
-    for (int e = tid; e < R * D; e += kThr) {
-      const int r = e / D, c = e % D;
-      Sst[(rs + r) * D + c] = Ss[r * (D + 1) + c];
-    }
-    const float* W = p.W + (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
-    for (int e = tid; e < kC * D; e += kThr) Ws[(e / D) * (D + 1) + e % D] = W[e];
-    load_rows<D>(Ks, static_cast<const __bf16*>(p.k), p, b, h, t0, n_valid);
-    if (tid < kC) g[tid] = p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid];
-    __syncthreads();
-    const float gC = g[kC - 1];
-    // U[i][r] = Up[i][rs + r] - sum_d W[i][d] S[r][d]: 64 x R, 4 per thread
-    {
-      const int i = tid / (R / 4), r0 = (tid % (R / 4)) * 4;
-      float acc[1][4] = {};
-      mm_acc<1, 4>(acc, Ws, D + 1, 1, Ss, 1, D + 1, i, r0, D);
-      const float* Up = p.Up + (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
-      float* U = p.U + (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
+  float S[RW][SC];                               // S[rs + RW w + j][SC l + e]
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float u = Up[i * D + rs + r0 + j] - acc[0][j];
-        Us[i * (R + 1) + r0 + j] = u;
-        U[i * D + rs + r0 + j] = u;
+  for (int j = 0; j < RW; ++j)
+#pragma unroll
+    for (int e = 0; e < SC; ++e)
+      S[j][e] = p.state_in != nullptr ? p.state_in[(bh * D + rs + RW * w + j) * D + SC * l + e] : 0.f;
+  float4 wn[KQ / 4], kn[NV];                     // the next block's W quarter row and Kt
+  float upn[RW];                                 // and Up[l][rs + RW w + j]
+  float gn;                                      // and its log gate at the last token
+  auto fetch = [&](int blk) {
+    const float* W = p.W + boff(blk) + l * D + w * KQ;
+#pragma unroll
+    for (int u = 0; u < KQ / 4; ++u) wn[u] = ld4(W + 4 * u);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) kn[u] = ld4(p.Kt + boff(blk) + (tid + u * kThr) * 4);
+#pragma unroll
+    for (int j = 0; j < RW; ++j) upn[j] = p.Up[boff(blk) + l * D + rs + RW * w + j];
+    gn = p.g[bh * (static_cast<size_t>(p.nb) * kC) + blk * kC + kC - 1];
+  };
+  fetch(0);
+  for (int blk = 0; blk < p.nb; ++blk) {
+    __syncthreads();                             // previous update's reads are done
+    float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int e = 0; e < SC; ++e) {
+        Ss[(RW * w + j) * LD + SC * l + e] = S[j][e];
+        Sst[(rs + RW * w + j) * D + SC * l + e] = S[j][e];
+      }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = (tid + u * kThr) * 4;
+      st4(Kts + (e / D) * LD + e % D, kn[u]);
+    }
+    float4 wc[KQ / 4];
+#pragma unroll
+    for (int u = 0; u < KQ / 4; ++u) wc[u] = wn[u];
+    float up[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) up[j] = upn[j];
+    const float gC = gn;
+    __syncthreads();
+    if (blk + 1 < p.nb) fetch(blk + 1);          // in flight during this block's arithmetic
+    {                                            // partial U[l][r] over this wave's key quarter
+      float acc[R] = {};
+#pragma unroll
+      for (int u = 0; u < KQ / 4; ++u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float4 sv = ld4(Ss + r * LD + w * KQ + 4 * u);   // same address on every lane
+          acc[r] = fmaf(wc[u].x, sv.x, acc[r]);
+          acc[r] = fmaf(wc[u].y, sv.y, acc[r]);
+          acc[r] = fmaf(wc[u].z, sv.z, acc[r]);
+          acc[r] = fmaf(wc[u].w, sv.w, acc[r]);
+        }
+      }
+      float* pp = part + (w * kC + l) * RL;
+#pragma unroll
+      for (int r = 0; r < R; r += 4) st4(pp + r, make_float4(acc[r], acc[r + 1], acc[r + 2], acc[r + 3]));
+      static_assert(R % 4 == 0, "partials are stored as float4");
+    }
+    __syncthreads();
+    {                                            // U[l][RW w + j] = Up - sum of the quarters
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum += part[(q * kC + l) * RL + RW * w + j];
+        const float u = up[j] - sum;
+        Us[l * RL + RW * w + j] = u;
+        p.U[boff(blk) + l * D + rs + RW * w + j] = u;
       }
     }
-    for (int e = tid; e < kC * D; e += kThr) {   // K rows times exp(g_C - g_i)
-      const int r = e / D, c = e % D;
-      Ks[r * (D + 1) + c] *= __expf(gC - g[r]);
-    }
     __syncthreads();
-    // S[r][c] = exp(g_C) S[r][c] + sum_i U[i][r] Ks[i][c]: R x D, R*D/256 per thread
-    {
-      constexpr int CN = R * D / kThr;           // columns per thread (one row each)
-      const int r = tid / (D / CN), c0 = (tid % (D / CN)) * CN;
-      float acc[1][CN];
+    {                                            // S = exp(g_C) S + U^T Kt, this thread's RW x SC
       const float dec = __expf(gC);
 #pragma unroll
-      for (int j = 0; j < CN; ++j) acc[0][j] = dec * Ss[r * (D + 1) + c0 + j];
-      mm_acc<1, CN>(acc, Us, 1, R + 1, Ks, D + 1, 1, r, c0, kC);
-      __syncthreads();                           // every thread has read the old rows
+      for (int j = 0; j < RW; ++j)
 #pragma unroll
-      for (int j = 0; j < CN; ++j) Ss[r * (D + 1) + c0 + j] = acc[0][j];
+        for (int e = 0; e < SC; ++e) S[j][e] *= dec;
+#pragma unroll 8
+      for (int i = 0; i < kC; ++i) {
+        float uu[RW];                            // U[i][RW w ..]: the same address on every lane
+#pragma unroll
+        for (int j = 0; j < RW; ++j) uu[j] = Us[i * RL + RW * w + j];
+        float kt[SC];
+        if constexpr (SC == 2) {
+          const float2 t = *reinterpret_cast<const float2*>(Kts + i * LD + 2 * l);
+          kt[0] = t.x;
+          kt[SC - 1] = t.y;
+        } else {
+          kt[0] = Kts[i * LD + l];
+        }
+#pragma unroll
+        for (int j = 0; j < RW; ++j)
+#pragma unroll
+          for (int e = 0; e < SC; ++e) S[j][e] = fmaf(uu[j], kt[e], S[j][e]);
+      }
     }
   }
-  __syncthreads();
-  for (int e = tid; e < R * D; e += kThr) {
-    const int r = e / D, c = e % D;
-    p.state_out[(bh * D + rs + r) * D + c] = Ss[r * (D + 1) + c];
-  }
+#pragma unroll
+  for (int j = 0; j < RW; ++j)
+#pragma unroll
+    for (int e = 0; e < SC; ++e) p.state_out[(bh * D + rs + RW * w + j) * D + SC * l + e] = S[j][e];
 }
 
 // ---- gdn_out: O = diag(exp g) Q S0^T + ((Q K^T) o M) U, one half of the Dv columns --------
@@ -231,54 +349,65 @@ template <int D>
 __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   constexpr int DH = D / 2;
-  float* Qs = sm;                                // [64][D + 1]
-  float* Ks = Qs + kC * (D + 1);                 // [64][D + 1]
-  float* P = Ks + kC * (D + 1);                  // [64][65]
-  float* Ss = P + kC * 65;                       // [DH][D + 1]  block-start state rows of this half
-  float* Us = Ss + DH * (D + 1);                 // [64][DH + 1]
-  float* g = Us + kC * (DH + 1);                 // [64]
+  constexpr int LD = D + 4;
+  constexpr int HL = DH + 4;
+  float* Qs = sm;                                // [64][LD]
+  float* Ks = Qs + kC * LD;                      // [64][LD]
+  float* P = Ks + kC * LD;                       // [64][kCL]
+  float* Ss = P + kC * kCL;                      // [DH][LD]  block-start state rows of this half
+  float* Us = Ss + DH * LD;                      // [64][HL]
+  float* g = Us + kC * HL;                       // [64]
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z >> 1, half = blockIdx.z & 1, tid = threadIdx.x;
   const int t0 = blk * kC, n_valid = min(kC, p.N - t0);
   const size_t bh = static_cast<size_t>(b) * p.H + h;
+  const size_t boff = (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
 
-  load_rows<D>(Qs, static_cast<const __bf16*>(p.q), p, b, h, t0, n_valid);
-  load_rows<D>(Ks, static_cast<const __bf16*>(p.k), p, b, h, t0, n_valid);
+  load_rows<D>(Qs, LD, static_cast<const __bf16*>(p.q), p, b, h, t0, n_valid);
+  load_rows<D>(Ks, LD, static_cast<const __bf16*>(p.k), p, b, h, t0, n_valid);
   if (tid < kC) g[tid] = p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid];
   const float* S0 = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
-  for (int e = tid; e < DH * D; e += kThr) {
-    const int r = e / D, c = e % D;
-    Ss[r * (D + 1) + c] = S0[(half * DH + r) * D + c];
+  for (int e = tid; e < DH * D / 4; e += kThr) {
+    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+    st4(Ss + r * LD + c, ld4(S0 + (half * DH + r) * D + c));
   }
-  const float* U = p.U + (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
-  for (int e = tid; e < kC * DH; e += kThr) {
-    const int i = e / DH, c = e % DH;
-    Us[i * (DH + 1) + c] = U[i * D + half * DH + c];
+  for (int e = tid; e < kC * DH / 4; e += kThr) {
+    const int i = e / (DH / 4), c = (e % (DH / 4)) * 4;
+    st4(Us + i * HL + c, ld4(p.U + boff + i * D + half * DH + c));
   }
   __syncthreads();
   {                                              // P_ij = exp(g_i - g_j) q_i.k_j for j <= i
     const int r0 = (tid / 16) * 4, c0 = (tid % 16) * 4;
     float acc[4][4] = {};
-    mm_acc<4, 4>(acc, Qs, D + 1, 1, Ks, 1, D + 1, r0, c0, D);
+    gemm<4, 4, D, true>(acc, Qs, LD, Ks, LD, r0, c0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = r0 + i, c = c0 + j;
-        P[r * 65 + c] = c <= r ? __expf(g[r] - g[c]) * acc[i][j] : 0.f;
+        P[r * kCL + c] = c <= r ? __expf(g[r] - g[c]) * acc[i][j] : 0.f;
       }
   }
   __syncthreads();
   constexpr int RN = DH / 16;
   const int r0 = (tid / 16) * 4, c0 = (tid % 16) * RN;
   float acc[4][RN] = {};
-  mm_acc<4, RN>(acc, Qs, D + 1, 1, Ss, 1, D + 1, r0, c0, D);       // Q S0^T
+  gemm<4, RN, D, true>(acc, Qs, LD, Ss, LD, r0, c0);            // Q S0^T
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float e = __expf(g[r0 + i]);
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[i][j] *= e;
   }
-  mm_acc<4, RN>(acc, P, 65, 1, Us, DH + 1, 1, r0, c0, kC);          // + P U
+  if constexpr (RN % 4 == 0) {
+    gemm<4, RN, kC, false>(acc, P, kCL, Us, HL, r0, c0);       // + P U
+  } else {
+#pragma unroll 4
+    for (int j = 0; j < kC; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < RN; ++c) acc[i][c] = fmaf(P[(r0 + i) * kCL + j], Us[j * HL + c0 + c], acc[i][c]);
+  }
   __bf16* out = static_cast<__bf16*>(p.out);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -292,29 +421,35 @@ __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
 }
 
 template <int D>
-constexpr size_t prep_lds() { return (2 * kC * (D + 1) + 2 * kC * 65 + 2 * kC) * sizeof(float); }
+constexpr size_t prep_lds() { return (2 * kC * (D + 4) + 2 * kC * kCL + 2 * kC) * sizeof(float); }
 template <int D>
 constexpr size_t scan_lds() {
-  return (kGdnScanRows * (D + 1) + 2 * kC * (D + 1) + kC * (kGdnScanRows + 1) + kC) * sizeof(float);
+  return (kGdnScanRows * (D + 4) + kC * (D + 4) + 5 * kC * (kGdnScanRows + 4)) * sizeof(float);
 }
 template <int D>
 constexpr size_t out_lds() {
-  return (2 * kC * (D + 1) + kC * 65 + (D / 2) * (D + 1) + kC * (D / 2 + 1) + kC) * sizeof(float);
+  return (2 * kC * (D + 4) + kC * kCL + (D / 2) * (D + 4) + kC * (D / 2 + 4) + kC) * sizeof(float);
 }
 
 template <int D>
 hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
   static_assert(prep_lds<D>() <= 160 * 1024 && scan_lds<D>() <= 160 * 1024 && out_lds<D>() <= 160 * 1024,
                 "LDS budget");
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_prep<D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(prep_lds<D>()));
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_scan<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(scan_lds<D>()));
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_out<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(out_lds<D>()));
-  if (e != hipSuccess) return e;
+  static_assert(kGdnScanRows % 4 == 0 && D % kGdnScanRows == 0 && kC * D / 4 % kThr == 0 && D % 64 == 0,
+                "scan thread tiles");
+  static bool attrs = false;                     // dynamic LDS above 64 KB, set once per process
+  if (!attrs) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_prep<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(prep_lds<D>()));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_scan<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(scan_lds<D>()));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_out<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(out_lds<D>()));
+    if (e != hipSuccess) return e;
+    attrs = true;
+  }
   hipLaunchKernelGGL(gdn_prep<D>, dim3(p.nb, p.H, p.B), dim3(kThr), prep_lds<D>(), st, p);
   hipLaunchKernelGGL(gdn_scan<D>, dim3(D / kGdnScanRows, p.H, p.B), dim3(kThr), scan_lds<D>(), st, p);
   hipLaunchKernelGGL(gdn_out<D>, dim3(p.nb, p.H, 2 * p.B), dim3(kThr), out_lds<D>(), st, p);

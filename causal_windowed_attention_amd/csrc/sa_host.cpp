@@ -981,7 +981,7 @@ sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* 
 namespace {
 
 struct GdnLayout {
-  size_t g, W, Up, U, Sst, total;
+  size_t g, W, Up, Kt, U, Sst, total;
   int32_t nb;
 };
 
@@ -996,6 +996,7 @@ sa_status gdn_layout(int32_t B, int32_t N, int32_t H, int32_t D, GdnLayout* L) {
   L->g = off; off = align_up(off + bhb * sa::kGdnBlock * 4, kAlign);
   L->W = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
   L->Up = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
+  L->Kt = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
   L->U = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
   L->Sst = off; off = align_up(off + bhb * static_cast<size_t>(D) * D * 4, kAlign);
   L->total = off > kAlign ? off : kAlign;        // never 0: 0 means unsupported sizes
@@ -1037,6 +1038,7 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
   p.g = reinterpret_cast<float*>(ws + L.g);
   p.W = reinterpret_cast<float*>(ws + L.W);
   p.Up = reinterpret_cast<float*>(ws + L.Up);
+  p.Kt = reinterpret_cast<float*>(ws + L.Kt);
   p.U = reinterpret_cast<float*>(ws + L.U);
   p.Sst = reinterpret_cast<float*>(ws + L.Sst);
   p.B = batch; p.N = tokens; p.H = heads; p.D = head_dim; p.nb = L.nb;

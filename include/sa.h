@@ -362,7 +362,7 @@ sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* 
  * S of size D x D (value rows, key columns) per (b, h).
  *
  * sa_gdn_workspace_bytes: device workspace sa_gdn_forward needs for these sizes (0 for
- * unsupported sizes): per 64-token block of each (b, h), fp32 gates, two 64 x D
+ * unsupported sizes): per 64-token block of each (b, h), fp32 gates, three 64 x D
  * products, the pseudo-values and the block's starting state (D x D).
  *
  * sa_gdn_forward: q, k, v: [B, N, H, D] bf16 (token-major, like sa_chunk_attend's

@@ -237,6 +237,6 @@ def gdn_inputs(batch: int, tokens: int, heads: int, head_dim: int, seed: int, st
     v = to_bf16_exact(g.standard_normal(shape, dtype=np.float32))
     alpha = g.uniform(0.9, 1.0, (batch, heads, tokens)).astype(np.float32)
     beta = g.uniform(0.0, 1.0, (batch, heads, tokens)).astype(np.float32)
-    s0 = (g.standard_normal((batch, heads, head_dim, head_dim), dtype=np.float32) / np.sqrt(head_dim)
-          if state else None)
+    s0 = ((g.standard_normal((batch, heads, head_dim, head_dim), dtype=np.float32)
+           / np.float32(np.sqrt(head_dim))).astype(np.float32) if state else None)
     return q, k, v, alpha, beta, s0

@@ -440,8 +440,8 @@ def test_gdn_sizes_and_errors():
     """The GDN entry points validate on the host before any device work."""
     need = cwa.sa_gdn_workspace_bytes(1, 3520, 16, 128)
     nb = 55
-    floor = 16 * nb * (64 * 4 + 3 * 64 * 128 * 4 + 128 * 128 * 4)
-    assert floor <= need <= floor + 5 * 256
+    floor = 16 * nb * (64 * 4 + 4 * 64 * 128 * 4 + 128 * 128 * 4)
+    assert floor <= need <= floor + 6 * 256
     assert cwa.sa_gdn_workspace_bytes(1, 3520, 16, 96) == 0          # D must be 64 or 128
     assert cwa.sa_gdn_workspace_bytes(0, 10, 1, 64) == 0
     assert cwa.sa_gdn_workspace_bytes(1, 0, 1, 64) > 0                # no tokens is valid

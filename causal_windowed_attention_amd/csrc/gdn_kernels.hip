@@ -15,10 +15,11 @@
 // Three kernels: gdn_prep (every block independently: gates, T by forward substitution,
 // W, Up and Kt), gdn_scan (the only sequential part: the state through the blocks, in
 // row slices of S, which evolve independently; records each block's starting state and
-// U), gdn_out (every block independently: the outputs). Arithmetic is fp32 on the VALU:
-// register tiles fed by 16-byte LDS reads from rows padded by 4 floats (aligned and
-// conflict-free), and in the scan operands prefetched from global memory into registers
-// and LDS broadcasts; inputs and outputs bf16, the state fp32.
+// U), gdn_out (every block independently: the outputs). Arithmetic is fp32: register
+// tiles on the VALU fed by 16-byte LDS reads (rows padded by 4 floats: aligned and
+// conflict-free) in gdn_prep and gdn_out; the scan's two products on the fp32 MFMA with
+// operands prefetched from global memory into registers. Inputs and outputs are bf16,
+// the state fp32.
 #include "sa_internal.h"
 
 namespace sa {
@@ -95,6 +96,16 @@ __device__ __forceinline__ void load_rows(float* dst, int ld, const __bf16* src,
     st4(dst + i * ld + c + 4, make_float4(static_cast<float>(x[4]), static_cast<float>(x[5]),
                                           static_cast<float>(x[6]), static_cast<float>(x[7])));
   }
+}
+
+// Storage order of W and Kt within a block, chosen for the scan's MFMA B operands:
+// W[i][k] at i * D + (k % 4) * (D / 4) + k / 4 (lane (i % 16, q = k % 4) reads its k-steps
+// contiguously); Kt[i][c] at ((c / 16) * 64 + 16 (i % 4) + c % 16) * 16 + i / 4 (lane
+// 16 (i % 4) + c % 16 of column tile c / 16 reads its 16 token steps contiguously).
+template <int D>
+__device__ __forceinline__ int wperm_index(int i, int k) { return i * D + (k & 3) * (D / 4) + (k >> 2); }
+__device__ __forceinline__ int ktperm_index(int i, int c) {
+  return ((c >> 4) * 64 + 16 * (i & 3) + (c & 15)) * 16 + (i >> 2);
 }
 
 // ---- gdn_prep: per block, log gates, T, W = T diag(gam) K, Up = T V, Kt ---------------------
@@ -186,10 +197,8 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
   for (int i = 0; i < 4; ++i) {                  // this thread's Kt entries, from the unscaled K
     const float e = __expf(gC - g[r0 + i]);
 #pragma unroll
-    for (int j = 0; j < RN; j += 4) {
-      const float4 kk = ld4(Ks + (r0 + i) * LD + c0 + j);
-      st4(p.Kt + boff + (r0 + i) * D + c0 + j, make_float4(e * kk.x, e * kk.y, e * kk.z, e * kk.w));
-    }
+    for (int j = 0; j < RN; ++j)
+      p.Kt[boff + ktperm_index(r0 + i, c0 + j)] = e * Ks[(r0 + i) * LD + c0 + j];
   }
   __syncthreads();
   for (int e = tid; e < kC * D / 4; e += kThr) { // K rows scaled by gam_i, in place
@@ -205,143 +214,119 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < RN; j += 4)
-        st4(p.W + boff + (r0 + i) * D + c0 + j, make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]));
+      for (int j = 0; j < RN; ++j) p.W[boff + wperm_index<D>(r0 + i, c0 + j)] = acc[i][j];
   }
 }
 
-// ---- gdn_scan: the state through the blocks, rows [rs, rs + R) of S per workgroup ----------
-// Per block: U = Up - W S^T (64 x R), then S = exp(g_C) S + U^T Kt (R x D).
-// Thread (lane l, wave w): for U, row i = l of W over the key quarter [w D/4, (w+1) D/4),
-// straight from global memory into registers (prefetched one block ahead), against state
-// rows read as LDS broadcasts; the four quarters' partial sums meet in LDS. For the update
-// it owns S[RW w + j][SC l + e] (j < RW = R / 4, e < SC = D / 64) in registers, reading U
-// as broadcasts and Kt rows from LDS.
+// ---- gdn_scan: the state through the blocks, rows [rs, rs + 16) of S per workgroup ----------
+// Per block, on the fp32 MFMA (v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16] and receives C[4 (l / 16) + j][l % 16]):
+//   U^T (16 x 64) = S (16 x D) W^T: wave w takes tokens [16 w, 16 w + 16), all of D;
+//   S' (16 x D) = exp(g_C) S + U^T (16 x 64) Kt (64 x D): wave w takes NT column tiles.
+// The state lives in registers in the C layout; U and S cross between waves through LDS
+// (read back in the A layout). gdn_prep stores W and Kt in the lane order of the B
+// operands (wperm_index, ktperm_index), so each lane prefetches contiguous float4s for
+// the next block while the current one computes.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  constexpr int R = kGdnScanRows;
-  constexpr int RW = R / 4;                      // state rows per wave
+  static_assert(kGdnScanRows == 16, "one 16-row MFMA tile of the state per workgroup");
   constexpr int LD = D + 4;
-  constexpr int RL = R + 4;
-  constexpr int KQ = D / 4;                      // key quarter per wave
-  constexpr int SC = D / 64;                     // state columns per lane
-  constexpr int NV = kC * D / 4 / kThr;          // float4 of Kt per thread
-  float* Ss = sm;                                // [R][LD]      state rows (broadcast reads)
-  float* Kts = Ss + R * LD;                      // [64][LD]     Kt of the block
-  float* part = Kts + kC * LD;                   // [4][64][RL]  per-quarter partial U
-  float* Us = part + 4 * kC * RL;                // [64][RL]     U columns of this slice
+  constexpr int KS = D / 4;                      // k-steps of the U product
+  constexpr int NT = D / 64;                     // 16-column tiles of the state per wave
+  float* Sx = sm;                                // [16][LD]  state exchange
+  float* Ux = Sx + 16 * LD;                      // [64][16]  U exchange
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int l = tid & 63, w = tid >> 6;
-  const int rs = split * R;
+  const int l = tid & 63, w = tid >> 6, lr = l & 15, lq = l >> 4;
+  const int rs = split * 16;
   const size_t bh = static_cast<size_t>(b) * p.H + h;
   auto boff = [&](int blk) { return (bh * p.nb + blk) * static_cast<size_t>(kC) * D; };
 
-  float S[RW][SC];                               // S[rs + RW w + j][SC l + e]
+  f32x4 sc[NT];                                  // S[4 lq + j][16 (NT w + t) + lr]
 #pragma unroll
-  for (int j = 0; j < RW; ++j)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int e = 0; e < SC; ++e)
-      S[j][e] = p.state_in != nullptr ? p.state_in[(bh * D + rs + RW * w + j) * D + SC * l + e] : 0.f;
-  float4 wn[KQ / 4], kn[NV];                     // the next block's W quarter row and Kt
-  float upn[RW];                                 // and Up[l][rs + RW w + j]
-  float gn;                                      // and its log gate at the last token
-  auto fetch = [&](int blk) {
-    const float* W = p.W + boff(blk) + l * D + w * KQ;
+    for (int j = 0; j < 4; ++j)
+      sc[t][j] = p.state_in != nullptr ? p.state_in[(bh * D + rs + 4 * lq + j) * D + 16 * (NT * w + t) + lr] : 0.f;
+  float wv[KS], kv[NT][16];                      // B operands: W^T and Kt of the block
+  float4 up;                                     // Up[16 w + lr][rs + 4 lq ..]
+  float gC;
+  auto fetch_w = [&](int blk) {
+    const float* src = p.W + boff(blk) + (16 * w + lr) * D + lq * KS;
 #pragma unroll
-    for (int u = 0; u < KQ / 4; ++u) wn[u] = ld4(W + 4 * u);
-#pragma unroll
-    for (int u = 0; u < NV; ++u) kn[u] = ld4(p.Kt + boff(blk) + (tid + u * kThr) * 4);
-#pragma unroll
-    for (int j = 0; j < RW; ++j) upn[j] = p.Up[boff(blk) + l * D + rs + RW * w + j];
-    gn = p.g[bh * (static_cast<size_t>(p.nb) * kC) + blk * kC + kC - 1];
+    for (int u = 0; u < KS / 4; ++u) {
+      const float4 t = ld4(src + 4 * u);
+      wv[4 * u] = t.x; wv[4 * u + 1] = t.y; wv[4 * u + 2] = t.z; wv[4 * u + 3] = t.w;
+    }
   };
-  fetch(0);
+  auto fetch_rest = [&](int blk) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float* src = p.Kt + boff(blk) + ((NT * w + t) * 64 + l) * 16;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = ld4(src + 4 * u);
+        kv[t][4 * u] = v.x; kv[t][4 * u + 1] = v.y; kv[t][4 * u + 2] = v.z; kv[t][4 * u + 3] = v.w;
+      }
+    }
+    up = ld4(p.Up + boff(blk) + (16 * w + lr) * D + rs + 4 * lq);
+    gC = p.g[bh * (static_cast<size_t>(p.nb) * kC) + blk * kC + kC - 1];
+  };
+  // state -> A layout (lane l: S[lr][4 s + lq]) through LDS
+  float sa[KS];
+  auto exchange_state = [&] {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Sx[(4 * lq + j) * LD + 16 * (NT * w + t) + lr] = sc[t][j];
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sa[s] = Sx[lr * LD + 4 * s + lq];
+  };
+  fetch_w(0);
+  fetch_rest(0);
+  exchange_state();
   for (int blk = 0; blk < p.nb; ++blk) {
-    __syncthreads();                             // previous update's reads are done
     float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
 #pragma unroll
-    for (int j = 0; j < RW; ++j)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int e = 0; e < SC; ++e) {
-        Ss[(RW * w + j) * LD + SC * l + e] = S[j][e];
-        Sst[(rs + RW * w + j) * D + SC * l + e] = S[j][e];
-      }
+      for (int j = 0; j < 4; ++j) Sst[(rs + 4 * lq + j) * D + 16 * (NT * w + t) + lr] = sc[t][j];
+    // U^T tile of tokens [16 w, 16 w + 16): two accumulators over the k-steps
+    f32x4 a0 = {}, a1 = {};
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = (tid + u * kThr) * 4;
-      st4(Kts + (e / D) * LD + e % D, kn[u]);
+    for (int s = 0; s < KS; s += 2) {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[s], wv[s], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[s + 1], wv[s + 1], a1, 0, 0, 0);
     }
-    float4 wc[KQ / 4];
-#pragma unroll
-    for (int u = 0; u < KQ / 4; ++u) wc[u] = wn[u];
-    float up[RW];
-#pragma unroll
-    for (int j = 0; j < RW; ++j) up[j] = upn[j];
-    const float gC = gn;
+    if (blk + 1 < p.nb) fetch_w(blk + 1);
+    // U[16 w + lr][4 lq + j] = Up - (S W^T)^T
+    const float4 u4 = make_float4(up.x - (a0[0] + a1[0]), up.y - (a0[1] + a1[1]), up.z - (a0[2] + a1[2]),
+                                  up.w - (a0[3] + a1[3]));
+    st4(p.U + boff(blk) + (16 * w + lr) * D + rs + 4 * lq, u4);
+    st4(Ux + (16 * w + lr) * 16 + 4 * lq, u4);
     __syncthreads();
-    if (blk + 1 < p.nb) fetch(blk + 1);          // in flight during this block's arithmetic
-    {                                            // partial U[l][r] over this wave's key quarter
-      float acc[R] = {};
+    float ua[16];                                // A layout of U^T: U[4 s + lq][lr]
 #pragma unroll
-      for (int u = 0; u < KQ / 4; ++u) {
+    for (int s = 0; s < 16; ++s) ua[s] = Ux[(4 * s + lq) * 16 + lr];
+    const float dec = __expf(gC);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float4 sv = ld4(Ss + r * LD + w * KQ + 4 * u);   // same address on every lane
-          acc[r] = fmaf(wc[u].x, sv.x, acc[r]);
-          acc[r] = fmaf(wc[u].y, sv.y, acc[r]);
-          acc[r] = fmaf(wc[u].z, sv.z, acc[r]);
-          acc[r] = fmaf(wc[u].w, sv.w, acc[r]);
-        }
-      }
-      float* pp = part + (w * kC + l) * RL;
+    for (int t = 0; t < NT; ++t) {
+      f32x4 acc = sc[t] * dec;
 #pragma unroll
-      for (int r = 0; r < R; r += 4) st4(pp + r, make_float4(acc[r], acc[r + 1], acc[r + 2], acc[r + 3]));
-      static_assert(R % 4 == 0, "partials are stored as float4");
+      for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s], kv[t][s], acc, 0, 0, 0);
+      sc[t] = acc;
     }
-    __syncthreads();
-    {                                            // U[l][RW w + j] = Up - sum of the quarters
-#pragma unroll
-      for (int j = 0; j < RW; ++j) {
-        float sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sum += part[(q * kC + l) * RL + RW * w + j];
-        const float u = up[j] - sum;
-        Us[l * RL + RW * w + j] = u;
-        p.U[boff(blk) + l * D + rs + RW * w + j] = u;
-      }
-    }
-    __syncthreads();
-    {                                            // S = exp(g_C) S + U^T Kt, this thread's RW x SC
-      const float dec = __expf(gC);
-#pragma unroll
-      for (int j = 0; j < RW; ++j)
-#pragma unroll
-        for (int e = 0; e < SC; ++e) S[j][e] *= dec;
-#pragma unroll 8
-      for (int i = 0; i < kC; ++i) {
-        float uu[RW];                            // U[i][RW w ..]: the same address on every lane
-#pragma unroll
-        for (int j = 0; j < RW; ++j) uu[j] = Us[i * RL + RW * w + j];
-        float kt[SC];
-        if constexpr (SC == 2) {
-          const float2 t = *reinterpret_cast<const float2*>(Kts + i * LD + 2 * l);
-          kt[0] = t.x;
-          kt[SC - 1] = t.y;
-        } else {
-          kt[0] = Kts[i * LD + l];
-        }
-#pragma unroll
-        for (int j = 0; j < RW; ++j)
-#pragma unroll
-          for (int e = 0; e < SC; ++e) S[j][e] = fmaf(uu[j], kt[e], S[j][e]);
-      }
-    }
+    if (blk + 1 < p.nb) fetch_rest(blk + 1);
+    exchange_state();                            // also orders this block's Ux reads before the next writes
   }
 #pragma unroll
-  for (int j = 0; j < RW; ++j)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int e = 0; e < SC; ++e) p.state_out[(bh * D + rs + RW * w + j) * D + SC * l + e] = S[j][e];
+    for (int j = 0; j < 4; ++j)
+      p.state_out[(bh * D + rs + 4 * lq + j) * D + 16 * (NT * w + t) + lr] = sc[t][j];
 }
 
 // ---- gdn_out: O = diag(exp g) Q S0^T + ((Q K^T) o M) U, one half of the Dv columns --------
@@ -423,9 +408,7 @@ __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
 template <int D>
 constexpr size_t prep_lds() { return (2 * kC * (D + 4) + 2 * kC * kCL + 2 * kC) * sizeof(float); }
 template <int D>
-constexpr size_t scan_lds() {
-  return (kGdnScanRows * (D + 4) + kC * (D + 4) + 5 * kC * (kGdnScanRows + 4)) * sizeof(float);
-}
+constexpr size_t scan_lds() { return (16 * (D + 4) + kC * 16) * sizeof(float); }
 template <int D>
 constexpr size_t out_lds() {
   return (2 * kC * (D + 4) + kC * kCL + (D / 2) * (D + 4) + kC * (D / 2 + 4) + kC) * sizeof(float);
@@ -435,8 +418,7 @@ template <int D>
 hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
   static_assert(prep_lds<D>() <= 160 * 1024 && scan_lds<D>() <= 160 * 1024 && out_lds<D>() <= 160 * 1024,
                 "LDS budget");
-  static_assert(kGdnScanRows % 4 == 0 && D % kGdnScanRows == 0 && kC * D / 4 % kThr == 0 && D % 64 == 0,
-                "scan thread tiles");
+  static_assert(D % 64 == 0, "scan tiles");
   static bool attrs = false;                     // dynamic LDS above 64 KB, set once per process
   if (!attrs) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_prep<D>),

@@ -110,10 +110,7 @@ constexpr int kMaxSkGroups = 512;
 // Gated delta rule (GDN) forward, chunkwise: tokens in blocks of kGdnBlock; the state scan
 // runs kGdnScanRows rows of each (b, h) state per workgroup.
 constexpr int kGdnBlock = 64;
-#ifndef SA_GDN_SCAN_ROWS
-#define SA_GDN_SCAN_ROWS 16
-#endif
-constexpr int kGdnScanRows = SA_GDN_SCAN_ROWS;
+constexpr int kGdnScanRows = 16;
 
 struct GdnParams {
   const void* q;          // [B, N, H, D] bf16
@@ -126,9 +123,9 @@ struct GdnParams {
   void* out;              // [B, N, H, D] bf16
   // workspace (nb = ceil(N / kGdnBlock) blocks per (b, h))
   float* g;               // [B*H][nb*64] log of the cumulative gate within each block
-  float* W;               // [B*H][nb][64][D] T diag(gam) K
+  float* W;               // [B*H][nb][64 * D] T diag(gam) K (in the scan's operand order)
   float* Up;              // [B*H][nb][64][D] T V
-  float* Kt;              // [B*H][nb][64][D] K rows times gam_C / gam_i
+  float* Kt;              // [B*H][nb][64 * D] K rows times gam_C / gam_i (scan operand order)
   float* U;               // [B*H][nb][64][D] pseudo-values
   float* Sst;             // [B*H][nb][D][D] state at each block start
   int32_t B, N, H, D, nb;

@@ -287,6 +287,58 @@ def bench_gdn(torch, cwa, synth, name="hybrid1280x704", steps=20):
             "kernels": ["gdn_prep", "gdn_scan", "gdn_out"]}
 
 
+BF16_CONFIGS = ("wan1.3b", "wan14b_b1", "wan14b_b2", "wan14b_b4", "hybrid1280x704", "long512p")
+
+
+def bench_configs(torch, cwa, synth, steps=20):
+    """Every bf16 workload shape at steady state (a full sink and window): the step (attend +
+    commit) per chunk as p50 / p99 of per-step events, the attention kernel's time and its
+    algorithmic FLOP rate (visible keys only), and misses against the per-chunk budgets of
+    24 and 16 frames/s. A pool of two distinct chunks cycles through the stream."""
+    res = {}
+    for name in BF16_CONFIGS:
+        w = synth.WORKLOADS[name]
+        cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
+                              w.sink_chunks, w.window_chunks, dtype="bf16")
+        s = cwa.Stream(cfg, device="cuda")
+        pool = [tuple(torch.from_numpy(x).to(torch.bfloat16).cuda() for x in synth.chunk_qkv(w, 300 + i))
+                for i in range(2)]
+        out = torch.empty_like(pool[0][0])
+
+        def step(i):
+            q, k, v = pool[i % 2]
+            s.chunk_attend(q, k, v, out=out)
+            s.kv_append(k, v)
+        for i in range(w.sink_chunks + w.window_chunks + 3):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            step(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        s.set_option(cwa.SA_OPT_PROFILE, 1)
+        s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+        for i in range(steps):
+            step(i)
+        attn_ms, na = s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+        keys = s.query()["visible_keys"]
+        s.close()
+        attn_ms /= max(na, 1)
+        nc = w.tokens_per_chunk
+        flops = 4.0 * w.batch * w.heads * w.head_dim * nc * keys
+        tf = flops / (attn_ms * 1e-3) / 1e12
+        budgets = {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)}
+        res[name] = {"batch": w.batch, "heads": w.heads, "tokens_per_chunk": nc, "visible_keys": keys,
+                     "step_ms_p50": t[len(t) // 2], "step_ms_p99": t[min(len(t) - 1, int(round(0.99 * (len(t) - 1))))],
+                     "attention_ms": attn_ms, "tokens_per_s": w.batch * nc / (t[len(t) // 2] * 1e-3),
+                     "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+                     "deadline_misses": {fps: sum(x > b for x in t) for fps, b in budgets.items()}}
+    return res
+
+
 def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), steps=20, deadline_ms=1.0,
                 calls=200):
     """Ragged batch: n steady-state streams (each its own cache and position) attended in one
@@ -461,6 +513,7 @@ def main():
     buffer_res = bench_buffer(torch, cwa, synth)
     fp8_res = bench_fp8(torch, cwa, synth)
     gdn_res = bench_gdn(torch, cwa, synth)
+    configs_res = bench_configs(torch, cwa, synth)
     steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
     batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
 
@@ -528,6 +581,7 @@ def main():
         "chunk_budget_ms": {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)},
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
+        "configs": configs_res,
         "fp8_attend": fp8_res,
         "gdn_forward": gdn_res,
         "buffer_attend": buffer_res,

@@ -305,7 +305,10 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
     // U[16 w + lr][4 lq + j] = Up - (S W^T)^T
     const float4 u4 = make_float4(up.x - (a0[0] + a1[0]), up.y - (a0[1] + a1[1]), up.z - (a0[2] + a1[2]),
                                   up.w - (a0[3] + a1[3]));
-    st4(p.U + boff(blk) + (16 * w + lr) * D + rs + 4 * lq, u4);
+    {                                            // U^T[c][token] for gdn_out
+      float* ut = p.U + boff(blk) + static_cast<size_t>(rs + 4 * lq) * kC + 16 * w + lr;
+      ut[0] = u4.x; ut[kC] = u4.y; ut[2 * kC] = u4.z; ut[3 * kC] = u4.w;
+    }
     st4(Ux + (16 * w + lr) * 16 + 4 * lq, u4);
     __syncthreads();
     float ua[16];                                // A layout of U^T: U[4 s + lq][lr]
@@ -329,79 +332,128 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
       p.state_out[(bh * D + rs + 4 * lq + j) * D + 16 * (NT * w + t) + lr] = sc[t][j];
 }
 
-// ---- gdn_out: O = diag(exp g) Q S0^T + ((Q K^T) o M) U, one half of the Dv columns --------
+// ---- gdn_out: the outputs of one block, transposed -------------------------------------
+//   O^T = S0 Q^T diag(gam) + U^T P^T,   P^T_ji = exp(g_i - g_j) k_j.q_i  (j <= i)
+// on v_mfma_f32_32x32x16_bf16 (lane l supplies A[l % 32][8 (l / 32) + e] and
+// B[8 (l / 32) + e][l % 32], e < 8, and receives C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]).
+// Q and K are bf16, so P^T = K Q^T has exact products; the fp32 operands S0, U^T and P^T
+// enter as bf16 pairs x = hi + lo (|x - hi - lo| <= 2^-16 |x|), S0 Q^T in two products and
+// U^T P^T in three (the lo * lo term, below 2^-16 of each product, is dropped). P^T leaves
+// its accumulator as the B operand in registers: the accumulator's row order within a
+// 16-row step is the token order tau(e) = 8 (e / 4) + 4 (l / 32) + e % 4, so the U^T operand
+// is read in that order (two 4-token runs per lane). Wave w takes query tile w % 2 and
+// Dv tiles [CTW (w / 2), CTW (w / 2) + CTW) of 32 rows; every operand comes straight from
+// global memory (L2), only the gates go through LDS.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 t = static_cast<__bf16>(x[e]);
+    hi[e] = t;
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(t));
+  }
+}
+__device__ __forceinline__ void unpack8(const float4& a, const float4& b, float (&x)[8]) {
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
-  extern __shared__ __attribute__((aligned(16))) float sm[];
-  constexpr int DH = D / 2;
-  constexpr int LD = D + 4;
-  constexpr int HL = DH + 4;
-  float* Qs = sm;                                // [64][LD]
-  float* Ks = Qs + kC * LD;                      // [64][LD]
-  float* P = Ks + kC * LD;                       // [64][kCL]
-  float* Ss = P + kC * kCL;                      // [DH][LD]  block-start state rows of this half
-  float* Us = Ss + DH * LD;                      // [64][HL]
-  float* g = Us + kC * HL;                       // [64]
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z >> 1, half = blockIdx.z & 1, tid = threadIdx.x;
+  __shared__ float gs[kC];
+  constexpr int KS = D / 16;                     // k-steps over D
+  constexpr int CTW = D / 64;                    // Dv tiles per wave
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int l = tid & 63, w = tid >> 6, lc = l & 31, hf = l >> 5;
+  const int it = w & 1;
   const int t0 = blk * kC, n_valid = min(kC, p.N - t0);
   const size_t bh = static_cast<size_t>(b) * p.H + h;
+  const size_t rs = static_cast<size_t>(p.H) * D;                  // token stride of q, k, out
+  const size_t base = (static_cast<size_t>(b) * p.N + t0) * rs + static_cast<size_t>(h) * D;
+  const __bf16* qb = static_cast<const __bf16*>(p.q) + base;
+  const __bf16* kb = static_cast<const __bf16*>(p.k) + base;
   const size_t boff = (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
-
-  load_rows<D>(Qs, LD, static_cast<const __bf16*>(p.q), p, b, h, t0, n_valid);
-  load_rows<D>(Ks, LD, static_cast<const __bf16*>(p.k), p, b, h, t0, n_valid);
-  if (tid < kC) g[tid] = p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid];
   const float* S0 = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
-  for (int e = tid; e < DH * D / 4; e += kThr) {
-    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-    st4(Ss + r * LD + c, ld4(S0 + (half * DH + r) * D + c));
-  }
-  for (int e = tid; e < kC * DH / 4; e += kThr) {
-    const int i = e / (DH / 4), c = (e % (DH / 4)) * 4;
-    st4(Us + i * HL + c, ld4(p.U + boff + i * D + half * DH + c));
+  const float* Ut = p.U + boff;                                     // U^T: [D][64]
+  if (tid < kC) gs[tid] = p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid];
+
+  const int qi = 32 * it + lc;                                      // this lane's query (column)
+  bf16x8 bq[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    bq[s] = qi < n_valid ? *reinterpret_cast<const bf16x8*>(qb + qi * rs + 16 * s + 8 * hf) : bf16x8{};
+  f32x16 pt[2] = {};
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    if (jt > it) break;
+    const int kj = 32 * jt + lc;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 ak = kj < n_valid ? *reinterpret_cast<const bf16x8*>(kb + kj * rs + 16 * s + 8 * hf) : bf16x8{};
+      pt[jt] = mfma_bf16(ak, bq[s], pt[jt]);
+    }
   }
   __syncthreads();
-  {                                              // P_ij = exp(g_i - g_j) q_i.k_j for j <= i
-    const int r0 = (tid / 16) * 4, c0 = (tid % 16) * 4;
-    float acc[4][4] = {};
-    gemm<4, 4, D, true>(acc, Qs, LD, Ks, LD, r0, c0);
+  const float gi = gs[qi];
+  bf16x8 pbh[2][2], pbl[2][2];                                      // [j tile][16-token step]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r0 + i, c = c0 + j;
-        P[r * kCL + c] = c <= r ? __expf(g[r] - g[c]) * acc[i][j] : 0.f;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * jt + 16 * s2 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        x[e] = (jt <= it && j <= qi) ? __expf(gi - gs[j]) * pt[jt][8 * s2 + e] : 0.f;
       }
-  }
-  __syncthreads();
-  constexpr int RN = DH / 16;
-  const int r0 = (tid / 16) * 4, c0 = (tid % 16) * RN;
-  float acc[4][RN] = {};
-  gemm<4, RN, D, true>(acc, Qs, LD, Ss, LD, r0, c0);            // Q S0^T
+      split_bf16(x, pbh[jt][s2], pbl[jt][s2]);
+    }
+  const float eg = __expf(gi);
+  __bf16* ob = static_cast<__bf16*>(p.out) + base;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float e = __expf(g[r0 + i]);
+  for (int u = 0; u < CTW; ++u) {
+    const int c = 32 * ((w >> 1) * CTW + u) + lc;                  // this lane's Dv row of O^T
+    f32x16 o = {};
 #pragma unroll
-    for (int j = 0; j < RN; ++j) acc[i][j] *= e;
-  }
-  if constexpr (RN % 4 == 0) {
-    gemm<4, RN, kC, false>(acc, P, kCL, Us, HL, r0, c0);       // + P U
-  } else {
-#pragma unroll 4
-    for (int j = 0; j < kC; ++j)
+    for (int s = 0; s < KS; ++s) {
+      const float* src = S0 + static_cast<size_t>(c) * D + 16 * s + 8 * hf;
+      float x[8];
+      unpack8(ld4(src), ld4(src + 4), x);
+      bf16x8 ah, al;
+      split_bf16(x, ah, al);
+      o = mfma_bf16(ah, bq[s], o);
+      o = mfma_bf16(al, bq[s], o);
+    }
+    o *= eg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int jt = 0; jt < 2; ++jt) {
+      if (jt > it) break;
 #pragma unroll
-        for (int c = 0; c < RN; ++c) acc[i][c] = fmaf(P[(r0 + i) * kCL + j], Us[j * HL + c0 + c], acc[i][c]);
-  }
-  __bf16* out = static_cast<__bf16*>(p.out);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const float* src = Ut + c * kC + 32 * jt + 16 * s2 + 4 * hf;
+        float x[8];
+        unpack8(ld4(src), ld4(src + 8), x);
+        bf16x8 ah, al;
+        split_bf16(x, ah, al);
+        o = mfma_bf16(ah, pbh[jt][s2], o);
+        o = mfma_bf16(al, pbh[jt][s2], o);
+        o = mfma_bf16(ah, pbl[jt][s2], o);
+      }
+    }
+    if (qi < n_valid) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + i;
-    if (r >= n_valid) continue;
-#pragma unroll
-    for (int j = 0; j < RN; ++j)
-      out[((static_cast<size_t>(b) * p.N + t0 + r) * p.H + h) * D + half * DH + c0 + j] =
-          static_cast<__bf16>(acc[i][j]);
+      for (int q = 0; q < 4; ++q) {
+        const int cr = 32 * ((w >> 1) * CTW + u) + 8 * q + 4 * hf;
+        const bf16x4 v = {static_cast<__bf16>(o[4 * q]), static_cast<__bf16>(o[4 * q + 1]),
+                          static_cast<__bf16>(o[4 * q + 2]), static_cast<__bf16>(o[4 * q + 3])};
+        *reinterpret_cast<bf16x4*>(ob + qi * rs + cr) = v;
+      }
+    }
   }
 }
 
@@ -409,14 +461,10 @@ template <int D>
 constexpr size_t prep_lds() { return (2 * kC * (D + 4) + 2 * kC * kCL + 2 * kC) * sizeof(float); }
 template <int D>
 constexpr size_t scan_lds() { return (16 * (D + 4) + kC * 16) * sizeof(float); }
-template <int D>
-constexpr size_t out_lds() {
-  return (2 * kC * (D + 4) + kC * kCL + (D / 2) * (D + 4) + kC * (D / 2 + 4) + kC) * sizeof(float);
-}
 
 template <int D>
 hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
-  static_assert(prep_lds<D>() <= 160 * 1024 && scan_lds<D>() <= 160 * 1024 && out_lds<D>() <= 160 * 1024,
+  static_assert(prep_lds<D>() <= 160 * 1024 && scan_lds<D>() <= 160 * 1024,
                 "LDS budget");
   static_assert(D % 64 == 0, "scan tiles");
   static bool attrs = false;                     // dynamic LDS above 64 KB, set once per process
@@ -426,15 +474,12 @@ hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
     if (e == hipSuccess)
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_scan<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(scan_lds<D>()));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_out<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(out_lds<D>()));
     if (e != hipSuccess) return e;
     attrs = true;
   }
   hipLaunchKernelGGL(gdn_prep<D>, dim3(p.nb, p.H, p.B), dim3(kThr), prep_lds<D>(), st, p);
   hipLaunchKernelGGL(gdn_scan<D>, dim3(D / kGdnScanRows, p.H, p.B), dim3(kThr), scan_lds<D>(), st, p);
-  hipLaunchKernelGGL(gdn_out<D>, dim3(p.nb, p.H, 2 * p.B), dim3(kThr), out_lds<D>(), st, p);
+  hipLaunchKernelGGL(gdn_out<D>, dim3(p.nb, p.H, p.B), dim3(kThr), 0, st, p);
   return hipGetLastError();
 }
 

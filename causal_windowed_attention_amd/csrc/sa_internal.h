@@ -126,7 +126,7 @@ struct GdnParams {
   float* W;               // [B*H][nb][64 * D] T diag(gam) K (in the scan's operand order)
   float* Up;              // [B*H][nb][64][D] T V
   float* Kt;              // [B*H][nb][64 * D] K rows times gam_C / gam_i (scan operand order)
-  float* U;               // [B*H][nb][64][D] pseudo-values
+  float* U;               // [B*H][nb][D][64] pseudo-values, transposed (U^T)
   float* Sst;             // [B*H][nb][D][D] state at each block start
   int32_t B, N, H, D, nb;
 };

@@ -123,9 +123,9 @@ struct GdnParams {
   void* out;              // [B, N, H, D] bf16
   // workspace (nb = ceil(N / kGdnBlock) blocks per (b, h))
   float* g;               // [B*H][nb*64] log of the cumulative gate within each block
-  float* W;               // [B*H][nb][64 * D] T diag(gam) K (in the scan's operand order)
-  float* Up;              // [B*H][nb][64][D] T V
-  float* Kt;              // [B*H][nb][64 * D] K rows times gam_C / gam_i (scan operand order)
+  float* W;               // [B*H][nb][64 * D] T diag(gam) K (in the scan's load order)
+  float* Up;              // [B*H][nb][D * 64] (T V)^T (in the scan's load order)
+  float* Kt;              // [B*H][nb][D * 64] (diag(gam_C / gam) K)^T (in the scan's load order)
   float* U;               // [B*H][nb][D][64] pseudo-values, transposed (U^T)
   float* Sst;             // [B*H][nb][D][D] state at each block start
   int32_t B, N, H, D, nb;

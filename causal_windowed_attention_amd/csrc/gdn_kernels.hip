@@ -70,6 +70,21 @@ __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16
     lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(t));
   }
 }
+// x = t1 + t2 + t3 to 2^-24 |x|: each part is the bf16 rounding of what the previous ones
+// leave (x - t1 and x - t1 - t2 are exact in fp32)
+__device__ __forceinline__ void split3_bf16(const float (&x)[8], bf16x8& t1, bf16x8& t2, bf16x8& t3) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float r = x[e];
+    const __bf16 a = static_cast<__bf16>(r);
+    r -= static_cast<float>(a);
+    const __bf16 b = static_cast<__bf16>(r);
+    r -= static_cast<float>(b);
+    t1[e] = a;
+    t2[e] = b;
+    t3[e] = static_cast<__bf16>(r);
+  }
+}
 __device__ __forceinline__ void unpack8(const float4& a, const float4& b, float (&x)[8]) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -78,13 +93,12 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, co
 }
 
 // ---- gdn_prep: per block, log gates, T, W = T diag(gam) K, Up = T V, Kt ---------------------
-// K K^T on v_mfma_f32_32x32x16_bf16 (bf16 inputs: exact products); T by forward
-// substitution on one wave while the others write Kt; T V and T diag(gam) K on the fp32
-// MFMA (v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
-// receives C[4 (l / 16) + j][l % 16]). Those two feed the state recurrence and keep fp32
-// operands; lane quad q takes tokens [16 q, 16 q + 16) of the contraction, one per step,
-// so its A row is 16 contiguous floats of T and its B column 16 contiguous bf16 of K^T or
-// V^T, which are staged transposed in LDS (rows of 64 + 8 bf16, conflict-free).
+// K K^T on v_mfma_f32_32x32x16_bf16 (bf16 inputs: exact products); T by a blocked inverse
+// (substitution within 16 x 16 blocks, merges on v_mfma_f32_16x16x4_f32: lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16] and receives C[4 (l / 16) + j][l % 16]); T V and
+// T diag(gam) K, which feed the state recurrence, on the bf16 MFMA with T split into three
+// bf16 parts (fp32 accuracy). K^T and V^T are staged transposed in LDS (rows of 64 + 8
+// bf16, conflict-free).
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
@@ -93,8 +107,10 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
   float* X = L + kC * kCL;                       // [64][kCL]: T
   float* g = X + kC * kCL;                       // [64] log cumulative gates
   float* bet = g + kC;                           // [64]
-  __bf16* KT = reinterpret_cast<__bf16*>(bet + kC);  // [D][VL]: K^T
+  float* gam = bet + kC;                         // [64] cumulative gates exp(g)
+  __bf16* KT = reinterpret_cast<__bf16*>(gam + kC);  // [D][VL]: K^T
   __bf16* VT = KT + D * VL;                      // [D][VL]: V^T
+  float* Mb = reinterpret_cast<float*>(VT + D * VL);  // [32][36]: products of the inverse's merges
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int l = tid & 63, w = tid >> 6, lc = l & 31, hf = l >> 5;
   const int t0 = blk * kC, n_valid = min(kC, p.N - t0);
@@ -115,9 +131,12 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
       if (tid >= o) s += t;
     }
     g[tid] = s;
+    gam[tid] = __expf(s);
     p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid] = s;
   }
+  for (int e = tid; e < kC * kCL / 4; e += kThr) st4(X + 4 * e, make_float4(0.f, 0.f, 0.f, 0.f));
   // K^T and V^T: a thread takes tokens (2 m, 2 m + 1) of 8 columns and writes packed pairs
+#pragma unroll
   for (int e = tid; e < 32 * (D / 8); e += kThr) {
     const int m = e & 31, c = (e >> 5) * 8, i0 = 2 * m;
     bf16x8 k0 = {}, k1 = {}, v0 = {}, v1 = {};
@@ -158,69 +177,118 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
     }
   }
   __syncthreads();
-  if (tid < kC) {
-    // X = (I + L)^-1 by forward substitution. Column j depends only on itself
-    // (X_jj = 1, X_ij = -sum_{k < i} L_ik X_kj), so lane j of the first wave solves it in
-    // registers; L_ik is the same address for every lane (an LDS broadcast). T = X diag(beta).
-    const int j = tid;
-    float x[kC];
+  // X = (I + L)^-1 (T = X diag(beta)), blocked over 16 x 16 blocks. (1) Each diagonal block
+  // by forward substitution: lane c < 16 of wave w solves column c of block w in registers
+  // (X_ii = 1, X_ij = -sum_{j <= k < i} L_ik X_kj). (2) The lower-left block of each 32 x 32
+  // diagonal block, and (3) that of the whole, as -X_B L_BA X_A for [[A, 0], [BA, B]], on
+  // the fp32 MFMA through the buffer Mb. The upper blocks stay zero.
+  if (l < 16) {
+    const int o = 16 * w, c = l;
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int k = 0; k + 3 < i; k += 4) {
-        const float4 lv = ld4(L + i * kCL + k);
-        s0 = fmaf(lv.x, x[k], s0);
-        s1 = fmaf(lv.y, x[k + 1], s1);
-        s2 = fmaf(lv.z, x[k + 2], s2);
-        s3 = fmaf(lv.w, x[k + 3], s3);
+      for (int k = 0; k < i; k += 2) {
+        s0 = fmaf(L[(o + i) * kCL + o + k], x[k], s0);
+        if (k + 1 < i) s1 = fmaf(L[(o + i) * kCL + o + k + 1], x[k + 1], s1);
       }
-#pragma unroll
-      for (int k = i & ~3; k < i; ++k) s0 = fmaf(L[i * kCL + k], x[k], s0);
-      x[i] = i == j ? 1.f : (i < j ? 0.f : -((s0 + s1) + (s2 + s3)));
+      x[i] = i == c ? 1.f : (i < c ? 0.f : -(s0 + s1));
     }
-    const float bj = bet[j];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) X[i * kCL + j] = x[i] * bj;
-  } else {
-    // meanwhile: Kt^T = (diag(exp(g_C - g)) K)^T in the scan's load order (kt_index),
-    // written contiguously: entry e is load (e / 256) of its wave's run, lane (e / 4) % 64
+    for (int i = 0; i < 16; ++i) X[(o + i) * kCL + o + c] = x[i];
+  }
+  const int lr = l & 15, q = l >> 4;
+  // 16 x 16 x 16 product on the fp32 MFMA: C += A B with A(r, k), B(k, c) read through
+  // accessors; k-step s of lane quad q is k = 4 s + q
+  auto mm16 = [&](f32x4 acc, auto A, auto B, int K) {
+    for (int s = 0; s < K / 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(lr, 4 * s + q), B(4 * s + q, lr), acc, 0, 0, 0);
+    return acc;
+  };
+  __syncthreads();
+  if (w < 2) {                                   // (2) blocks (2w, 2w + 1)
+    const int a0 = 32 * w, b0 = 32 * w + 16;
+    f32x4 m = mm16(f32x4{}, [&](int r, int k) { return L[(b0 + r) * kCL + a0 + k]; },
+                   [&](int k, int c) { return X[(a0 + k) * kCL + a0 + c]; }, 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Mb[(16 * w + 4 * q + j) * 36 + lr] = m[j];
+  }
+  __syncthreads();
+  if (w < 2) {
+    const int a0 = 32 * w, b0 = 32 * w + 16;
+    f32x4 x = mm16(f32x4{}, [&](int r, int k) { return X[(b0 + r) * kCL + b0 + k]; },
+                   [&](int k, int c) { return Mb[(16 * w + k) * 36 + c]; }, 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) X[(b0 + 4 * q + j) * kCL + a0 + lr] = -x[j];
+  }
+  __syncthreads();
+  const int tr = 16 * (w >> 1), tc = 16 * (w & 1);   // (3) this wave's 16 x 16 tile of 32 x 32
+  {
+    f32x4 m = mm16(f32x4{}, [&](int r, int k) { return L[(32 + tr + r) * kCL + k]; },
+                   [&](int k, int c) { return X[k * kCL + tc + c]; }, 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Mb[(tr + 4 * q + j) * 36 + tc + lr] = m[j];
+  }
+  __syncthreads();
+  {
+    f32x4 x = mm16(f32x4{}, [&](int r, int k) { return X[(32 + tr + r) * kCL + 32 + k]; },
+                   [&](int k, int c) { return Mb[k * 36 + tc + c]; }, 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) X[(32 + tr + 4 * q + j) * kCL + tc + lr] = -x[j];
+  }
+  {
+    // Kt^T = (diag(exp(g_C - g)) K)^T in the scan's load order (kt_index), written
+    // contiguously: entry e is load (e / 256) of its wave's run, lane (e / 4) % 64
     const float gC = g[kC - 1];
     constexpr int NT = D / 64;
-    for (int e = tid - kC; e < kC * D; e += kThr - kC) {
-      const int l = (e >> 2) & 63, run = e >> 8, u = run & 3, t = (run >> 2) % NT, w = run / (4 * NT);
-      const int c = w * (D / 4) + 16 * t + (l & 15), i = 16 * (l >> 4) + 4 * u + (e & 3);
+    for (int e = tid; e < kC * D; e += kThr) {
+      const int l2 = (e >> 2) & 63, run = e >> 8, u = run & 3, t = (run >> 2) % NT, ww = run / (4 * NT);
+      const int c = ww * (D / 4) + 16 * t + (l2 & 15), i = 16 * (l2 >> 4) + 4 * u + (e & 3);
       p.Kt[boff + e] = __expf(gC - g[i]) * static_cast<float>(KT[c * VL + i]);
     }
   }
   __syncthreads();
-  // Up = T V and W = T diag(gam) K: wave w takes the 16 tokens [16 w, 16 w + 16)
-  const int lr = l & 15, q = l >> 4, i = 16 * w + lr;
-  float ta[16], tg[16];
+  // Up = T V and W^T = K^T (T diag(gam))^T on v_mfma_f32_32x32x16_bf16. T enters as three
+  // bf16 parts (split3: t1 + t2 + t3 = T to 2^-24), V and K are bf16: every product is exact
+  // and the sums are fp32, as for an fp32 product. Tiles of 32 x 32: (token tile it, column
+  // tile dt), wave w takes tiles w, w + 4, ...; the T rows this lane reads serve as the A
+  // operand of Up and (scaled by gam) the B operand of W^T.
+  for (int tile = w; tile < 2 * (D / 32); tile += 4) {
+    const int it = tile & 1, dt = tile >> 1;
+    const int ti = 32 * it + lc, dc = 32 * dt + lc;
+    f32x16 au = {}, aw = {};
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-    const float4 t = ld4(X + i * kCL + 16 * q + 4 * s4);
-    ta[4 * s4] = t.x; ta[4 * s4 + 1] = t.y; ta[4 * s4 + 2] = t.z; ta[4 * s4 + 3] = t.w;
-  }
+    for (int ks = 0; ks < kC / 16; ++ks) {
+      const int j0 = 16 * ks + 8 * hf;
+      const float4 x0 = ld4(X + ti * kCL + j0), x1 = ld4(X + ti * kCL + j0 + 4);
+      float tb[8], tgm[8];
+      unpack8(x0, x1, tb);
 #pragma unroll
-  for (int s = 0; s < 16; ++s) tg[s] = ta[s] * __expf(g[16 * q + s]);
-#pragma unroll 2
-  for (int ct = 0; ct < D / 16; ++ct) {
-    const int d = 16 * ct + lr;
-    const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(VT + d * VL + 16 * q);
-    const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(VT + d * VL + 16 * q + 8);
-    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(KT + d * VL + 16 * q);
-    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(KT + d * VL + 16 * q + 8);
-    f32x4 au = {}, aw = {};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      au = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[s], static_cast<float>(s < 8 ? v0[s] : v1[s - 8]), au, 0, 0, 0);
-      aw = __builtin_amdgcn_mfma_f32_16x16x4f32(tg[s], static_cast<float>(s < 8 ? k0[s] : k1[s - 8]), aw, 0, 0, 0);
+      for (int e = 0; e < 8; ++e) {
+        tb[e] *= bet[j0 + e];
+        tgm[e] = tb[e] * gam[j0 + e];
+      }
+      bf16x8 u1, u2, u3, g1, g2, g3;
+      split3_bf16(tb, u1, u2, u3);
+      split3_bf16(tgm, g1, g2, g3);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(VT + dc * VL + j0);
+      const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(KT + dc * VL + j0);
+      au = mfma_bf16(u3, vb, au);
+      au = mfma_bf16(u2, vb, au);
+      au = mfma_bf16(u1, vb, au);
+      aw = mfma_bf16(kb8, g3, aw);
+      aw = mfma_bf16(kb8, g2, aw);
+      aw = mfma_bf16(kb8, g1, aw);
     }
+    // au: Up[32 it + 8 (r / 4) + 4 hf + r % 4][dc]; aw: W[32 it + lc][32 dt + 8 (r / 4) + 4 hf + r % 4]
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      p.Up[boff + up_index(d, 16 * w + 4 * q + jj)] = au[jj];
-      p.W[boff + w_index<D>(16 * w + 4 * q + jj, d)] = aw[jj];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int o = 8 * r4 + 4 * hf;
+      st4(p.Up + boff + up_index(dc, 32 * it + o),
+          make_float4(au[4 * r4], au[4 * r4 + 1], au[4 * r4 + 2], au[4 * r4 + 3]));
+      st4(p.W + boff + w_index<D>(ti, 32 * dt + o),
+          make_float4(aw[4 * r4], aw[4 * r4 + 1], aw[4 * r4 + 2], aw[4 * r4 + 3]));
     }
   }
 }
@@ -459,7 +527,7 @@ __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
 }
 
 template <int D>
-constexpr size_t prep_lds() { return (2 * kC * kCL + 2 * kC) * sizeof(float) + 2 * D * (kC + 8) * sizeof(__bf16); }
+constexpr size_t prep_lds() { return (2 * kC * kCL + 3 * kC + 32 * 36) * sizeof(float) + 2 * D * (kC + 8) * sizeof(__bf16); }
 
 template <int D>
 hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {

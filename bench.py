@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--variant", type=int, default=0,
                     help="bf16 attention kernel variant (0 automatic, 1 = 32 rows/wave, 2 = 64 rows/wave)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline workload only (a profiler's per-kernel averages then cover it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 4 times (scales the HBM byte counters)")
     return ap.parse_args()
@@ -510,13 +512,15 @@ def main():
             kern[name] = ms / n
     s.set_option(cwa.SA_OPT_PROFILE, 0)
 
-    mfma_probe = probe_mfma(torch, cwa)
-    buffer_res = bench_buffer(torch, cwa, synth)
-    fp8_res = bench_fp8(torch, cwa, synth)
-    gdn_res = bench_gdn(torch, cwa, synth)
-    configs_res = bench_configs(torch, cwa, synth)
-    steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
-    batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
+    mfma_probe = buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = None
+    if not args.headline_only:
+        mfma_probe = probe_mfma(torch, cwa)
+        buffer_res = bench_buffer(torch, cwa, synth)
+        fp8_res = bench_fp8(torch, cwa, synth)
+        gdn_res = bench_gdn(torch, cwa, synth)
+        configs_res = bench_configs(torch, cwa, synth)
+        steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
+        batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
 
     nk = st["visible_keys"]
     flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk

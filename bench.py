@@ -595,6 +595,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if configs_res is not None:
+            # the oracle beside every bf16 shape: heads of one steady chunk for about 1.5 s each
+            for name, c in configs_res.items():
+                o = cpu_baseline(synth.WORKLOADS[name], 1.5)
+                c["oracle"] = {"seconds_per_chunk": o["seconds_per_chunk"], "tokens_per_s": o["value"],
+                               "sample": o["sample"], "cores": o["cores"],
+                               "gpu_over_oracle": c["tokens_per_s"] / o["value"]}
     s.close()
     print(json.dumps(res), flush=True)
 

@@ -531,16 +531,14 @@ constexpr size_t prep_lds() { return (2 * kC * kCL + 3 * kC + 32 * 36) * sizeof(
 
 template <int D>
 hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
-  static_assert(prep_lds<D>() <= 160 * 1024,
-                "LDS budget");
+  static_assert(prep_lds<D>() <= 160 * 1024, "LDS budget");
   static_assert(D % 64 == 0, "scan tiles");
-  static bool attrs = false;                     // dynamic LDS above 64 KB, set once per process
-  if (!attrs) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_prep<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(prep_lds<D>()));
-    if (e != hipSuccess) return e;
-    attrs = true;
-  }
+  // gdn_prep takes more than 64 KB of dynamic LDS. Set on every call: a host-side call, safe
+  // from any thread and on whichever device is current.
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gdn_prep<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(prep_lds<D>()));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gdn_prep<D>, dim3(p.nb, p.H, p.B), dim3(kThr), prep_lds<D>(), st, p);
   hipLaunchKernelGGL(gdn_scan<D>, dim3(D / kGdnScanRows, p.H, p.B), dim3(kThr), 0, st, p);
   hipLaunchKernelGGL(gdn_out<D>, dim3(p.nb, p.H, p.B), dim3(kThr), 0, st, p);

@@ -51,5 +51,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_DEMO_SRC = os.path.join(ROOT, "tests", "c_abi", "sa_c_demo.c")
+C_DEMO = os.path.join(ROOT, "tests", "c_abi", "sa_c_demo")
+
+
+def build_c_demo(verbose: bool = False) -> str:
+    """Compile the plain C consumer of the C ABI (tests/c_abi/sa_c_demo.c) against libsa.so
+    and the HIP runtime with the host C compiler; it finds libsa.so next to this file."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = shutil.which(os.environ.get("CC", "gcc")) or "cc"
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), C_DEMO_SRC,
+           "-L", PKG, "-lsa", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../causal_windowed_attention_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_DEMO]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("C consumer build failed:\n" + r.stdout + r.stderr)
+    return C_DEMO
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_demo(verbose="-v" in sys.argv))

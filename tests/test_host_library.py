@@ -460,3 +460,18 @@ def test_gdn_sizes_and_errors():
     with pytest.raises(cwa.SaError) as e:
         cwa.sa_gdn_forward(1, 10, 1, 80, fake, fake, fake, fake, fake, None, fake, fake, fake, need)
     assert e.value.status == L.SA_ERR_UNSUPPORTED
+
+
+def test_c_consumer_builds_and_validates_before_any_device_call():
+    """The plain C consumer of the ABI (tests/c_abi/sa_c_demo, built by build()) links
+    against libsa.so and rejects bad arguments with status 2 before any HIP call, so
+    this runs without a GPU."""
+    import subprocess
+    from causal_windowed_attention_amd import build as b
+    assert os.path.exists(b.C_DEMO), "tests/c_abi/sa_c_demo is missing: run __graft_entry__.build()"
+    r = subprocess.run([b.C_DEMO], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage" in r.stderr
+    # head_dim 96 has no kernel: sa_config_check says so
+    r = subprocess.run([b.C_DEMO, "/nonexistent", "1", "2", "96", "4", "4", "2", "1", "2", "3"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "unsupported" in r.stderr.lower(), r.stderr

@@ -545,7 +545,22 @@ hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// state_out = state_in (zeros when state_in is null): the whole call when there are no
+// tokens. A kernel rather than a memset or copy node, so a captured call holds kernels only.
+__global__ __launch_bounds__(kThr) void gdn_state_pass(const float4* in, float4* out, size_t n4) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * kThr + threadIdx.x;
+  if (i < n4) out[i] = in != nullptr ? in[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 }  // namespace
+
+hipError_t launch_gdn_state_pass(const float* in, float* out, size_t n, hipStream_t st) {
+  const size_t n4 = n / 4;                        // n = B H D D, a multiple of 4096
+  if (n4 == 0 || in == out) return hipSuccess;
+  hipLaunchKernelGGL(gdn_state_pass, dim3(static_cast<unsigned>((n4 + kThr - 1) / kThr)), dim3(kThr), 0, st,
+                     reinterpret_cast<const float4*>(in), reinterpret_cast<float4*>(out), n4);
+  return hipGetLastError();
+}
 
 hipError_t launch_gdn_forward(const GdnParams& p, hipStream_t st) {
   if (p.N <= 0) return hipSuccess;

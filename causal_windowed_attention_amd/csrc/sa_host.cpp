@@ -1018,7 +1018,9 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
   const sa_status st = gdn_layout(batch, tokens, heads, head_dim, &L);
   if (st != SA_OK) return st;
   auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-  if (state_out == nullptr || !a4(state_out) || (state_in != nullptr && !a4(state_in))) return SA_ERR_INVALID_ARGUMENT;
+  // the states move as float4s
+  if (state_out == nullptr || !aligned16(state_out) || (state_in != nullptr && !aligned16(state_in)))
+    return SA_ERR_INVALID_ARGUMENT;
   if (tokens > 0) {                              // with no tokens only the state is touched
     if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || out == nullptr ||
         workspace == nullptr)
@@ -1044,10 +1046,8 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
   p.B = batch; p.N = tokens; p.H = heads; p.D = head_dim; p.nb = L.nb;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (tokens == 0) {                             // no tokens: the state passes through
-    const size_t n = static_cast<size_t>(batch) * heads * head_dim * head_dim * 4;
-    if (state_in == nullptr) return hipMemsetAsync(state_out, 0, n, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
-    if (state_in == state_out) return SA_OK;
-    return hipMemcpyAsync(state_out, state_in, n, hipMemcpyDeviceToDevice, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
+    const size_t n = static_cast<size_t>(batch) * heads * head_dim * head_dim;
+    return sa::launch_gdn_state_pass(state_in, state_out, n, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
   }
   return sa::launch_gdn_forward(p, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
 }

@@ -149,5 +149,7 @@ hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st
 hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 hipError_t launch_gdn_forward(const GdnParams& p, hipStream_t st);
+// out[0, n) = in[0, n), or zeros when in is null (n floats, a multiple of 4; in == out: nothing)
+hipError_t launch_gdn_state_pass(const float* in, float* out, size_t n, hipStream_t st);
 
 }  // namespace sa

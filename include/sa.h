@@ -374,8 +374,8 @@ sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* 
  * a triangular solve per block, the state carried block to block). All buffers are
  * the caller's; nothing is allocated. With N = 0 only state_in / state_out are used
  * (the state passes through; the others may be NULL). Errors: SA_ERR_INVALID_ARGUMENT
- * for NULL or misaligned pointers (16 bytes for bf16 tensors and the workspace, 4 for
- * float32) or sizes < 1 (N < 0);
+ * for NULL or misaligned pointers (16 bytes for the bf16 tensors, the states and the
+ * workspace, 4 for alpha and beta) or sizes < 1 (N < 0);
  * SA_ERR_UNSUPPORTED for D not 64 or 128, H or B beyond 32767, N beyond 2^24;
  * SA_ERR_WORKSPACE_TOO_SMALL; SA_ERR_DEVICE if a launch fails.
  */

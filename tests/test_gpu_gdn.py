@@ -54,7 +54,7 @@ def test_gdn_matches_recurrence(B, N, H, D):
 
 def test_gdn_carried_state_in_place_and_zero_state():
     """Two calls with the state carried (in place) equal one call over both token ranges;
-    no initial state means zeros; N = 0 passes the state through."""
+    no initial state means zeros; N = 0 passes the state through (zeros without one)."""
     B, N, H, D = 1, 200, 2, 128
     q, k, v, a, b_, _ = synth.gdn_inputs(B, N, H, D, seed=9, state=False)
     o_ref, S_ref = gdn_recurrent(q, k, v, a, b_)
@@ -70,8 +70,11 @@ def test_gdn_carried_state_in_place_and_zero_state():
     e = torch.empty((B, 0, H, D), dtype=torch.bfloat16, device="cuda")
     ea = torch.empty((B, H, 0), dtype=torch.float32, device="cuda")
     _, s_out = cwa.gdn_forward(e, e, e, ea, ea, state=state)
+    z = torch.full_like(state, 7.0)
+    _, z_out = cwa.gdn_forward(e, e, e, ea, ea, state=None, state_out=z)     # no state in: zeros out
     torch.cuda.synchronize()
     assert torch.equal(s_out, before)
+    assert z_out.data_ptr() == z.data_ptr() and not torch.any(z)
 
 
 @pytest.mark.parametrize("name", ["hybrid1280x704", "wan1.3b"])

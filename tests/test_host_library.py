@@ -451,6 +451,8 @@ def test_gdn_sizes_and_errors():
                 workspace=fake, workspace_bytes=need)
     for kw, code in [(dict(q=None), L.SA_ERR_INVALID_ARGUMENT), (dict(out=fake + 8), L.SA_ERR_INVALID_ARGUMENT),
                      (dict(alpha=fake + 2), L.SA_ERR_INVALID_ARGUMENT),
+                     (dict(state_out=fake + 4), L.SA_ERR_INVALID_ARGUMENT),     # states move as float4s
+                     (dict(state_in=fake + 8), L.SA_ERR_INVALID_ARGUMENT),
                      (dict(workspace_bytes=need - 1), L.SA_ERR_WORKSPACE_TOO_SMALL)]:
         a = dict(args, **kw)
         with pytest.raises(cwa.SaError) as e:

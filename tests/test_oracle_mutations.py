@@ -38,6 +38,13 @@ M = [
  ("stream.py", [("self.ring_next = (self.ring_next + 1) % s.window_chunks", "self.ring_next = (self.ring_next + 2) % s.window_chunks")], "ring slot order"),
  ("stream.py", [("            self.sink_meta[j] = [True, self.n_appends, self.t_next]", "            self.sink_meta[j] = [True, self.n_appends, 0]")], "ring sink chunks all at t = 0"),
  ("stream.py", [("entry = [self.n_appends, self.t_next, np.array(k", "entry = [self.n_appends, self.t_next + 1, np.array(k")], "chunks committed one frame late"),
+ ("stream.py", [("                tmp.t_next = self.t_next + j * s.frames_per_chunk", "                tmp.t_next = self.t_next")], "steps: every chunk at t_next"),
+ ("stream.py", [("            if not steps and j + 1 < n:\n                tmp.append(k[:, sl], v[:, sl])", "            if not steps and j + 1 < n:\n                tmp.t_next += s.frames_per_chunk")], "buffer: earlier chunks not visible"),
+ ("stream.py", [("            self.sink[j] = [-1, j * s.frames_per_chunk,", "            self.sink[j] = [-1, 0,")], "history sink update: all at t = 0"),
+ ("stream.py", [("    k = -math.floor(math.log2(c))", "    k = -math.ceil(math.log2(c))")], "fp8 query factor in [0.5, 1)"),
+ ("stream.py", [("            return self.spec.sink_chunks * self.spec.frames_per_chunk", "            return self.spec.sink_chunks")], "refresh default base in chunks"),
+ ("rope.py", [("        dh = 2 * (head_dim // 6)", "        dh = 2 * (head_dim // 8)")], "default RoPE split"),
+ ("attention.py", [("            scores.append(acc * scale)", "            scores.append(acc)")], "scalar twin without scale"),
  ("bf16.py", [("spacing_exp = np.maximum(e - 8, -133)", "spacing_exp = np.maximum(e - 9, -133)")], "bf16 spacing"),
  ("bf16.py", [("np.rint(np.ldexp(v, -spacing_exp))", "np.trunc(np.ldexp(v, -spacing_exp))")], "bf16 truncation"),
  ("fp8.py", [("spacing_exp = np.maximum(e - 4, -9)", "spacing_exp = np.maximum(e - 3, -9)")], "E4M3 spacing"),

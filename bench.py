@@ -425,8 +425,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(a stream's caches live on one GPU; see DESIGN.md for how it would shard)",
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(a stream's caches live on one GPU; streams and heads would shard across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -31,9 +31,9 @@ only shared module is ``synth`` (seeded input generators, no method arithmetic).
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 closed forms, library special cases, brute force and hand-worked expectations.
 The conventions the pages leave open (RoPE axis split, base, pairing, the
-temporal unit, refresh semantics) are readings, documented in the design doc; they
-cannot be pinned against the pages' own systems, which print no formula or
-number for this path.
+temporal unit, refresh semantics) are readings, each stated in the module that
+applies it; they cannot be pinned against the pages' own systems, which print
+no formula or number for this path.
 """
 from .bf16 import round_bf16, is_bf16_exact
 from .fp8 import round_e4m3, is_e4m3_exact

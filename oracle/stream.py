@@ -10,7 +10,7 @@ What the pages fix (in words, not quoted):
 * RoPE offsets are reset periodically at chunk boundaries so positions stay
   aligned over long horizons (StreamDiffusionV2, 2.A.2).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * the chunk attends to itself fully (no causal mask inside the chunk);
 * W counts previous committed chunks, excluding the current one;
 * the first S committed chunks become the sink and do not also enter the

@@ -811,9 +811,14 @@ __device__ __forceinline__ void pp_segment(const AttnParams& p, const Bases& bs,
   for (int i = 1; i < n; ++i) {
     if (!lag) wait_tile(i);
     __syncthreads();
+    // bf16: the wave in its MFMA block (and the copies it issues) takes priority over the
+    // other group's softmax on the same SIMD (measured: 1-2 % on one chunk, 5-6 % on the
+    // group kernel); the VALU-bound fp8 blocks gain nothing from it
+    if constexpr (!F8) __builtin_amdgcn_s_setprio(1);
     if (i + 2 < n) issue_tile(i + 2);
     qk_pv(i);                                    // M(i)
     block_end();
+    if constexpr (!F8) __builtin_amdgcn_s_setprio(0);
     if (lag && i + 1 < n) wait_tile(i + 1);
     __syncthreads();
     softmax(i);                                  // V(i)

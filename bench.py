@@ -295,7 +295,7 @@ BF16_CONFIGS = ("wan1.3b", "wan14b_b1", "wan14b_b2", "wan14b_b4", "hybrid1280x70
 
 def bench_configs(torch, cwa, synth, steps=20):
     """Every bf16 workload shape at steady state (a full sink and window): the step (attend +
-    commit) per chunk as p50 / p99 of per-step events, the attention kernel's time and its
+    commit) and the attend alone per chunk as p50 / p99 of per-step events, the attention kernel's time and its
     algorithmic FLOP rate (visible keys only), and misses against the per-chunk budgets of
     24 and 16 frames/s. A pool of two distinct chunks cycles through the stream."""
     res = {}
@@ -308,20 +308,23 @@ def bench_configs(torch, cwa, synth, steps=20):
                 for i in range(2)]
         out = torch.empty_like(pool[0][0])
 
-        def step(i):
+        def step(i, mid=None):
             q, k, v = pool[i % 2]
             s.chunk_attend(q, k, v, out=out)
+            if mid is not None:
+                mid.record()
             s.kv_append(k, v)
         for i in range(w.sink_chunks + w.window_chunks + 3):
             step(i)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
         for i in range(steps):
             evs[i][0].record()
-            step(i)
-            evs[i][1].record()
+            step(i, evs[i][1])
+            evs[i][2].record()
         torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in evs)
+        t = sorted(a.elapsed_time(c) for a, _, c in evs)
+        ta = sorted(a.elapsed_time(b) for a, b, _ in evs)
         s.set_option(cwa.SA_OPT_PROFILE, 1)
         s.profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
         for i in range(steps):
@@ -336,6 +339,8 @@ def bench_configs(torch, cwa, synth, steps=20):
         budgets = {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)}
         res[name] = {"batch": w.batch, "heads": w.heads, "tokens_per_chunk": nc, "visible_keys": keys,
                      "step_ms_p50": t[len(t) // 2], "step_ms_p99": t[min(len(t) - 1, int(round(0.99 * (len(t) - 1))))],
+                     "attend_ms_p50": ta[len(ta) // 2],
+                     "attend_ms_p99": ta[min(len(ta) - 1, int(round(0.99 * (len(ta) - 1))))],
                      "attention_ms": attn_ms, "tokens_per_s": w.batch * nc / (t[len(t) // 2] * 1e-3),
                      "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
                      "deadline_misses": {fps: sum(x > b for x in t) for fps, b in budgets.items()}}
@@ -452,9 +457,11 @@ def main():
         pool.append(tuple(torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v)))
     out = torch.empty_like(pool[0][0])
 
-    def step(i):
+    def step(i, mid=None):
         q, k, v = pool[i % len(pool)]
         s.chunk_attend(q, k, v, out=out)
+        if mid is not None:
+            mid.record()                         # attend done, append next
         s.kv_append(k, v)
 
     # ---- full stream from empty (warm-up chunks included), once -----------------
@@ -479,14 +486,15 @@ def main():
     value = w.batch * nc * args.steps / dt
 
     # ---- per-step GPU time distribution (events on the stream the library uses) ---
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     for i in range(args.steps):
         evs[i][0].record()
-        step(i)
-        evs[i][1].record()
+        step(i, evs[i][1])
+        evs[i][2].record()
     torch.cuda.synchronize()
-    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
+    step_ms = sorted(a.elapsed_time(c) for a, _, c in evs)
+    attend_only_ms = sorted(a.elapsed_time(b) for a, b, _ in evs)
+    pct = lambda q, v=step_ms: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
     # ---- per-kernel durations: HIP events on the launch stream ------------------
     s.set_option(cwa.SA_OPT_PROFILE, 1)
@@ -581,6 +589,8 @@ def main():
         "pct_bf16_peak_attend": flops / (attend_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stream_cold_start": {"chunks": w.n_chunks, "ms": stream_ms, "ms_per_chunk": stream_ms / w.n_chunks},
         "step_ms": {"p50": pct(0.5), "p99": pct(0.99), "max": step_ms[-1], "n": len(step_ms)},
+        "attend_step_ms": {"p50": pct(0.5, attend_only_ms), "p99": pct(0.99, attend_only_ms),
+                           "max": attend_only_ms[-1], "n": len(attend_only_ms)},
         # a chunk of F latent frames must be produced within F frame periods; this layer's
         # attention step is one of many inside that budget
         "chunk_budget_ms": {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)},

@@ -76,3 +76,42 @@ def test_batch_attend_matches_per_stream_oracles(case):
             hists[i].append(data[i][1], data[i][2])
     for s in streams:
         s.close()
+
+
+@pytest.mark.gpu
+def test_batch_attend_full_size_sampled():
+    """The launch bench.py times: eight long512p streams (H = 24, Nc = 2048, S = 1, W = 3) at 0 to 7
+    commits (empty, partly filled and wrapped windows; one refreshed) in one ragged launch.
+    Sampled query rows of two heads of every stream against that stream's fp64 oracle."""
+    w = synth.WORKLOADS["long512p"]
+    n, heads = 8, [0, w.heads - 1]
+    nc = w.tokens_per_chunk
+    say("batch full size long512p: streams", n, "H", w.heads, "Nc", nc, "heads checked", heads)
+    cfg = config_for(w)
+    streams = [cwa.Stream(cfg) for _ in range(n)]
+    hists = [HistoryOracle(spec_for(w, heads)) for _ in range(n)]
+    for i in range(n):
+        for c in range(i):
+            _, k, v = synth.chunk_qkv(w, 100 * i + c)
+            streams[i].kv_append(dev(k, w.dtype), dev(v, w.dtype))
+            hists[i].append(k[:, :, heads], v[:, :, heads])
+    assert streams[6].rope_refresh(-1, 0) == hists[6].refresh(None, 0)
+    data = [synth.chunk_qkv(w, 100 * i + 99) for i in range(n)]
+    qs, ks, vs = ([dev(d[j], w.dtype) for d in data] for j in range(3))
+    outs = [torch.empty_like(x) for x in qs]
+    lses = [torch.empty((w.batch, w.heads, nc), dtype=torch.float32, device="cuda") for _ in range(n)]
+    cwa.sa_batch_attend(streams, qs, ks, vs, outs, lses)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(2), np.arange(nc - 2, nc), g.choice(nc, 28, replace=False)]))
+    for i in range(n):
+        q, k, v = (x[:, :, heads] for x in data[i])
+        want, want_lse = hists[i].attend(q, k, v, rows=list(rows))
+        got = host(outs[i])[:, rows][:, :, heads]
+        got_lse = host(lses[i])[:, heads][:, :, rows]
+        a, r = err(got, want[:, rows])
+        la, _ = err(got_lse, want_lse[:, :, rows])
+        say(f"  stream {i} ({streams[i].query()['visible_keys']} keys): max {a:.2e} rel {r:.2e}; lse {la:.2e}")
+        assert a <= BF16_ABS and r <= BF16_REL and la <= BF16_ABS, (i, a, r, la)
+    for s in streams:
+        s.close()

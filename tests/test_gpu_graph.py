@@ -75,3 +75,50 @@ def test_captured_attend_replays_match_eager(splits):
     if splits:
         assert plan["last_kv_splits"] == splits
     s.close()
+
+
+def test_captured_gdn_forward_carries_state_like_eager():
+    """sa_gdn_forward keeps no host state: a captured call, replayed over consecutive chunks
+    with the state carried in place, equals the same calls made eagerly (bit for bit)."""
+    B, N, H, D = 1, 150, 2, 128
+    say("graph capture: gdn_forward B", B, "N", N, "H", H, "D", D)
+    chunks = [synth.gdn_inputs(B, N, H, D, seed=40 + j, state=False) for j in range(3)]
+    d16 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
+    d32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    q_s, k_s, v_s = (torch.empty((B, N, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    a_s, b_s = (torch.empty((B, H, N), dtype=torch.float32, device="cuda") for _ in range(2))
+    out_s = torch.empty_like(q_s)
+    state = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cwa.sa_gdn_workspace_bytes(B, N, H, D), dtype=torch.uint8, device="cuda")
+
+    def load(j):
+        q, k, v, a, b, _ = chunks[j]
+        for dst, x in ((q_s, d16(q)), (k_s, d16(k)), (v_s, d16(v)), (a_s, d32(a)), (b_s, d32(b))):
+            dst.copy_(x)
+
+    def call():
+        cwa.gdn_forward(q_s, k_s, v_s, a_s, b_s, state=state, out=out_s, state_out=state, workspace=ws)
+
+    eager = []
+    for j in range(len(chunks)):
+        load(j)
+        call()
+        torch.cuda.synchronize()
+        eager.append((out_s.clone(), state.clone()))
+    state.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    load(0)
+    torch.cuda.synchronize()
+    snapshot = state.clone()
+    with torch.cuda.graph(g):
+        call()
+    state.copy_(snapshot)                        # capture runs nothing; start again from zeros
+    for j in range(len(chunks)):
+        load(j)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(out_s, eager[j][0]) and torch.equal(state, eager[j][1])
+        say(f"  replay chunk {j}: identical to eager: {same}")
+        assert same, j

@@ -238,14 +238,20 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
     for (int j = 0; j < 4; ++j) X[(32 + tr + 4 * q + j) * kCL + tc + lr] = -x[j];
   }
   {
-    // Kt^T = (diag(exp(g_C - g)) K)^T in the scan's load order (kt_index), written
-    // contiguously: entry e is load (e / 256) of its wave's run, lane (e / 4) % 64
+    // Kt^T = (diag(exp(g_C - g)) K)^T in the scan's load order (kt_index), written as
+    // float4s: entries 4 f .. 4 f + 3 are load (f / 64) of their wave's run, lane f % 64,
+    // i.e. four consecutive tokens of one column (one 8-byte read of K^T)
     const float gC = g[kC - 1];
     constexpr int NT = D / 64;
-    for (int e = tid; e < kC * D; e += kThr) {
-      const int l2 = (e >> 2) & 63, run = e >> 8, u = run & 3, t = (run >> 2) % NT, ww = run / (4 * NT);
-      const int c = ww * (D / 4) + 16 * t + (l2 & 15), i = 16 * (l2 >> 4) + 4 * u + (e & 3);
-      p.Kt[boff + e] = __expf(gC - g[i]) * static_cast<float>(KT[c * VL + i]);
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    for (int f = tid; f < kC * D / 4; f += kThr) {
+      const int l2 = f & 63, run = f >> 6, u = run & 3, t = (run >> 2) % NT, ww = run / (4 * NT);
+      const int c = ww * (D / 4) + 16 * t + (l2 & 15), i = 16 * (l2 >> 4) + 4 * u;
+      const bf16x4 kk = *reinterpret_cast<const bf16x4*>(KT + c * VL + i);
+      st4(p.Kt + boff + 4 * f, make_float4(__expf(gC - g[i]) * static_cast<float>(kk[0]),
+                                           __expf(gC - g[i + 1]) * static_cast<float>(kk[1]),
+                                           __expf(gC - g[i + 2]) * static_cast<float>(kk[2]),
+                                           __expf(gC - g[i + 3]) * static_cast<float>(kk[3])));
     }
   }
   __syncthreads();

@@ -188,7 +188,9 @@ typedef enum sa_option {
   SA_OPT_PROFILE = 1,       /* 1: record HIP events around every launch (sa_profile_read)    */
   SA_OPT_ATTN_VARIANT = 2,  /* bf16 attention kernel: 0 automatic (3), 1 = 4 waves x 32
                                query rows, 2 = 4 waves x 64 rows, 3 = 8 waves x 32 rows with
-                               a ping-pong MFMA/softmax schedule (SA_FP8: 0 or 3 only)       */
+                               a ping-pong MFMA/softmax schedule, 4 = 8 waves x 32 rows, each
+                               wave software-pipelining its own MFMAs and softmax (head_dim
+                               128; other sizes run 3). SA_FP8: 0 or 3 only                   */
   SA_OPT_SCHEDULE = 3       /* variant 3 work distribution: 0 automatic (1), 1 = one workgroup per
                                (b, h, q-tile, split), 2 = stream-K (persistent workgroups
                                sharing the q-tile x key-tile iterations evenly, partial tiles
@@ -290,9 +292,13 @@ sa_status sa_buffer_plan(const sa_stream* s, int32_t n_chunks, uint32_t flags, i
                          int32_t* seg_lo, int32_t* seg_hi);
 
 /*
- * Commit one chunk: its k, v ([B, Nc, H, D]) are rotated at positions t_next..
- * and stored into the next sink slot while the sink is not full, else into the
- * window, evicting the oldest window chunk; then t_next += F. With k = v =
+ * Commit one chunk (SANA-Streaming, "Transformer a diffusione ibrido": the
+ * softmax blocks keep a persistent sink chunk and a sliding local window of the
+ * most recent chunks, so the cache stays bounded as the stream grows; this call
+ * is the step that slides that window). Its k, v ([B, Nc, H, D]) are rotated
+ * at positions t_next.. and stored into the next sink slot while the sink is
+ * not full, else into the window, evicting the oldest window chunk; then
+ * t_next += F. k and v are read only; ownership stays with the caller. With k = v =
  * NULL the K/V staged by the last sa_chunk_attend are committed without any
  * device work (SA_ERR_BAD_STATE if no attend staged them since the last state
  * change).

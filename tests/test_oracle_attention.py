@@ -36,6 +36,25 @@ def test_rows_sum_to_one_and_lse():
     np.testing.assert_allclose(l, logsumexp((q @ k.T) * 0.125, axis=1), rtol=1e-14)
 
 
+@pytest.mark.parametrize("nq,nk,d", [(5, 5, 4), (3, 9, 6), (8, 8, 3), (6, 2, 5)])
+def test_attention_probs_are_the_weights(nq, nk, d):
+    """attention_probs is the weight matrix of the same definition: with the identity as
+    the values, the scalar-loop twin returns exactly the weights (row i of its output is
+    p_i.), the weights times any V give attend()'s output, and log p_ij = s_ij - LSE_i.
+    Square cases (nq = nk) catch a transposed score product, which has the right shape
+    there."""
+    q, k = _r((nq, d), 11), _r((nk, d), 12)
+    p = attention_probs(q, k, 0.6)
+    assert p.shape == (nq, nk)
+    pb, lb = attend_bruteforce(q, k, np.eye(nk), 0.6)
+    np.testing.assert_allclose(p, pb, rtol=0, atol=1e-14)
+    v = _r((nk, 5), 13)
+    o, l = attend(q, k, v, 0.6)
+    np.testing.assert_allclose(p @ v, o, rtol=0, atol=1e-13)
+    s = np.array([[0.6 * sum(float(a) * float(b) for a, b in zip(qi, kj)) for kj in k] for qi in q])
+    np.testing.assert_allclose(np.log(p), s - lb[:, None], rtol=0, atol=1e-12)
+
+
 def test_closed_forms():
     k, v = _r((9, 4), 7), _r((9, 3), 8)
     # q = 0: uniform weights -> mean of the visible values

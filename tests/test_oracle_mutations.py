@@ -45,6 +45,13 @@ M = [
  ("stream.py", [("            return self.spec.sink_chunks * self.spec.frames_per_chunk", "            return self.spec.sink_chunks")], "refresh default base in chunks"),
  ("rope.py", [("        dh = 2 * (head_dim // 6)", "        dh = 2 * (head_dim // 8)")], "default RoPE split"),
  ("attention.py", [("            scores.append(acc * scale)", "            scores.append(acc)")], "scalar twin without scale"),
+ ("attention.py", [("    s = (np.asarray(q, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T) * scale",
+                   "    s = (np.asarray(q, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)")], "weights: scale dropped"),
+ ("attention.py", [("    s = (np.asarray(q, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T) * scale",
+                   "    s = (np.asarray(k, dtype=np.float64) @ np.asarray(q, dtype=np.float64).T) * scale")], "weights: transposed score product"),
+ ("attention.py", [("    return p / p.sum(axis=1, keepdims=True)", "    return p / p.sum(axis=0, keepdims=True)")], "weights: normalised over queries"),
+ ("attention.py", [("    m = s.max(axis=1, keepdims=True)\n    p = np.exp(s - m)\n    return",
+                   "    m = s.max(axis=0, keepdims=True)\n    p = np.exp(s - m)\n    return")], "weights: maximum over queries"),
  ("bf16.py", [("spacing_exp = np.maximum(e - 8, -133)", "spacing_exp = np.maximum(e - 9, -133)")], "bf16 spacing"),
  ("bf16.py", [("np.rint(np.ldexp(v, -spacing_exp))", "np.trunc(np.ldexp(v, -spacing_exp))")], "bf16 truncation"),
  ("fp8.py", [("spacing_exp = np.maximum(e - 4, -9)", "spacing_exp = np.maximum(e - 3, -9)")], "E4M3 spacing"),

@@ -936,6 +936,408 @@ __device__ __forceinline__ void chunk_attention_pp_body(const AttnParams& p) {
   }
 }
 
+// ---- Software-pipelined schedule ("pipe") ---------------------------------------------------
+// 8 waves x 32 query rows (BM = 256), two waves per SIMD and no lag between them: every wave
+// streams MFMAs and softmax VALU work at once, so both waves of a SIMD feed its matrix pipe
+// and the softmax runs under the MFMAs. Iteration j of a wave issues, in one straight block,
+//   first half    QK(j)   S_j = K_j Q^T              16 MFMAs, K operands read from LDS
+//   second half   PV(j-2) O^T += V_{j-2}^T P_{j-2}^T 16 MFMAs, V^T operands read from LDS
+//   throughout    weights of tile j-1: P = 2^(S c - m_{j-1}), rounded to bf16, row sums
+//   second half   row maximum of tile j (its scores are complete after the first half)
+// The VALU work is software-pipelined (scale-and-shift of pair p+2, exponentials of pair
+// p+1 and packing of pair p in one step), so no instruction waits on the one before it.
+// Running maximum: m_j = max_j S c if that passes m_{j-1} by more than 2^8, else m_{j-1};
+// the weights of tile j use m_j, and O_j = alpha_j O_{j-1} + P_j V_j, l_j = alpha_j l_{j-1} +
+// sum P_j with alpha_j = 2^(m_{j-1} - m_j): alpha_{j-1} is applied to O at the end of
+// iteration j, after PV(j-2) and before PV(j-1). Scores and weights alternate between two
+// register sets with the parity of j.
+// K and V^T tiles sit in separate LDS rings of kPipeStages stages. Iteration j issues the
+// copies of K_{j+3} and V_{j+1}, both read at iteration j + 3; one barrier per iteration
+// publishes the tiles iteration j reads and retires the stages its copies overwrite.
+constexpr int kPipeStages = 4;
+
+template <int D>
+struct PipeSmem {
+  static constexpr int BYTES = kPipeStages * (Bf16Geom<D>::KBYTES + Bf16Geom<D>::VBYTES);
+};
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, N] (the instruction takes an immediate).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if constexpr (N <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= N) __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    else wait_vm_at_most<N - 1>(n);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pipe_segment(const AttnParams& p, const Bases& bs, char* smem, int bh, int q_base,
+                                             int q_end, int t_begin, int t_end, int mode, int slot) {
+  using G = Bf16Geom<D>;
+  constexpr int NW = 8, ST = kPipeStages;
+  constexpr int BN = G::BN;
+  constexpr int KSTEPS = D / 16, MT = BN / 32, DT = D / 32, PSTEPS = BN / 16;
+  constexpr int NQK = KSTEPS * MT, NPV = PSTEPS * DT;   // MFMAs of QK and of PV per iteration
+  static_assert(NQK == NPV && NQK % 2 == 0, "QK and PV halves of equal length");
+  constexpr int HALF = NQK / 2;                  // steps per half (two MFMAs a step)
+  constexpr int STEPS = 2 * HALF;
+  constexpr int NEL = MT * 16;                   // scores per lane per tile
+  constexpr int NPAIR = NEL / 2;
+  static_assert(NPAIR <= STEPS, "at most one weight pair per step");
+  constexpr int KC = G::KBYTES / 1024 / NW;      // 1 KB copies per wave per K tile
+  constexpr int VC = G::VBYTES / 1024 / NW;
+  static_assert(KC * NW * 1024 == G::KBYTES && VC * NW * 1024 == G::VBYTES, "copy split");
+  static_assert(2 * (KC + VC) <= 63, "vmcnt range");
+  char* const kring = smem;
+  char* const vring = smem + ST * G::KBYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int n = t_end - t_begin;                 // key tiles of this work item (>= 1)
+  const int n_keys = p.n_keys;
+
+  const char* kbase = static_cast<const char*>(bs.kcache) + static_cast<size_t>(bh) * p.k_bh_stride * 2;
+  const char* vbase = static_cast<const char*>(bs.vtcache) + static_cast<size_t>(bh) * p.vt_bh_stride * 2;
+
+  const int q = q_base + wave * 32 + l32;
+  bf16x8 bq[KSTEPS];                             // Q^T operand: lane l holds query l % 32
+  {
+    const int qrow = min(q, q_end - 1);
+    const char* qsrc = static_cast<const char*>(bs.q) + (static_cast<size_t>(bh) * bs.rows + qrow) * D * 2;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qsrc + (16 * s + 8 * g) * 2);
+  }
+
+  // tile copies (the ping-pong kernel's swizzled images, K and V^T in separate rings)
+  auto k_src = [&](int c) {
+    const int P = (c * NW + wave) * 64 + lane;
+    const int r = P / G::KC;
+    return swap_bits23(r) * G::KROW + swz(P % G::KC, r, G::KC) * 16;
+  };
+  auto v_src = [&](int c) {
+    const int P = (c * NW + wave) * 64 + lane;
+    const int d = P / G::VC;
+    return d * p.key_stride * 2 + swz(P % G::VC, d, G::VC) * 16;
+  };
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, p.k_bh_stride * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, p.vt_bh_stride * 2);
+  auto issue_k = [&](int i) {
+    const int key0 = (t_begin + i) * BN;
+    char* dst = kring + (i % ST) * G::KBYTES;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) lds_copy16(krs, key0 * G::KROW + k_src(c), dst + (c * NW + wave) * 1024);
+  };
+  auto issue_v = [&](int i) {
+    const int key0 = (t_begin + i) * BN;
+    char* dst = vring + (i % ST) * G::VBYTES;
+#pragma unroll
+    for (int c = 0; c < VC; ++c) lds_copy16(vrs, key0 * 2 + v_src(c), dst + (c * NW + wave) * 1024);
+  };
+  // copies issued at iteration x: a full set (K_{x+3}, V_{x+1}, or nothing useful past the
+  // end) from x = 0; the prologue (x = -3, -2, -1) issues K_{x+3} and, at x = -1, V_0
+  auto set_size = [&](int x) {
+    if (x >= 0) return KC + VC;
+    return KC * ((x + 3 < n) ? 1 : 0) + VC * (x == -1 ? 1 : 0);
+  };
+
+  const int ka_row = l32 * G::KROW;
+  auto k_op = [&](const char* ks, int s, int mt) {
+    return *reinterpret_cast<const bf16x8*>(ks + ka_row + swz(2 * s + g, l32, G::KC) * 16 + mt * 32 * G::KROW);
+  };
+  auto v_op = [&](const char* vs, int s, int dt) {
+    return *reinterpret_cast<const bf16x8*>(vs + l32 * G::VROW + swz(2 * s + g, l32, G::VC) * 16 + dt * 32 * G::VROW);
+  };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
+  f32x16 sc[2][MT];                              // scores of tiles of parity 0 / 1
+  bf16x8 pw[2][PSTEPS];                          // their weights
+  // m: reference of the latest tile whose maximum is known; the weights of the tile before
+  // it use m_prev (= m except right after that maximum moved it)
+  float m = -__builtin_inff(), nm_w = 0.f, l = 0.f, alpha_prev = 1.f;
+  bool raise_prev = false;
+  const float c2 = p.scale_log2;
+  const int tail_tile = (n_keys % BN) && (t_end == p.key_tiles) ? n - 1 : -1;
+
+  // Iteration j: QK(j) and the maximum of tile j if QK, the weights of tile j-1 if SM, PV(j-2)
+  // if PV; TAIL masks tile j's keys past n_keys before its maximum. STG = j % ST when known at
+  // compile time (the LDS offsets then fold into the read instructions), else -1; PAR = j % 2.
+  auto iteration = [&](int j, auto stg_c, auto par_c, auto qk_c, auto sm_c, auto pv_c, auto tail_c) {
+    constexpr int STG = decltype(stg_c)::value, PAR = decltype(par_c)::value;
+    constexpr bool QK = decltype(qk_c)::value, SM = decltype(sm_c)::value, PV = decltype(pv_c)::value;
+    constexpr bool TAIL = decltype(tail_c)::value;
+    static_assert(STG < 0 || STG % 2 == PAR, "stage and parity agree");
+    // K_j and V_{j-2} (the copies of iteration j - 3) have landed for this wave; the copies of
+    // iterations j - 2 and j - 1 may still be in flight. The barrier makes every wave's land.
+    wait_vm_at_most<2 * (KC + VC)>(set_size(j - 2) + set_size(j - 1));
+    __builtin_amdgcn_s_barrier();
+    // this iteration's copies (K_{j+3}, V_{j+1}) go out one at a time through the block: all
+    // eight waves issuing theirs right after the barrier queue on the memory issue path. They
+    // are issued unconditionally (no branch splits the block): past the last tile the source
+    // offset points beyond the buffer resource, which reads zeros, into stages nothing reads.
+    constexpr int kFar = 0x40000000;             // past any (b, h) region (those stay below 2^31 bytes)
+    const int kofs = j + 3 < n ? (t_begin + j + 3) * BN * G::KROW : kFar;
+    const int vofs = j + 1 < n ? (t_begin + j + 1) * BN * 2 : kFar;
+    char* const kdst = kring + ((j + 3) % ST) * G::KBYTES;
+    char* const vdst = vring + ((j + 1) % ST) * G::VBYTES;
+    auto copy_at = [&](int k) {                  // copy c of KC + VC at step k = (c + 1) * CP_EVERY - 2
+      constexpr int NC = KC + VC, CP_EVERY = STEPS / NC;
+      static_assert(CP_EVERY >= 2 && NC * CP_EVERY <= STEPS, "copy spacing");
+      if ((k + 2) % CP_EVERY == 0 && (k + 2) / CP_EVERY <= NC) {
+        const int c = (k + 2) / CP_EVERY - 1;
+        if (c < KC) lds_copy16(krs, kofs + k_src(c), kdst + (c * NW + wave) * 1024);
+        else lds_copy16(vrs, vofs + v_src(c - KC), vdst + ((c - KC) * NW + wave) * 1024);
+      }
+    };
+    const int kst = STG >= 0 ? STG : j % ST;
+    const int vst = STG >= 0 ? (STG + 2) % ST : (j + 2) % ST;   // (j - 2) mod ST
+    const char* ks = kring + kst * G::KBYTES;
+    const char* vs = vring + vst * G::VBYTES;
+
+    // MFMA x of the iteration (x < NQK: QK step, else PV step) and its operand read
+    constexpr int RA = 4, RB = RA + 2;           // reads in flight ahead of their MFMA; ring size (two reads
+                                                 // are issued before the two MFMAs of a step)
+    [[maybe_unused]] bf16x8 op[RB];
+    auto has = [&](int x) { return x < NQK ? QK : PV; };
+    auto read = [&](int x) {
+      if (x < NQK) {
+        if constexpr (QK) op[x % RB] = k_op(ks, x / MT, x % MT);
+      } else {
+        if constexpr (PV) op[x % RB] = v_op(vs, (x - NQK) / DT, (x - NQK) % DT);
+      }
+    };
+    auto mfma = [&](int x) {
+      if (x < NQK) {
+        if constexpr (QK) {
+          const int s = x / MT, mt = x % MT;
+          sc[PAR][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[x % RB], bq[s], s == 0 ? f32x16{} : sc[PAR][mt],
+                                                                0, 0, 0);
+        }
+      } else {
+        if constexpr (PV) {
+          const int s = (x - NQK) / DT, dt = (x - NQK) % DT;
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[x % RB], pw[PAR][s], o[dt], 0, 0, 0);
+        }
+      }
+    };
+
+    // weights of tile j - 1 (scores in sc[PAR ^ 1]); pair p = elements 2p, 2p + 1; element i
+    // is accumulator (i / 8) >> 1, entry 8 ((i / 8) & 1) + i % 8, and goes to pw[i / 8][i % 8]
+    f32x16* const sw = sc[PAR ^ 1];
+    auto el = [](int i) { return 8 * ((i / 8) & 1) + i % 8; };
+    [[maybe_unused]] float rs = 0.f;
+    auto w_scale = [&](int pr) {                 // s c - m
+      if (pr < NPAIR) {
+        const int i = 2 * pr;
+        sw[(i / 8) >> 1][el(i)] = fmaf(sw[(i / 8) >> 1][el(i)], c2, nm_w);
+        sw[(i / 8) >> 1][el(i + 1)] = fmaf(sw[(i / 8) >> 1][el(i + 1)], c2, nm_w);
+      }
+    };
+    auto w_exp = [&](int pr) {
+      if (pr < NPAIR) {
+        const int i = 2 * pr;
+        sw[(i / 8) >> 1][el(i)] = fast_exp2(sw[(i / 8) >> 1][el(i)]);
+        sw[(i / 8) >> 1][el(i + 1)] = fast_exp2(sw[(i / 8) >> 1][el(i + 1)]);
+      }
+    };
+    auto w_pack = [&](int pr) {                  // bf16 pair; the row sum adds the rounded weights
+      if (pr < NPAIR) {
+        const int i = 2 * pr;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 pk = {static_cast<__bf16>(sw[(i / 8) >> 1][el(i)]),
+                           static_cast<__bf16>(sw[(i / 8) >> 1][el(i + 1)])};
+        const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, rs, false);
+        pw[PAR ^ 1][i / 8][i % 8] = pk[0];
+        pw[PAR ^ 1][i / 8][i % 8 + 1] = pk[1];
+      }
+    };
+
+    // maximum of tile j (scores in sc[PAR], complete after the first half): four independent
+    // partial maxima over MAXSTEPS steps of the second half
+    constexpr int MAX0 = HALF + 1, MAXSTEPS = HALF - 2;   // leave the first step for the MFMA latency
+    constexpr int NCH = 4, PER = NEL / NCH;
+    static_assert(NCH * PER == NEL, "max split");
+    [[maybe_unused]] float part[NCH];
+    [[maybe_unused]] const int key0 = (t_begin + j) * BN;
+    auto sm_max = [&](int st) {                  // st = 0 .. MAXSTEPS - 1
+      f32x16* const sm = sc[PAR];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        // chain c folds its elements c*PER .. c*PER+PER-1 in groups over the steps
+        const int lo = c * PER + (st * PER) / MAXSTEPS, hi = c * PER + ((st + 1) * PER) / MAXSTEPS;
+#pragma unroll
+        for (int i = lo; i < hi; ++i) {
+          if constexpr (TAIL) {
+            const int kk = key0 + 32 * (i / 16) + 16 * ((i / 8) & 1) + 8 * g + i % 8;
+            if (kk >= n_keys) sm[(i / 8) >> 1][el(i)] = -__builtin_inff();
+          }
+          const float x = sm[(i / 8) >> 1][el(i)];
+          part[c] = (i == c * PER) ? x : __builtin_fmaxf(part[c], x);
+        }
+      }
+    };
+
+    if constexpr (SM) { w_scale(0); w_scale(1); w_exp(0); }
+#pragma unroll
+    for (int x = 0; x < RA; ++x)
+      if (has(x)) read(x);
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+      const int x0 = 2 * k, x1 = 2 * k + 1;
+      if (x0 + RA < 2 * STEPS && has(x0 + RA)) read(x0 + RA);
+      if (x1 + RA < 2 * STEPS && has(x1 + RA)) read(x1 + RA);
+      if (has(x0)) mfma(x0);
+      copy_at(k);
+      if constexpr (SM) w_scale(k + 2);
+      if constexpr (QK) {
+        if (k >= MAX0 && k < MAX0 + MAXSTEPS) sm_max(k - MAX0);
+      }
+      if (has(x1)) mfma(x1);
+      if constexpr (SM) { w_exp(k + 1); w_pack(k); }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the block's results are produced inside it (without this the compiler sinks the
+    // softmax past the branches below, into the next iteration)
+    if constexpr (SM) {
+#pragma unroll
+      for (int s2 = 0; s2 < PSTEPS; ++s2) asm volatile("" : "+v"(pw[PAR ^ 1][s2]));
+      asm volatile("" : "+v"(rs));
+    }
+    if constexpr (QK) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(part[c]));
+    }
+    if constexpr (SM) {
+      l = fmaf(l, alpha_prev, rs);
+      if (raise_prev) {                          // rare: tile j-1 moved the reference by more than 2^8
+#pragma unroll
+        for (int d = 0; d < DT; ++d) o[d] *= alpha_prev;
+      }
+    }
+    if constexpr (QK) {
+      float mx = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+      mx = fmaxf(mx, xor32(mx)) * c2;
+      const float m_new = mx > m + kRescaleThreshold ? mx : m;
+      raise_prev = __any(m_new != m);
+      alpha_prev = fast_exp2(m - m_new);
+      m = m_new;
+      nm_w = -m_new;
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using SR = std::integral_constant<int, -1>;   // stage computed at run time
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  // prologue copies: K_0 (iteration -3), K_1 (-2), K_2 and V_0 (-1)
+  issue_k(0);
+  if (n > 1) issue_k(1);
+  if (n > 2) issue_k(2);
+  issue_v(0);
+  const bool tail = tail_tile == n - 1;          // the last tile is ragged
+  if (n == 1) {
+    if (tail) iteration(0, S0{}, P0{}, T_{}, F_{}, F_{}, T_{});
+    else iteration(0, S0{}, P0{}, T_{}, F_{}, F_{}, F_{});
+    iteration(1, S1{}, P1{}, F_{}, T_{}, F_{}, F_{});
+    iteration(2, S2{}, P0{}, F_{}, F_{}, T_{}, F_{});
+  } else {
+    iteration(0, S0{}, P0{}, T_{}, F_{}, F_{}, F_{});
+    int j = 1;
+    if (n > 2) {
+      iteration(1, S1{}, P1{}, T_{}, T_{}, F_{}, F_{});
+      // full iterations j = 2 .. n - 2, four at a time (stages 2, 3, 0, 1)
+      j = 2;
+      for (; j + 3 < n - 1; j += 4) {
+        iteration(j, S2{}, P0{}, T_{}, T_{}, T_{}, F_{});
+        iteration(j + 1, S3{}, P1{}, T_{}, T_{}, T_{}, F_{});
+        iteration(j + 2, S0{}, P0{}, T_{}, T_{}, T_{}, F_{});
+        iteration(j + 3, S1{}, P1{}, T_{}, T_{}, T_{}, F_{});
+      }
+      if (j < n - 1) { iteration(j, S2{}, P0{}, T_{}, T_{}, T_{}, F_{}); ++j; }
+      if (j < n - 1) { iteration(j, S3{}, P1{}, T_{}, T_{}, T_{}, F_{}); ++j; }
+      if (j < n - 1) { iteration(j, S0{}, P0{}, T_{}, T_{}, T_{}, F_{}); ++j; }
+    }
+    // j = n - 1: the last QK (masked when ragged); j = n: weights of the last tile; j = n + 1
+    const bool pv = n > 2;                       // PV(n - 3) exists at j = n - 1
+    if ((n - 1) & 1) {
+      if (pv) {
+        if (tail) iteration(n - 1, SR{}, P1{}, T_{}, T_{}, T_{}, T_{});
+        else iteration(n - 1, SR{}, P1{}, T_{}, T_{}, T_{}, F_{});
+      } else {
+        if (tail) iteration(n - 1, SR{}, P1{}, T_{}, T_{}, F_{}, T_{});
+        else iteration(n - 1, SR{}, P1{}, T_{}, T_{}, F_{}, F_{});
+      }
+      iteration(n, SR{}, P0{}, F_{}, T_{}, T_{}, F_{});
+      iteration(n + 1, SR{}, P1{}, F_{}, F_{}, T_{}, F_{});
+    } else {
+      if (tail) iteration(n - 1, SR{}, P0{}, T_{}, T_{}, T_{}, T_{});
+      else iteration(n - 1, SR{}, P0{}, T_{}, T_{}, T_{}, F_{});
+      iteration(n, SR{}, P1{}, F_{}, T_{}, T_{}, F_{});
+      iteration(n + 1, SR{}, P0{}, F_{}, F_{}, T_{}, F_{});
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  const float l_tot = l + xor32(l);
+  const float inv = 1.f / l_tot;
+  const float lse2 = m + __log2f(l_tot);
+  if (q >= q_end) return;
+  const int b = bh / p.H, h = bh - b * p.H;
+  if (mode == kPpFinal) {
+    __bf16* dst = static_cast<__bf16*>(bs.out) + ((static_cast<size_t>(b) * bs.rows + q) * p.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(o[dt][4 * jj + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * jj + 4 * g) = v;
+      }
+    if (bs.lse != nullptr && g == 0) bs.lse[static_cast<size_t>(bh) * bs.rows + q] = lse2 * kLn2;
+  } else {
+    const size_t row = (static_cast<size_t>(slot) * p.B * p.H + bh) * p.Nc + q;
+    float* dst = p.part_o + row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * jj + 4 * g) =
+            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                        o[dt][4 * jj + 3] * inv);
+    if (g == 0) p.part_lse[row] = lse2;
+  }
+}
+
+// Pipelined kernel driver: one workgroup per (b*h, split, q-tile).
+template <int D>
+__device__ __forceinline__ void chunk_attention_pipe_body(const AttnParams& p) {
+  __shared__ __attribute__((aligned(1024))) char smem[PipeSmem<D>::BYTES];
+  const int G = p.B * p.H * p.q_tiles * p.kv_splits;
+  const int w = xcd_remap(blockIdx.x, G);
+  const int T = p.key_tiles;
+  const int qt = w % p.q_tiles;
+  const int rest = w / p.q_tiles;
+  const int split = rest % p.kv_splits;
+  const int bh = rest / p.kv_splits;
+  const int t0 = static_cast<int>((static_cast<int64_t>(split) * T) / p.kv_splits);
+  const int t1 = static_cast<int>((static_cast<int64_t>(split + 1) * T) / p.kv_splits);
+  pipe_segment<D>(p, bases_shared(p), smem, bh, qt * (8 * 32), p.Nc, t0, t1,
+                  p.kv_splits == 1 ? kPpFinal : kPpSplit, split);
+}
+
 __global__ __launch_bounds__(kThreads, 2) void chunk_attention_bf16_d128(AttnParams p) {
   chunk_attention_bf16_body<128, 4, 1, 2>(p);
 }
@@ -958,6 +1360,10 @@ __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_pp(
 
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d64_pp(AttnParams p) {
   chunk_attention_pp_body<64, false, false>(p);
+}
+
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_attention_bf16_d128_pipe(AttnParams p) {
+  chunk_attention_pipe_body<128>(p);
 }
 
 // moving-buffer attend: query groups with their own key ranges
@@ -1191,7 +1597,9 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
     if (p.n_groups > 0) {
       hipLaunchKernelGGL(p.D == 128 ? chunk_attention_bf16_d128_ppg : chunk_attention_bf16_d64_ppg, dim3(n_work),
                          dim3(2 * kThreads), 0, st, p);
-    } else if (p.variant == 3) {
+    } else if (p.variant == 4 && p.D == 128) {
+      hipLaunchKernelGGL(chunk_attention_bf16_d128_pipe, dim3(n_work), dim3(2 * kThreads), 0, st, p);
+    } else if (p.variant == 3 || p.variant == 4) {
       hipLaunchKernelGGL(p.D == 128 ? chunk_attention_bf16_d128_pp : chunk_attention_bf16_d64_pp, dim3(n_work),
                          dim3(2 * kThreads), 0, st, p);
     } else {

@@ -744,7 +744,7 @@ sa_status sa_stream_set_option(sa_stream* s, int32_t option, int64_t value) {
       s->kv_splits_opt = static_cast<int32_t>(value);
       return SA_OK;
     case SA_OPT_ATTN_VARIANT:
-      if (value < 0 || value > 3 || (s->d.dtype == SA_FP8 && value != 0 && value != 3))
+      if (value < 0 || value > 4 || (s->d.dtype == SA_FP8 && value != 0 && value != 3))
         return SA_ERR_INVALID_ARGUMENT;
       s->variant_opt = static_cast<int32_t>(value);
       return SA_OK;

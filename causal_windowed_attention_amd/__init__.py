@@ -177,8 +177,17 @@ def sa_buffer_plan(handle, n_chunks: int, flags: int = 0):
 
 
 def sa_batch_attend(handles, qs, ks, vs, outs, lses=None, stream=None) -> None:
-    """Ragged batch: one attend per handle (each at its own state), one attention launch."""
+    """Ragged batch: one attend per handle (each at its own state), one attention launch.
+    Entries given as Stream objects have their tensors checked (shape, dtype, device,
+    contiguity) before the call; raw handles pass pointers through (planning handles
+    ignore them)."""
     n = len(handles)
+    for i, hd in enumerate(handles):
+        if isinstance(hd, Stream):
+            for xs, name in ((qs, "q"), (ks, "k"), (vs, "v"), (outs, "out")):
+                hd._check_tensor(None if xs is None else xs[i], hd.Nc, f"{name}[{i}]")
+            if lses is not None:
+                hd._check_lse(lses[i], hd.Nc, f"lse[{i}]")
     arr = lambda xs: (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in xs]) if xs is not None else None
     h = (ctypes.c_void_p * max(n, 1))(*[x.handle if isinstance(x, Stream) else x for x in handles])
     _check(L.load().sa_batch_attend(n, h, arr(qs), arr(ks), arr(vs), arr(outs), arr(lses),
@@ -214,8 +223,15 @@ def gdn_forward(q, k, v, alpha, beta, state=None, out=None, state_out=None, work
         if tuple(t.shape) != (B, H, N) or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{n}: expected contiguous float32 CUDA [B, H, N]")
     for t, n in ((state, "state"), (state_out, "state_out")):
-        if t is not None and (tuple(t.shape) != (B, H, D, D) or t.dtype != torch.float32 or not t.is_contiguous()):
-            raise ValueError(f"{n}: expected contiguous float32 [B, H, D, D]")
+        if t is not None and (tuple(t.shape) != (B, H, D, D) or t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{n}: expected contiguous float32 [B, H, D, D] on {q.device}")
+    if out is not None and (tuple(out.shape) != (B, N, H, D) or out.dtype != torch.bfloat16
+                            or not out.is_contiguous() or out.device != q.device):
+        raise ValueError(f"out: expected contiguous bf16 [B, N, H, D] on {q.device}")
+    for t, n in ((k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        if t.device != q.device:
+            raise ValueError(f"{n}: expected on {q.device}, got {t.device}")
     if out is None:
         out = torch.empty_like(v)
     if state_out is None:
@@ -225,6 +241,8 @@ def gdn_forward(q, k, v, alpha, beta, state=None, out=None, state_out=None, work
         raise SaError(L.SA_ERR_UNSUPPORTED, "gdn_forward: unsupported sizes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace: expected contiguous memory on {q.device}")
     sa_gdn_forward(B, N, H, D, q, k, v, alpha, beta, state, state_out, out, workspace, workspace.numel(), stream)
     return out, state_out
 
@@ -255,13 +273,29 @@ class Stream:
         return {SA_F32: torch.float32, SA_BF16: torch.bfloat16, SA_FP8: torch.float8_e4m3fn}[self.cfg.dtype]
 
     def _check_tensor(self, t, n_tokens, name):
-        if self.workspace is None and t is None:
-            return
+        """Shape, dtype, contiguity and (for a device handle) the device of an input or output.
+        A planning handle accepts None (it ignores data pointers)."""
+        if t is None:
+            if self.workspace is None:
+                return
+            raise ValueError(f"{name}: a tensor is required")
         shape = (self.cfg.batch, n_tokens, self.cfg.heads, self.cfg.head_dim)
+        where = self.workspace.device if self.workspace is not None else None
         if tuple(t.shape) != shape or t.dtype != self._torch_dtype() or not t.is_contiguous() \
-                or t.device != self.workspace.device:
-            raise ValueError(f"{name}: expected contiguous {self._torch_dtype()} {shape} on "
-                             f"{self.workspace.device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+                or (where is not None and t.device != where):
+            raise ValueError(f"{name}: expected contiguous {self._torch_dtype()} {shape}"
+                             + (f" on {where}" if where is not None else "")
+                             + f", got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+    def _check_lse(self, lse, rows, name="lse"):
+        if lse is None:
+            return
+        import torch
+        where = self.workspace.device if self.workspace is not None else None
+        if tuple(lse.shape) != (self.cfg.batch, self.cfg.heads, rows) or lse.dtype != torch.float32 \
+                or not lse.is_contiguous() or (where is not None and lse.device != where):
+            raise ValueError(f"{name}: expected contiguous float32 [B, H, {rows}]"
+                             + (f" on {where}" if where is not None else ""))
 
     def new_output(self):
         import torch
@@ -273,11 +307,7 @@ class Stream:
             out = self.new_output()
         for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
             self._check_tensor(t, self.Nc, n)
-        if lse is not None:
-            import torch
-            if tuple(lse.shape) != (self.cfg.batch, self.cfg.heads, self.Nc) or \
-                    lse.dtype != torch.float32 or not lse.is_contiguous():
-                raise ValueError("lse: expected contiguous float32 [B, H, Nc]")
+        self._check_lse(lse, self.Nc)
         sa_chunk_attend(self.handle, q, k, v, out, lse, stream)
         return out
 
@@ -295,11 +325,7 @@ class Stream:
                               dtype=self._torch_dtype(), device=self.workspace.device)
         for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
             self._check_tensor(t, rows, n)
-        if lse is not None:
-            import torch
-            if tuple(lse.shape) != (self.cfg.batch, self.cfg.heads, rows) or \
-                    lse.dtype != torch.float32 or not lse.is_contiguous():
-                raise ValueError("lse: expected contiguous float32 [B, H, n*Nc]")
+        self._check_lse(lse, rows)
         sa_buffer_attend(self.handle, q, k, v, n_chunks, out, lse, stream,
                          L.SA_BUFFER_STEPS if steps else 0)
         return out

@@ -477,3 +477,42 @@ def test_c_consumer_builds_and_validates_before_any_device_call():
     r = subprocess.run([b.C_DEMO, "/nonexistent", "1", "2", "96", "4", "4", "2", "1", "2", "3"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "unsupported" in r.stderr.lower(), r.stderr
+
+
+def test_binding_rejects_wrong_tensors_before_any_call():
+    """The binding checks shape, dtype and contiguity (and the device, on device handles)
+    before calling the library; a planning handle shows the shape and dtype checks on the CPU."""
+    import torch
+    cfg = _cfg()
+    s = cwa.Stream(cfg, planning=True)
+    B, H, D = cfg.batch, cfg.heads, cfg.head_dim
+    nc = cfg.frames_per_chunk * cfg.frame_h * cfg.frame_w
+    good = torch.zeros((B, nc, H, D), dtype=torch.bfloat16)
+    bad_shape = torch.zeros((B, nc + 1, H, D), dtype=torch.bfloat16)
+    bad_dtype = torch.zeros((B, nc, H, D), dtype=torch.float32)
+    strided = torch.zeros((B, nc, H, 2 * D), dtype=torch.bfloat16)[..., :D]
+    before = s.query()
+    for bad in (bad_shape, bad_dtype, strided):
+        with pytest.raises(ValueError):
+            s.chunk_attend(good, bad, good, out=good)
+        with pytest.raises(ValueError):
+            s.kv_append(bad, good)
+    with pytest.raises(ValueError):
+        s.chunk_attend(good, good, good, out=good, lse=torch.zeros((B, H, nc + 1), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        s.chunk_attend(good, good, good, out=good, lse=torch.zeros((B, H, nc), dtype=torch.float64))
+    assert s.query() == before                   # nothing reached the library
+    s2 = cwa.Stream(cfg, planning=True)
+    with pytest.raises(ValueError):
+        cwa.sa_batch_attend([s, s2], [good, good], [good, bad_shape], [good, good], [good, good])
+    with pytest.raises(ValueError):
+        cwa.sa_batch_attend([s, s2], [good, good], [good, good], [good, good], [good, good],
+                            lses=[None, torch.zeros((B, H, 3), dtype=torch.float32)])
+    assert s.query() == before and s2.query()["n_appends"] == 0
+    # gdn_forward: host tensors are refused before any call
+    q = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16)
+    a = torch.ones((1, 2, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        cwa.gdn_forward(q, q, q, a, a)
+    s.close()
+    s2.close()

@@ -348,17 +348,18 @@ def bench_configs(torch, cwa, synth, steps=20):
 
 
 def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), steps=20, deadline_ms=1.0,
-                calls=200):
+                model_calls=60, calls=1000, margin=0.10):
     """Ragged batch: n steady-state streams (each its own cache and position) attended in one
     launch; per n the call time, attended tokens/s and the attention kernel's TFLOP/s.
 
-    Then a deadline-driven choice of n: a least-squares latency model ms(n) = a + b*waves(n)
-    over the measured sizes, waves(n) = ceil(n * workgroups per stream / CUs) (one 256-row
-    workgroup per CU at a time), gives the largest n whose predicted call time meets
-    deadline_ms; that
-    batch runs `calls` times, each call timed by its own events, and the miss rate (calls over
-    the deadline) and the mean jitter (mean |difference| of consecutive call times) are
-    reported."""
+    Then a deadline-driven choice of n (Stream-Batch: adapt the batch to the load without
+    breaking the latency bound). The latency model is measured on the running box at start-up:
+    per n, model_calls calls each timed by its own events, and the model is their p99 (a tail
+    quantile, not a mean fit). The chosen n is the largest whose p99 times (1 + margin) meets the
+    deadline; margin covers drift between the model's measurement and the run (boxes differ by
+    up to 10 %). The chosen batch then runs `calls` calls, each timed by its own events; the
+    miss rate (calls over the deadline), p50 / p99 / max and the mean jitter (mean |difference|
+    of consecutive call times) are reported beside the prediction."""
     import numpy as np
     w = synth.WORKLOADS[name]
     cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
@@ -372,7 +373,19 @@ def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), st
             s.kv_append(k, v)
         q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in synth.chunk_qkv(w, 900 + i))
         streams.append(s); qs.append(q); ks.append(k); vs.append(v); outs.append(torch.empty_like(q))
+
+    def timed_calls(n, count):
+        args = (streams[:n], qs[:n], ks[:n], vs[:n], outs[:n])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+        for a, b in ev:
+            a.record()
+            cwa.sa_batch_attend(*args)
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
     res = {}
+    model = {}
     for n in sizes:
         args = (streams[:n], qs[:n], ks[:n], vs[:n], outs[:n])
         for _ in range(3):
@@ -387,35 +400,32 @@ def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), st
         call_ms = a.elapsed_time(b) / steps
         streams[0].set_option(cwa.SA_OPT_PROFILE, 1)
         streams[0].profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+        streams[0].profile_read(cwa.SA_K_ROPE_APPLY, reset=True)
         for _ in range(steps):
             cwa.sa_batch_attend(*args)
         attn_ms, na = streams[0].profile_read(cwa.SA_K_CHUNK_ATTENTION, reset=True)
+        rope_ms, nr = streams[0].profile_read(cwa.SA_K_ROPE_APPLY, reset=True)
         streams[0].set_option(cwa.SA_OPT_PROFILE, 0)
         attn_ms /= max(na, 1)
+        t = timed_calls(n, model_calls)
+        model[n] = {"p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)),
+                    "max_ms": float(t.max())}
         flops = sum(4.0 * w.batch * w.heads * w.head_dim * nc * st.query()["visible_keys"] for st in streams[:n])
         tf = flops / (attn_ms * 1e-3) / 1e12
         res[n] = {"ms_per_call": call_ms, "tokens_per_s": n * w.batch * nc / (call_ms * 1e-3),
-                  "attention_ms": attn_ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wg = w.batch * w.heads * streams[0].query()["last_q_tiles"]      # workgroups per stream
-    waves = lambda n: -(-n * wg // cus)
-    xs = np.array([waves(n) for n in sizes], dtype=np.float64)
-    ys = np.array([res[n]["ms_per_call"] for n in sizes])
-    slope, icept = np.polyfit(xs, ys, 1)
-    fits = [n for n in range(1, max(sizes) + 1) if icept + slope * waves(n) <= deadline_ms]
-    n = max(fits) if fits else 1
-    args = (streams[:n], qs[:n], ks[:n], vs[:n], outs[:n])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-    for a, b in ev:
-        a.record()
-        cwa.sa_batch_attend(*args)
-        b.record()
-    torch.cuda.synchronize()
-    t = np.array([a.elapsed_time(b) for a, b in ev])
-    sched = {"deadline_ms_per_call": deadline_ms,
-             "model_ms": {"intercept": icept, "per_wave": slope, "workgroups_per_stream": wg, "cus": cus},
-             "chosen_streams": n, "predicted_ms": icept + slope * waves(n), "calls": calls,
-             "p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)),
+                  "attention_ms": attn_ms, "rope_launches_per_call": nr / max(steps, 1),
+                  "rope_ms": rope_ms / max(nr, 1), "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+                  "call_p50_ms": model[n]["p50_ms"], "call_p99_ms": model[n]["p99_ms"]}
+    fits = [n for n in sizes if model[n]["p99_ms"] * (1.0 + margin) <= deadline_ms]
+    # among the sizes that meet the deadline, the one with the highest throughput (a size that
+    # leaves the last wave of workgroups mostly empty can be slower per token than a smaller one)
+    n = max(fits, key=lambda m: m / model[m]["p50_ms"]) if fits else min(sizes)
+    t = timed_calls(n, calls)
+    sched = {"deadline_ms_per_call": deadline_ms, "model": "p99 of %d calls per size, measured at start-up" % model_calls,
+             "margin": margin, "model_p99_ms": {k: v["p99_ms"] for k, v in model.items()},
+             "chosen_streams": n, "deadline_met_by_model": bool(fits),
+             "predicted_p99_ms": model[n]["p99_ms"], "calls": calls,
+             "p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)), "max_ms": float(t.max()),
              "miss_rate": float(np.mean(t > deadline_ms)), "mean_jitter_ms": float(np.mean(np.abs(np.diff(t)))),
              "tokens_per_s": n * w.batch * nc / (float(np.mean(t)) * 1e-3)}
     for s in streams:
@@ -484,6 +494,21 @@ def main():
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
     value = w.batch * nc * args.steps / dt
+
+    # ---- the same step committing the staged K/V (sa_kv_append(NULL, NULL): the attend
+    # already wrote the rotated K and V^T into the slot the commit makes visible) ---------
+    def step_zero_copy(i):
+        q, k, v = pool[i % len(pool)]
+        s.chunk_attend(q, k, v, out=out)
+        s.kv_append(None, None)
+    for i in range(args.warmup):
+        step_zero_copy(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_zero_copy(i)
+    torch.cuda.synchronize()
+    dt_zc = time.perf_counter() - t0
 
     # ---- per-step GPU time distribution (events on the stream the library uses) ---
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
@@ -584,6 +609,10 @@ def main():
             "rope_refresh": gbs(2 * w.batch * w.heads * w.window_chunks * nc * d_t * 2,
                                 kern["rope_refresh"]) if "rope_refresh" in kern else None,
         },
+        "step_zero_copy_commit": {"ms_per_step": dt_zc * 1e3 / args.steps,
+                                  "tokens_per_s": w.batch * nc * args.steps / dt_zc,
+                                  "what": "attend + sa_kv_append(NULL, NULL): the staged K/V committed "
+                                          "without device work"},
         "attend_ms": attend_ms,
         "attend_tokens_per_s": w.batch * nc / (attend_ms * 1e-3),
         "pct_bf16_peak_attend": flops / (attend_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

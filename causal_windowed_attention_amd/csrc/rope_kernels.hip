@@ -50,8 +50,8 @@ template <> __device__ __forceinline__ fp8e4m3 from_f<fp8e4m3>(float x) {
 }
 
 // (cos, sin) of the pair starting at even channel ch of a token at (frame, y, x).
-__device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const RopeWriteParams& p, int ch,
-                                          int f, int y, int x) {
+template <typename P>
+__device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const P& p, int ch, int f, int y, int x) {
   if (ch < p.dt) return s_tcs[f * (p.dt >> 1) + (ch >> 1)];
   ch -= p.dt;
   if (ch < p.dh) return p.h_cs[y * (p.dh >> 1) + (ch >> 1)];
@@ -117,15 +117,21 @@ __device__ __forceinline__ void transpose_block(const uint4 (&in)[16 / sizeof(T)
   }
 }
 
-// One block: 64 tokens of head blockIdx.y of stream blockIdx.z.
+// One block: 64 tokens of head blockIdx.y of batch entry b.
 //  * K (and Q): thread (tid % vpt) owns one 16-byte channel vector of tokens
 //    tid / vpt + j * (256 / vpt); all its loads are issued before any store.
 //  * V: thread owns a VN x VN (tokens x channels) block, transposes it in
 //    registers and stores VN 16-byte rows of V^T; lanes with consecutive token
 //    groups of one channel group write 128 contiguous bytes per channel row.
-// TI: input element type; TS: cache (storage) element type.
-template <typename TI, typename TS, bool HAS_Q>
-__device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
+// Every global load is issued before the block sets up its position tables in LDS, so the
+// table set-up and its barrier run under the load latency.
+// TI: input element type; TS: cache (storage) element type. P holds the geometry (a
+// RopeWriteParams or RopeBatchParams); the target pointers are passed apart; fill_tcs(i)
+// gives temporal (cos, sin) entry i = frame * d_t/2 + pair.
+template <typename TI, typename TS, bool HAS_Q, typename P, typename FillT>
+__device__ __forceinline__ void rope_write_core(const P& p, int b, const void* q_in, const void* k_in,
+                                                const void* v_in, void* qrot, void* kcache, void* vtcache,
+                                                int row0, int q_row0, int in_tok0, FillT fill_tcs) {
   using T = TI;
   using VecS = VecN<TS, 16 / sizeof(TI)>;
   constexpr int VN = 16 / sizeof(T);             // elements per 16-byte input vector
@@ -135,28 +141,17 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
 
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * kTileTokens;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int ntab = p.n_frames * (p.dt >> 1);
-  for (int i = tid; i < ntab; i += kThreads) s_tcs[i] = p.t_cs[i];
-  if (tid < kTileTokens) {
-    const int n = min(n0 + tid, p.n_tokens - 1);
-    const int hw = p.Hf * p.Wf;
-    const int f = n / hw, rem = n - f * hw, y = rem / p.Wf;
-    s_fyx[tid][0] = f;
-    s_fyx[tid][1] = y;
-    s_fyx[tid][2] = rem - y * p.Wf;
-  }
-  __syncthreads();
+  const int h = blockIdx.y;
 
   const size_t bh = static_cast<size_t>(b) * p.H + h;
-  const T* __restrict__ kin = static_cast<const T*>(p.k);
-  const T* __restrict__ qin = static_cast<const T*>(p.q);
-  const T* __restrict__ vin = static_cast<const T*>(p.v);
-  TS* __restrict__ kc = static_cast<TS*>(p.kcache) + bh * p.k_bh_stride;
-  TS* __restrict__ qo = static_cast<TS*>(p.qrot) + (bh * p.q_rows + p.q_row0) * p.D;
-  TS* __restrict__ vt = static_cast<TS*>(p.vtcache) + bh * p.vt_bh_stride + p.row0 + n0;
+  const T* __restrict__ kin = static_cast<const T*>(k_in);
+  const T* __restrict__ qin = static_cast<const T*>(q_in);
+  const T* __restrict__ vin = static_cast<const T*>(v_in);
+  TS* __restrict__ kc = static_cast<TS*>(kcache) + bh * p.k_bh_stride;
+  TS* __restrict__ qo = static_cast<TS*>(qrot) + (bh * p.q_rows + q_row0) * p.D;
+  TS* __restrict__ vt = static_cast<TS*>(vtcache) + bh * p.vt_bh_stride + row0 + n0;
   auto in_off = [&](int n, int c) {
-    return ((static_cast<size_t>(b) * p.in_tokens + p.in_tok0 + n) * p.H + h) * p.D + c;
+    return ((static_cast<size_t>(b) * p.in_tokens + in_tok0 + n) * p.H + h) * p.D + c;
   };
 
   // ---- issue every load first: V blocks, then K (and Q) vectors ---------------
@@ -189,6 +184,19 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
     }
   }
 
+  // ---- position tables (under the load latency) ------------------------------
+  const int ntab = p.n_frames * (p.dt >> 1);
+  for (int i = tid; i < ntab; i += kThreads) s_tcs[i] = fill_tcs(i);
+  if (tid < kTileTokens) {
+    const int n = min(n0 + tid, p.n_tokens - 1);
+    const int hw = p.Hf * p.Wf;
+    const int f = n / hw, rem = n - f * hw, y = rem / p.Wf;
+    s_fyx[tid][0] = f;
+    s_fyx[tid][1] = y;
+    s_fyx[tid][2] = rem - y * p.Wf;
+  }
+  __syncthreads();
+
   // ---- K (and Q): rotate 16-byte channel vectors ----------------------------
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
@@ -197,7 +205,7 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
       float2 cs[VN / 2];
 #pragma unroll
       for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, p, c0 + 2 * e, s_fyx[tl][0], s_fyx[tl][1], s_fyx[tl][2]);
-      *reinterpret_cast<VecS*>(kc + static_cast<size_t>(p.row0 + n) * p.D + c0) = rotate<TI, TS>(kv[j], cs);
+      *reinterpret_cast<VecS*>(kc + static_cast<size_t>(row0 + n) * p.D + c0) = rotate<TI, TS>(kv[j], cs);
       // fp8 queries are stored times q_scale (the base-2 softmax scale brought into [1, 2))
       if constexpr (HAS_Q)
         *reinterpret_cast<VecS*>(qo + static_cast<size_t>(n) * p.D + c0) =
@@ -206,7 +214,7 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
   }
 
   // ---- V: VN x VN register transposes straight into V^T ---------------------
-  const bool vec_ok = (p.row0 % VN) == 0;        // vector-aligned V^T rows
+  const bool vec_ok = (row0 % VN) == 0;          // vector-aligned V^T rows
 #pragma unroll
   for (int r = 0; r < MAXB; ++r) {
     const int blk = tid + r * kThreads;
@@ -228,6 +236,28 @@ __device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
   }
 }
 
+// Single-stream writes: batch entry blockIdx.z, temporal table from the kernel arguments.
+template <typename TI, typename TS, bool HAS_Q>
+__device__ __forceinline__ void rope_write_body(const RopeWriteParams& p) {
+  rope_write_core<TI, TS, HAS_Q>(p, blockIdx.z, p.q, p.k, p.v, p.qrot, p.kcache, p.vtcache, p.row0, p.q_row0,
+                                 p.in_tok0, [&](int i) { return p.t_cs[i]; });
+}
+
+// Ragged batch: blockIdx.z = stream e * B + b; stream e's temporal (cos, sin) from fp64 on the
+// device, (t0[e] + frame) * theta_t[pair] rounded to fp32 (the same angle the host tables use).
+template <typename TI, typename TS>
+__global__ __launch_bounds__(kThreads) void rope_apply_batch(RopeBatchParams p) {
+  const int e = blockIdx.z / p.B, b = blockIdx.z - (blockIdx.z / p.B) * p.B;
+  const int np = p.dt >> 1;
+  const int t0 = p.t0[e];
+  rope_write_core<TI, TS, true>(p, b, p.q[e], p.k[e], p.v[e], p.qrot[e], p.kcache[e], p.vtcache[e], p.row0[e], 0, 0,
+                                [&](int i) {
+                                  const int f = i / np, j = i - f * np;
+                                  const double a = static_cast<double>(t0 + f) * p.theta_t[j];
+                                  return make_float2(static_cast<float>(cos(a)), static_cast<float>(sin(a)));
+                                });
+}
+
 template <typename TI, typename TS>
 __global__ __launch_bounds__(kThreads) void rope_apply(RopeWriteParams p) {
   rope_write_body<TI, TS, true>(p);
@@ -243,26 +273,59 @@ __global__ __launch_bounds__(kThreads) void sink_update(RopeWriteParams p) {
   rope_write_body<TI, TS, false>(p);
 }
 
-// One thread per (row, temporal pair) of one slot of one (b, h).
+// Refresh items: 16-byte vectors of the rows' temporal segments (channels [0, d_t)) of
+// every target slot of one (b, h) = blockIdx.z; consecutive items cover one row's segment,
+// then the next row. A thread takes kRefreshPerThread items a block apart (all loads first);
+// the last vector of a segment may reach into the h channels, which are written back as read.
+constexpr int kRefreshPerThread = 4;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rope_refresh(RefreshParams p) {
+  constexpr int VN = 16 / sizeof(T);
+  constexpr int R = kRefreshPerThread;
   __shared__ float2 s_cs[kMaxRefreshPairs];
   const int np = p.dt >> 1;
+  const int nvec = (p.dt + VN - 1) / VN;         // vectors per row segment
+  const int64_t items = static_cast<int64_t>(p.n_slot) * p.Nc * nvec;
+  T* const base = static_cast<T*>(p.kcache) + static_cast<size_t>(blockIdx.z) * p.k_bh_stride;
+  T* e[R];
+  int vv[R];
+  Vec16<T> in[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * R + k) * kThreads + threadIdx.x;
+    e[k] = nullptr;
+    vv[k] = 0;
+    if (i < items) {
+      const int v = static_cast<int>(i % nvec);
+      const int64_t r = i / nvec;
+      const int slot = static_cast<int>(r / p.Nc), row = static_cast<int>(r - static_cast<int64_t>(slot) * p.Nc);
+      e[k] = base + static_cast<size_t>(p.slot_row0[slot] + row) * p.D + v * VN;
+      vv[k] = v;
+      in[k] = *reinterpret_cast<const Vec16<T>*>(e[k]);
+    }
+  }
   if (threadIdx.x < np) s_cs[threadIdx.x] = p.cs[threadIdx.x];
   __syncthreads();
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= static_cast<int64_t>(p.Nc) * np) return;
-  const int row = static_cast<int>(i / np), j = static_cast<int>(i - static_cast<int64_t>(row) * np);
-  T* e = static_cast<T*>(p.kcache) + static_cast<size_t>(blockIdx.z) * p.k_bh_stride +
-         static_cast<size_t>(p.slot_row0[blockIdx.y] + row) * p.D + 2 * j;
-  struct alignas(2 * sizeof(T)) Pair { T a, b; };
-  const Pair in = *reinterpret_cast<const Pair*>(e);
-  const float u0 = to_f(in.a), u1 = to_f(in.b);
-  const float2 cs = s_cs[j];
-  Pair out;
-  out.a = from_f<T>(u0 * cs.x - u1 * cs.y);
-  out.b = from_f<T>(u0 * cs.y + u1 * cs.x);
-  *reinterpret_cast<Pair*>(e) = out;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (e[k] == nullptr) continue;
+    VecN<T, VN> out;
+#pragma unroll
+    for (int c = 0; c < VN / 2; ++c) {
+      const int j = vv[k] * (VN / 2) + c;        // temporal pair index
+      const float u0 = to_f(in[k].e[2 * c]), u1 = to_f(in[k].e[2 * c + 1]);
+      if (j < np) {
+        const float2 cs = s_cs[j];
+        out.e[2 * c] = from_f<T>(u0 * cs.x - u1 * cs.y);
+        out.e[2 * c + 1] = from_f<T>(u0 * cs.y + u1 * cs.x);
+      } else {
+        out.e[2 * c] = in[k].e[2 * c];
+        out.e[2 * c + 1] = in[k].e[2 * c + 1];
+      }
+    }
+    *reinterpret_cast<VecN<T, VN>*>(e[k]) = out;
+  }
 }
 
 }  // namespace
@@ -283,10 +346,21 @@ SA_WRITE_LAUNCHER(launch_kv_append, kv_ring_append)
 SA_WRITE_LAUNCHER(launch_sink_update, sink_update)
 #undef SA_WRITE_LAUNCHER
 
+hipError_t launch_rope_apply_batch(const RopeBatchParams& p, int dtype, hipStream_t st) {
+  if (p.n_tokens <= 0 || p.n <= 0) return hipSuccess;
+  const dim3 grid((p.n_tokens + kTileTokens - 1) / kTileTokens, p.H, p.B * p.n);
+  if (dtype == 2) hipLaunchKernelGGL((rope_apply_batch<__bf16, fp8e4m3>), grid, dim3(kThreads), 0, st, p);
+  else if (dtype == 1) hipLaunchKernelGGL((rope_apply_batch<__bf16, __bf16>), grid, dim3(kThreads), 0, st, p);
+  else hipLaunchKernelGGL((rope_apply_batch<float, float>), grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_refresh(const RefreshParams& p, int dtype, hipStream_t st) {
-  const int64_t items = static_cast<int64_t>(p.Nc) * (p.dt >> 1);
+  const int vn = dtype == 2 ? 16 : dtype == 1 ? 8 : 4;   // elements per 16-byte vector
+  const int64_t items = static_cast<int64_t>(p.n_slot) * p.Nc * ((p.dt + vn - 1) / vn);
   if (items <= 0 || p.n_slot <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((items + kThreads - 1) / kThreads), p.n_slot, p.BH);
+  const int64_t per_block = static_cast<int64_t>(kThreads) * kRefreshPerThread;
+  const dim3 grid(static_cast<unsigned>((items + per_block - 1) / per_block), 1, p.BH);
   if (dtype == 2) hipLaunchKernelGGL(rope_refresh<fp8e4m3>, grid, dim3(kThreads), 0, st, p);
   else if (dtype == 1) hipLaunchKernelGGL(rope_refresh<__bf16>, grid, dim3(kThreads), 0, st, p);
   else hipLaunchKernelGGL(rope_refresh<float>, grid, dim3(kThreads), 0, st, p);

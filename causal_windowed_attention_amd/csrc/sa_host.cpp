@@ -33,6 +33,7 @@ using sa::AttnParams;
 using sa::CombineParams;
 using sa::RefreshParams;
 using sa::RopeWriteParams;
+static_assert(sa::kMaxBatchStreams == SA_MAX_BATCH_STREAMS, "one batched RoPE launch per sa_batch_attend");
 
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxPosition = 1 << 30;   // guard against int32 overflow when max_t == 0
@@ -913,16 +914,36 @@ sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* cons
     hipStream_t hs = static_cast<hipStream_t>(stream);
     AttnParams ap;
     std::memset(&ap, 0, sizeof(ap));
-    for (int i = 0; i < n; ++i) {                // stage each entry's chunk in its own workspace
-      sa_stream* si = streams[i];
+    // one launch stages every entry's chunk in its own workspace
+    sa::RopeBatchParams bp;
+    std::memset(&bp, 0, sizeof(bp));
+    {
       RopeWriteParams rp;
-      base_write_params(si, &rp);
-      rp.q = q[i]; rp.k = k[i]; rp.v = v[i];
-      rp.qrot = si->qscratch();
-      rp.row0 = si->staging_slot() * d.Nc;
-      fill_temporal(d, si->t_next, d.F, rp.t_cs);
-      const sa_status st = timed(si, SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply(rp, d.dtype, hs); });
+      base_write_params(s0, &rp);
+      bp.h_cs = rp.h_cs; bp.w_cs = rp.w_cs;
+      bp.k_bh_stride = rp.k_bh_stride; bp.vt_bh_stride = rp.vt_bh_stride;
+      bp.key_stride = rp.key_stride; bp.n_tokens = rp.n_tokens; bp.in_tokens = rp.in_tokens;
+      bp.B = rp.B; bp.H = rp.H; bp.D = rp.D; bp.Hf = rp.Hf; bp.Wf = rp.Wf;
+      bp.dt = rp.dt; bp.dh = rp.dh; bp.dw = rp.dw; bp.n_frames = rp.n_frames; bp.q_rows = rp.q_rows;
+      bp.q_scale = rp.q_scale;
+    }
+    bp.n = n;
+    for (int j = 0; j < d.dt / 2; ++j) bp.theta_t[j] = freq(d, d.dt, j);
+    for (int i = 0; i < n; ++i) {
+      sa_stream* si = streams[i];
+      bp.q[i] = q[i]; bp.k[i] = k[i]; bp.v[i] = v[i];
+      bp.qrot[i] = si->qscratch();
+      bp.kcache[i] = si->kcache();
+      bp.vtcache[i] = si->vtcache();
+      bp.row0[i] = si->staging_slot() * d.Nc;
+      bp.t0[i] = si->t_next;
+    }
+    {
+      const sa_status st = timed(streams[0], SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply_batch(bp, d.dtype, hs); });
       if (st != SA_OK) return st;
+    }
+    for (int i = 0; i < n; ++i) {
+      sa_stream* si = streams[i];
       ap.g_q[i] = si->qscratch();
       ap.g_kc[i] = si->kcache();
       ap.g_vt[i] = si->vtcache();
@@ -1010,26 +1031,12 @@ size_t sa_gdn_workspace_bytes(int32_t batch, int32_t tokens, int32_t heads, int3
   return gdn_layout(batch, tokens, heads, head_dim, &L) == SA_OK ? L.total : 0;
 }
 
-sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim, const void* q,
-                         const void* k, const void* v, const float* alpha, const float* beta,
-                         const float* state_in, float* state_out, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  GdnLayout L;
-  const sa_status st = gdn_layout(batch, tokens, heads, head_dim, &L);
-  if (st != SA_OK) return st;
-  auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-  // the states move as float4s
-  if (state_out == nullptr || !aligned16(state_out) || (state_in != nullptr && !aligned16(state_in)))
-    return SA_ERR_INVALID_ARGUMENT;
-  if (tokens > 0) {                              // with no tokens only the state is touched
-    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || out == nullptr ||
-        workspace == nullptr)
-      return SA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) || !a4(alpha) ||
-        !a4(beta))
-      return SA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < L.total) return SA_ERR_WORKSPACE_TOO_SMALL;
-  }
+namespace {
+
+// The forward over a workspace of ws_bytes at ws (the caller's, or the fixed scratch).
+sa_status gdn_forward_impl(const GdnLayout& L, int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim,
+                           const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                           const float* state_in, float* state_out, void* out, void* workspace, hipStream_t hs) {
   char* ws = static_cast<char*>(workspace);
   sa::GdnParams p;
   std::memset(&p, 0, sizeof(p));
@@ -1044,7 +1051,6 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
   p.U = reinterpret_cast<float*>(ws + L.U);
   p.Sst = reinterpret_cast<float*>(ws + L.Sst);
   p.B = batch; p.N = tokens; p.H = heads; p.D = head_dim; p.nb = L.nb;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
   if (tokens == 0) {                             // no tokens: the state passes through
     const size_t n = static_cast<size_t>(batch) * heads * head_dim * head_dim;
     return sa::launch_gdn_state_pass(state_in, state_out, n, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
@@ -1052,3 +1058,37 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
   return sa::launch_gdn_forward(p, hs) == hipSuccess ? SA_OK : SA_ERR_DEVICE;
 }
 
+// Argument checks shared by both forwards (the workspace is checked by the caller).
+sa_status gdn_check_args(int32_t tokens, const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state_in, const float* state_out, const void* out) {
+  auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  // the states move as float4s
+  if (state_out == nullptr || !aligned16(state_out) || (state_in != nullptr && !aligned16(state_in)))
+    return SA_ERR_INVALID_ARGUMENT;
+  if (tokens > 0) {                              // with no tokens only the state is touched
+    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || out == nullptr)
+      return SA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !a4(alpha) || !a4(beta))
+      return SA_ERR_INVALID_ARGUMENT;
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const float* state_in, float* state_out, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  GdnLayout L;
+  sa_status st = gdn_layout(batch, tokens, heads, head_dim, &L);
+  if (st != SA_OK) return st;
+  st = gdn_check_args(tokens, q, k, v, alpha, beta, state_in, state_out, out);
+  if (st != SA_OK) return st;
+  if (tokens > 0) {
+    if (workspace == nullptr || !aligned16(workspace)) return SA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < L.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return gdn_forward_impl(L, batch, tokens, heads, head_dim, q, k, v, alpha, beta, state_in, state_out, out,
+                          workspace, static_cast<hipStream_t>(stream));
+}

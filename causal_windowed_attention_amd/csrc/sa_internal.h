@@ -52,6 +52,36 @@ struct RopeWriteParams {
   float2 t_cs[kMaxTemporalPairs];  // [frame][d_t/2]: (cos, sin) of (t0 + frame) * theta_t,j
 };
 
+// One launch of rope_apply for the n streams of a ragged batch: stream e's q, k, v go
+// to its own Q scratch and staging slot (row0[e]), rotated at positions t0[e] + frame.
+// The geometry is shared (the streams have equal configurations); each stream's temporal
+// (cos, sin) come from theta_t in fp64 on the device.
+constexpr int kMaxBatchStreams = 8;     // SA_MAX_BATCH_STREAMS
+struct RopeBatchParams {
+  const float2* h_cs;   // [Hf][d_h/2], as in RopeWriteParams (stream 0's copy)
+  const float2* w_cs;   // [Wf][d_w/2]
+  int64_t k_bh_stride;  // elements
+  int64_t vt_bh_stride; // elements
+  int32_t key_stride;
+  int32_t n_tokens;     // Nc
+  int32_t in_tokens;
+  int32_t B, H, D, Hf, Wf;
+  int32_t dt, dh, dw;
+  int32_t n_frames;
+  int32_t q_rows;
+  float q_scale;
+  int32_t n;            // streams
+  const void* q[kMaxBatchStreams];
+  const void* k[kMaxBatchStreams];
+  const void* v[kMaxBatchStreams];
+  void* qrot[kMaxBatchStreams];
+  void* kcache[kMaxBatchStreams];
+  void* vtcache[kMaxBatchStreams];
+  int32_t row0[kMaxBatchStreams];
+  int32_t t0[kMaxBatchStreams];     // temporal position of each stream's first frame
+  double theta_t[64];               // theta^(-2j / d_t) for j < d_t / 2
+};
+
 // In-place re-rotation of the temporal pairs of whole cache slots by -Delta.
 struct RefreshParams {
   void* kcache;         // [B*H][n_slots*Nc][D]
@@ -141,6 +171,7 @@ struct CombineParams {
 
 // dtype: 0 = fp32, 1 = bf16 (sa_dtype)
 hipError_t launch_rope_apply(const RopeWriteParams& p, int dtype, hipStream_t st);
+hipError_t launch_rope_apply_batch(const RopeBatchParams& p, int dtype, hipStream_t st);
 hipError_t launch_kv_append(const RopeWriteParams& p, int dtype, hipStream_t st);
 hipError_t launch_sink_update(const RopeWriteParams& p, int dtype, hipStream_t st);
 hipError_t launch_rope_refresh(const RefreshParams& p, int dtype, hipStream_t st);

@@ -273,9 +273,10 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
  * with one attention launch over all entries, each with its own visible keys.
  * 1 <= n <= SA_MAX_BATCH_STREAMS distinct handles created from equal configs
  * (all planning handles or none); lse may be NULL, as may any lse[i]. Every
- * entry is validated before any launch: on an error no state changes. Each
- * handle's profiler records its own RoPE launch; the attention launch is
- * recorded on streams[0].
+ * entry is validated before any launch: on an error no state changes. One
+ * RoPE launch stages every entry's chunk in its own workspace, then one
+ * attention launch serves all entries; both are recorded by streams[0]'s
+ * profiler.
  */
 sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* const* q, const void* const* k,
                           const void* const* v, void* const* out, float* const* lse, void* stream);

@@ -26,7 +26,7 @@ __all__ = [
     "sa_stream_create", "sa_stream_destroy", "sa_chunk_attend", "sa_kv_append",
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
     "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16",
-    "sa_gdn_workspace_bytes", "sa_gdn_forward", "gdn_forward",
+    "sa_gdn_workspace_bytes", "sa_gdn_forward", "sa_gdn_forward_noalloc", "gdn_forward",
     "sa_buffer_attend", "sa_buffer_plan", "sa_batch_attend", "Stream",
     "SA_F32", "SA_BF16", "SA_FP8", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
     "SA_OPT_ATTN_VARIANT", "SA_OPT_SCHEDULE",
@@ -208,6 +208,13 @@ def sa_gdn_forward(batch, tokens, heads, head_dim, q, k, v, alpha, beta, state_i
     _check(L.load().sa_gdn_forward(batch, tokens, heads, head_dim, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(workspace),
                                    workspace_bytes, _stream_ptr(stream)), "sa_gdn_forward")
+
+
+def sa_gdn_forward_noalloc(batch, tokens, heads, head_dim, q, k, v, alpha, beta, state_in, state_out, out,
+                           stream=None) -> None:
+    _check(L.load().sa_gdn_forward_noalloc(batch, tokens, heads, head_dim, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                           _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                           _stream_ptr(stream)), "sa_gdn_forward_noalloc")
 
 
 def gdn_forward(q, k, v, alpha, beta, state=None, out=None, state_out=None, workspace=None, stream=None):

@@ -26,6 +26,7 @@ SA_MAX_BUFFER_CHUNKS = 8
 SA_MAX_KEY_SEGMENTS = 4
 SA_MAX_BATCH_STREAMS = 8
 SA_BUFFER_STEPS = 1
+SA_GDN_SCRATCH_BYTES = 67108864
 # sa_slot_kind
 SA_SLOT_EMPTY, SA_SLOT_SINK, SA_SLOT_WINDOW, SA_SLOT_STAGING = 0, 1, 2, 3
 # sa_kernel_id
@@ -99,6 +100,7 @@ SIGNATURES = {
                                        ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
     "sa_gdn_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "sa_gdn_forward": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sa_gdn_forward_noalloc": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

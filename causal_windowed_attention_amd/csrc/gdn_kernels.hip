@@ -23,6 +23,8 @@
 // outputs are bf16, the state fp32.
 #include "sa_internal.h"
 
+#include <mutex>
+
 namespace sa {
 namespace {
 
@@ -571,6 +573,45 @@ hipError_t launch_gdn_state_pass(const float* in, float* out, size_t n, hipStrea
 hipError_t launch_gdn_forward(const GdnParams& p, hipStream_t st) {
   if (p.N <= 0) return hipSuccess;
   return p.D == 128 ? launch_gdn_d<128>(p, st) : launch_gdn_d<64>(p, st);
+}
+
+// ---- scratch for the workspace-free forward ---------------------------------------------------
+// A fixed device array stands in for the caller's workspace (sa_gdn_forward_noalloc). Each GPU
+// the library runs on holds its own copy, placed when the code object loads there and kept
+// until the process ends. Host code never uses the array's name as an address: it takes each
+// device's address once from hipGetSymbolAddress and passes that to the kernels.
+static_assert(kGdnScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) char scratch[kGdnScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t gdn_scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {          // first call on this device: with it current
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace sa

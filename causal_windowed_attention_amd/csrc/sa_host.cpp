@@ -1092,3 +1092,20 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
   return gdn_forward_impl(L, batch, tokens, heads, head_dim, q, k, v, alpha, beta, state_in, state_out, out,
                           workspace, static_cast<hipStream_t>(stream));
 }
+
+sa_status sa_gdn_forward_noalloc(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim, const void* q,
+                                 const void* k, const void* v, const float* alpha, const float* beta,
+                                 const float* state_in, float* state_out, void* out, void* stream) {
+  static_assert(sa::kGdnScratchBytes == SA_GDN_SCRATCH_BYTES, "scratch size in the header");
+  GdnLayout L;
+  sa_status st = gdn_layout(batch, tokens, heads, head_dim, &L);
+  if (st != SA_OK) return st;
+  if (tokens > 0 && L.total > sa::kGdnScratchBytes) return SA_ERR_WORKSPACE_TOO_SMALL;
+  st = gdn_check_args(tokens, q, k, v, alpha, beta, state_in, state_out, out);
+  if (st != SA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  if (tokens > 0 && sa::gdn_scratch_address(hs, &scratch) != hipSuccess) return SA_ERR_DEVICE;
+  return gdn_forward_impl(L, batch, tokens, heads, head_dim, q, k, v, alpha, beta, state_in, state_out, out,
+                          scratch, hs);
+}

@@ -180,6 +180,10 @@ hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st
 hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 hipError_t launch_gdn_forward(const GdnParams& p, hipStream_t st);
+// Bytes of the fixed device scratch of the workspace-free GDN forward, and its address on the
+// device of stream st (null: the current device), looked up once per device.
+constexpr size_t kGdnScratchBytes = size_t(64) << 20;
+hipError_t gdn_scratch_address(hipStream_t st, void** out);
 // out[0, n) = in[0, n), or zeros when in is null (n floats, a multiple of 4; in == out: nothing)
 hipError_t launch_gdn_state_pass(const float* in, float* out, size_t n, hipStream_t st);
 

@@ -392,6 +392,24 @@ sa_status sa_gdn_forward(int32_t batch, int32_t tokens, int32_t heads, int32_t h
                          const float* state_in, float* state_out, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: sa_gdn_forward without the workspace
+ * argument. Its scratch is a fixed device array of SA_GDN_SCRATCH_BYTES inside the library;
+ * each GPU the library runs on holds its own copy from the first use until the process ends.
+ * The caller still passes every input and output (same meaning, layouts and errors as
+ * sa_gdn_forward). Nothing is allocated: sizes whose workspace (sa_gdn_workspace_bytes)
+ * exceeds SA_GDN_SCRATCH_BYTES return SA_ERR_WORKSPACE_TOO_SMALL before any device work.
+ * The scratch needs no clearing (every call writes what it reads) and keeps the last call's
+ * contents. All calls on one GPU share it: calls that overlap on one GPU race, so order them
+ * on one stream (or synchronise between streams). The first call on a GPU looks up the
+ * array's address there (SA_ERR_DEVICE if that fails); later calls only launch.
+ */
+#define SA_GDN_SCRATCH_BYTES 67108864
+sa_status sa_gdn_forward_noalloc(int32_t batch, int32_t tokens, int32_t heads, int32_t head_dim, const void* q,
+                                 const void* k, const void* v, const float* alpha, const float* beta,
+                                 const float* state_in, float* state_out, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,14 +13,17 @@
 //   O  = diag(gam) Q S0^T + ((Q K^T) o M) U,  M_ij = gam_i / gam_j  (j <= i)
 //   S' = gam_C S0 + U^T Kt,  Kt = diag(gam_C / gam) K
 // Three kernels: gdn_prep (every block independently: gates, T by forward substitution,
-// W, Up and Kt), gdn_scan (the only sequential part: the state through the blocks, in
-// row slices of S, which evolve independently; records each block's starting state and
-// U), gdn_out (every block independently: the outputs). Products whose inputs are bf16
-// (K K^T, Q K^T) run on the bf16 MFMA with exact products; those feeding the state
-// recurrence (T V, T diag(gam) K, and the scan's two) on the fp32 MFMA; gdn_out's
-// remaining products on the bf16 MFMA with fp32 operands split into bf16 hi/lo pairs
-// (an output's error stays near 2^-16 of its terms and does not feed back). Inputs and
-// outputs are bf16, the state fp32.
+// W, Up and a bf16 copy of K^T), gdn_scan (the only sequential part: the state through the
+// blocks, in row slices of S, which evolve independently; records each block's starting
+// state and U), gdn_out (every block independently: the outputs). All products but the
+// merges of T's blocked inverse (fp32 MFMA) run on the bf16 MFMA with fp32 accumulation.
+// Products whose inputs are bf16 (K K^T, Q K^T) are exact;
+// those feeding the state recurrence (T V, T diag(gam) K, and the scan's W S^T and
+// K^T diag(gam_C / gam) U) take each fp32 operand as three bf16 parts (t1 + t2 + t3 = x to
+// 2^-24 |x|) and keep every partial product down to 2^-24 of the whole, which matches an
+// fp32 product; gdn_out's remaining products split fp32 operands into bf16 hi/lo pairs (an
+// output's error stays near 2^-16 of its terms and does not feed back). Inputs and outputs
+// are bf16, the state fp32.
 #include "sa_internal.h"
 
 #include <mutex>
@@ -35,25 +38,21 @@ constexpr int kCL = kC + 4;          // padded row of a 64-wide LDS tile
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
-// Storage order of the scan's per-block operands: each of the scan's float4 loads reads
-// 1 KB contiguously (lane l takes floats [4 l, 4 l + 4) of its load's run). Lane l = lr +
-// 16 lq of wave w (columns [D/4 w, D/4 (w + 1)), NT = D / 64 tiles of 16) loads
-//   W     load (mt, t): W[16 mt + lr][D/4 w + 16 t + 4 lq + e]
-//   Kt^T  load (t, u):  Kt^T[D/4 w + 16 t + lr][16 lq + 4 u + e]
-//   Up^T  load u of row slice r / 16: Up^T[16 (r / 16) + lr][16 lq + 4 u + e]
+// Storage order of the scan's per-block operands. The scan keeps the state slice in the
+// accumulator layout of a 16 x 16 MFMA tile and feeds it back as the B operand of the next
+// block's W S^T, so a lane quad q of wave w (columns [D/4 w, D/4 (w + 1)), NT = D / 64) holds
+// the KQ = 4 NT consecutive columns D/4 w + KQ q + e, e < KQ; accumulator tile t, row 4 q + j
+// is column D/4 w + KQ q + 4 t + j. Every operand run below is 64 lanes of contiguous
+// elements, read by one load per lane.
+//   W, three bf16 parts (run (w, mt, part)): lane l = r + 16 q holds W[16 mt + r][D/4 w + KQ q + e]
+//   K^T, bf16 (run (w, t, s)): lane l = m + 16 q holds K^T[D/4 w + KQ (m / 4) + 4 t + m % 4][32 s + 8 q + e]
+//   Up^T, fp32 (load u of row slice r / 16): Up^T[16 (r / 16) + lr][16 lq + 4 u + e]
 template <int D>
-__device__ __forceinline__ int w_index(int i, int k) {      // W[i][k], i token, k column
-  constexpr int NT = D / 64;
+__device__ __forceinline__ int w3_index(int i, int k) {     // part 0 of W[i][k]; part p at + p * 64 KQ
+  constexpr int KQ = D / 16;
   const int w = k / (D / 4), cc = k % (D / 4);
-  const int l = (i & 15) + 16 * ((cc & 15) >> 2);
-  return ((((w * 4 + (i >> 4)) * NT + (cc >> 4)) * 64 + l) << 2) + (cc & 3);
-}
-template <int D>
-__device__ __forceinline__ int kt_index(int c, int i) {     // Kt^T[c][i], c column, i token
-  constexpr int NT = D / 64;
-  const int w = c / (D / 4), cc = c % (D / 4);
-  const int l = (cc & 15) + 16 * (i >> 4);
-  return ((((w * NT + (cc >> 4)) * 4 + ((i & 15) >> 2)) * 64 + l) << 2) + (i & 3);
+  const int l = (i & 15) + 16 * (cc / KQ);
+  return (((w * 4 + (i >> 4)) * 3 * 64 + l) * KQ) + cc % KQ;
 }
 __device__ __forceinline__ int up_index(int r, int i) {     // Up^T[r][i], r row of the state, i token
   const int l = (r & 15) + 16 * (i >> 4);
@@ -87,6 +86,39 @@ __device__ __forceinline__ void split3_bf16(const float (&x)[8], bf16x8& t1, bf1
     t3[e] = static_cast<__bf16>(r);
   }
 }
+template <int N> struct BfVec;
+template <> struct BfVec<4> { typedef __bf16 type __attribute__((ext_vector_type(4))); };
+template <> struct BfVec<8> { typedef __bf16 type __attribute__((ext_vector_type(8))); };
+// x = t1 + t2 + t3 to 2^-24 |x| for N values (as split3_bf16)
+template <int N>
+__device__ __forceinline__ void split3(const float* x, typename BfVec<N>::type& t1, typename BfVec<N>::type& t2,
+                                       typename BfVec<N>::type& t3) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    float r = x[e];
+    const __bf16 a = static_cast<__bf16>(r);
+    r -= static_cast<float>(a);
+    const __bf16 b = static_cast<__bf16>(r);
+    r -= static_cast<float>(b);
+    t1[e] = a;
+    t2[e] = b;
+    t3[e] = static_cast<__bf16>(r);
+  }
+}
+// 16 x 16 tile on the bf16 MFMA with KQ = 8 (v_mfma_f32_16x16x32_bf16) or 4
+// (v_mfma_f32_16x16x16_bf16) depth values per lane: lane l supplies A[l % 16][KQ (l / 16) + e]
+// and B[KQ (l / 16) + e][l % 16], e < KQ, and receives C[4 (l / 16) + j][l % 16]
+template <int KQ>
+__device__ __forceinline__ f32x4 mfma16(const typename BfVec<KQ>::type& a, const typename BfVec<KQ>::type& b,
+                                        const f32x4& c) {
+  if constexpr (KQ == 8) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  } else {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+  }
+}
 __device__ __forceinline__ void unpack8(const float4& a, const float4& b, float (&x)[8]) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -94,13 +126,14 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, co
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---- gdn_prep: per block, log gates, T, W = T diag(gam) K, Up = T V, Kt ---------------------
+// ---- gdn_prep: per block, log gates, T, W = T diag(gam) K, Up = T V, K^T ---------------------
 // K K^T on v_mfma_f32_32x32x16_bf16 (bf16 inputs: exact products); T by a blocked inverse
 // (substitution within 16 x 16 blocks, merges on v_mfma_f32_16x16x4_f32: lane l supplies
 // A[l % 16][l / 16] and B[l / 16][l % 16] and receives C[4 (l / 16) + j][l % 16]); T V and
 // T diag(gam) K, which feed the state recurrence, on the bf16 MFMA with T split into three
-// bf16 parts (fp32 accuracy). K^T and V^T are staged transposed in LDS (rows of 64 + 8
-// bf16, conflict-free).
+// bf16 parts (fp32 accuracy); W leaves as three bf16 parts, K^T as a bf16 copy, both in the
+// scan's operand order. K^T and V^T are staged transposed in LDS (rows of 64 + 8 bf16,
+// conflict-free).
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
@@ -240,20 +273,14 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
     for (int j = 0; j < 4; ++j) X[(32 + tr + 4 * q + j) * kCL + tc + lr] = -x[j];
   }
   {
-    // Kt^T = (diag(exp(g_C - g)) K)^T in the scan's load order (kt_index), written as
-    // float4s: entries 4 f .. 4 f + 3 are load (f / 64) of their wave's run, lane f % 64,
-    // i.e. four consecutive tokens of one column (one 8-byte read of K^T)
-    const float gC = g[kC - 1];
+    // K^T in bf16 for the scan's state update, in its operand order: run (w, t, s) of 64
+    // lanes x 8 tokens (16 bytes per lane, straight from the transposed copy in LDS)
     constexpr int NT = D / 64;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    for (int f = tid; f < kC * D / 4; f += kThr) {
-      const int l2 = f & 63, run = f >> 6, u = run & 3, t = (run >> 2) % NT, ww = run / (4 * NT);
-      const int c = ww * (D / 4) + 16 * t + (l2 & 15), i = 16 * (l2 >> 4) + 4 * u;
-      const bf16x4 kk = *reinterpret_cast<const bf16x4*>(KT + c * VL + i);
-      st4(p.Kt + boff + 4 * f, make_float4(__expf(gC - g[i]) * static_cast<float>(kk[0]),
-                                           __expf(gC - g[i + 1]) * static_cast<float>(kk[1]),
-                                           __expf(gC - g[i + 2]) * static_cast<float>(kk[2]),
-                                           __expf(gC - g[i + 3]) * static_cast<float>(kk[3])));
+    __bf16* ktb = static_cast<__bf16*>(p.Kt) + boff;
+    for (int f = tid; f < kC * D / 8; f += kThr) {
+      const int l2 = f & 63, run = f >> 6, s = run & 1, t = (run >> 1) % NT, ww = run / (2 * NT);
+      const int m = l2 & 15, c = ww * (D / 4) + 4 * NT * (m >> 2) + 4 * t + (m & 3);
+      *reinterpret_cast<bf16x8*>(ktb + 8 * f) = *reinterpret_cast<const bf16x8*>(KT + c * VL + 32 * s + 8 * (l2 >> 4));
     }
   }
   __syncthreads();
@@ -295,136 +322,199 @@ __global__ __launch_bounds__(kThr) void gdn_prep(GdnParams p) {
       const int o = 8 * r4 + 4 * hf;
       st4(p.Up + boff + up_index(dc, 32 * it + o),
           make_float4(au[4 * r4], au[4 * r4 + 1], au[4 * r4 + 2], au[4 * r4 + 3]));
-      st4(p.W + boff + w_index<D>(ti, 32 * dt + o),
-          make_float4(aw[4 * r4], aw[4 * r4 + 1], aw[4 * r4 + 2], aw[4 * r4 + 3]));
+      // W in three bf16 parts (the scan's A operands): four consecutive columns, 8 bytes per part
+      const float wv[4] = {aw[4 * r4], aw[4 * r4 + 1], aw[4 * r4 + 2], aw[4 * r4 + 3]};
+      typename BfVec<4>::type w1, w2, w3;
+      split3<4>(wv, w1, w2, w3);
+      __bf16* wb = static_cast<__bf16*>(p.W) + 3 * boff + w3_index<D>(ti, 32 * dt + o);
+      *reinterpret_cast<typename BfVec<4>::type*>(wb) = w1;
+      *reinterpret_cast<typename BfVec<4>::type*>(wb + 64 * (D / 16)) = w2;
+      *reinterpret_cast<typename BfVec<4>::type*>(wb + 128 * (D / 16)) = w3;
     }
   }
 }
 
 // ---- gdn_scan: the state through the blocks, rows [rs, rs + 16) of S per workgroup ----------
-// Per block, on the fp32 MFMA (v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16]
-// and B[l / 16][l % 16] and receives C[4 (l / 16) + j][l % 16]), with wave w owning the
-// columns [D/4 w, D/4 (w + 1)) of the slice:
-//   U (64 x 16) = Up - W S^T: wave w forms the partial over its columns (less Up on its
-//     own 16 tokens), the four partials meet in LDS (double-buffered: one barrier per block);
-//   S'^T = exp(g_C) S^T + Kt^T U on the wave's columns.
-// The state is held as S^T in the C layout, which is also the B operand of W S^T (k-step
-// (t, j) of lane quad q is column 16 t + 4 q + j): no exchange of the state between waves.
-// The reduced U is read back in the B layout of Kt^T U (k-step s of quad q is token
-// 16 q + s). Operands of the next block (W, Kt^T, Up^T, its gate) are fetched while the
+// Per block, on the bf16 MFMA (mfma16), with wave w owning the columns [D/4 w, D/4 (w + 1))
+// of the slice:
+//   U (64 x 16) = Up - W S^T: wave w forms the partial over its columns (less Up on its own
+//     16 tokens) from W's three bf16 parts and the slice's three (t1 + t2 + t3 = x to 2^-24 |x|;
+//     the six products down to 2^-24 of the whole, accumulated in fp32); the four partials
+//     meet in LDS (double-buffered: one barrier per block);
+//   S'^T = exp(g_C) S^T + K^T diag(exp(g_C - g)) U on the wave's columns: K is bf16 (exact
+//     products) and the scaled U enters as three bf16 parts.
+// The state is held as S^T in the accumulator layout, which is also the B operand of the next
+// block's W S^T (lane quad q holds columns KQ q + e of the wave's range): no exchange of the
+// state between waves. The reduced U is read back in the B layout of the state update (tokens
+// 32 s + 8 q + e). Operands of the next block (W, K^T, Up^T, the gates) are fetched while the
 // current one computes.
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
   static_assert(kGdnScanRows == 16, "one 16-row MFMA tile of the state per workgroup");
-  constexpr int NT = D / 64;                     // 16-column tiles per wave
+  constexpr int NT = D / 64;                     // 16-column accumulator tiles per wave
+  constexpr int KQ = 4 * NT;                     // columns per lane quad: the depth of W S^T
+  typedef typename BfVec<KQ>::type bfq;
   __shared__ __attribute__((aligned(16))) float part[2][4][16][kCL];  // [buffer][wave][row][token]
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int l = tid & 63, w = tid >> 6, lr = l & 15, lq = l >> 4;
+  __shared__ __attribute__((aligned(16))) float fsh[2][kC];           // [buffer][token] exp(g_C - g)
+  // Workgroup -> (row slice, (b, h)). The SL = D / 16 slices of one (b, h) read the same W,
+  // K^T and Up of every block. Workgroups go to the 8 XCDs (each with its own L2) in turn,
+  // id mod 8, so the slices of one (b, h) take ids of one residue mod 8 and read one L2 copy
+  // of those operands; the (b, h) past the last full group of 8 take consecutive ids.
+  constexpr int SL = D / kGdnScanRows;
+  const int id = blockIdx.x, G8 = (p.B * p.H) & ~7;
+  int split, g;
+  if (id < SL * G8) {
+    const int r = id >> 3;
+    split = r % SL;
+    g = (id & 7) + 8 * (r / SL);
+  } else {
+    const int t = id - SL * G8;
+    split = t % SL;
+    g = G8 + t / SL;
+  }
+  const int tid = threadIdx.x;
+  const int l = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), lr = l & 15, lq = l >> 4;
+  const int wv = tid >> 6;                       // the wave index as a per-lane value
   const int rs = split * 16, cw = w * (D / 4);
-  const size_t bh = static_cast<size_t>(b) * p.H + h;
+  const size_t bh = static_cast<size_t>(g);
   auto boff = [&](int blk) { return (bh * p.nb + blk) * static_cast<size_t>(kC) * D; };
+  const float* gbh = p.g + bh * (static_cast<size_t>(p.nb) * kC);
+  const size_t srow = (bh * D + rs + lr) * D + cw + KQ * lq;      // this lane's run of a state row
 
-  f32x4 sc[NT];                                  // S[rs + lr][cw + 16 t + 4 lq + j]
+  f32x4 sc[NT];                                  // S[rs + lr][cw + KQ lq + 4 t + j]
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.state_in != nullptr) v = ld4(p.state_in + (bh * D + rs + lr) * D + cw + 16 * t + 4 * lq);
+    if (p.state_in != nullptr) v = ld4(p.state_in + srow + 4 * t);
     sc[t] = f32x4{v.x, v.y, v.z, v.w};
   }
   struct Ops {
-    float4 wa[4][NT];                            // W[16 mt + lr][cw + 16 t + 4 lq ..]     (w_index)
-    float4 ka[NT][4];                            // Kt^T[cw + 16 t + lr][16 lq + 4 u ..]   (kt_index)
-    float4 up;                                   // Up^T[rs + lr][16 w + 4 lq ..]          (up_index)
-    float gC;
+    bfq wa[4][3];                                // W parts, token tile mt
+    bf16x8 ka[NT][2];                            // K^T, column tile t, 32-token step s
+    float4 up;                                   // Up^T[rs + lr][16 w + 4 lq ..]   (up_index)
+    float gl;                                    // g of token l (lane 63: g_C)
   };
-  auto fetch = [&](int blk, Ops& o) {
-    const size_t bo = boff(blk);
+  // The next block's operands are loaded in pieces between this block's MFMA groups: issued
+  // together they would fill the CU's vector memory queue and hold the wave until the whole
+  // 17 KB per wave had been accepted.
+  // (in the order of use: W part 2, 1, 0 of all four token tiles; then Up^T and the gates;
+  // then K^T by 32-token step)
+  auto fetch_w = [&](int blk, Ops& o, int pt) {
+    const __bf16* wsrc = static_cast<const __bf16*>(p.W) + 3 * boff(blk);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) o.wa[mt][t] = ld4(p.W + bo + ((((w * 4 + mt) * NT + t) * 64 + l) << 2));
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) o.ka[t][u] = ld4(p.Kt + bo + ((((w * NT + t) * 4 + u) * 64 + l) << 2));
-    o.up = ld4(p.Up + bo + (((split * 4 + lq) * 64 + lr + 16 * w) << 2));
-    o.gC = p.g[bh * (static_cast<size_t>(p.nb) * kC) + blk * kC + kC - 1];
+      o.wa[mt][pt] = *reinterpret_cast<const bfq*>(wsrc + (((w * 4 + mt) * 3 + pt) * 64 + l) * KQ);
   };
-  // One block: the loads of the next block go out first, then the stores (this block's
-  // starting state, later its U^T), the same number in every wave. The memory counter
-  // retires in issue order, so a store issued before those loads would have to complete
-  // before the current block's operands (loaded one block earlier) count as arrived.
+  auto fetch_k = [&](int blk, Ops& o) {
+    const size_t bo = boff(blk);
+    o.up = ld4(p.Up + bo + (((split * 4 + lq) * 64 + lr + 16 * w) << 2));
+    o.gl = gbh[blk * kC + l];
+    const __bf16* ksrc = static_cast<const __bf16*>(p.Kt) + bo;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        o.ka[t][s2] = *reinterpret_cast<const bf16x8*>(ksrc + (((w * NT + t) * 2 + s2) * 64 + l) * 8);
+  };
+  auto fetch = [&](int blk, Ops& o) {
+#pragma unroll
+    for (int pt = 2; pt >= 0; --pt) fetch_w(blk, o, pt);
+    fetch_k(blk, o);
+  };
   auto step = [&](int blk, const Ops& cur, Ops& nxt) {
-    fetch(min(blk + 1, p.nb - 1), nxt);
-    __builtin_amdgcn_sched_barrier(0);
+    const int nb1 = min(blk + 1, p.nb - 1);
     float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      st4(Sst + (rs + lr) * D + cw + 16 * t + 4 * lq, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
+    for (int t = 0; t < NT; ++t) st4(Sst + (srow - bh * D * D) + 4 * t, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
+    // the slice as the B operand of W S^T, in three bf16 parts
+    float sv[KQ];
+#pragma unroll
+    for (int e = 0; e < KQ; ++e) sv[e] = sc[e >> 2][e & 3];
+    bfq s1, s2, s3;
+    split3<KQ>(sv, s1, s2, s3);
     __builtin_amdgcn_sched_barrier(0);
-    // partial of W S^T over this wave's columns: four 16-token tiles
+    // partial of W S^T over this wave's columns: four 16-token tiles, smallest products first,
+    // the four chains interleaved; the next block's W parts load between the groups
     f32x4 acc[4] = {};
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int k = 0; k < 6; ++k) {
+      constexpr int wp[6] = {2, 1, 0, 1, 0, 0};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const float a = j == 0 ? cur.wa[mt][t].x : j == 1 ? cur.wa[mt][t].y : j == 2 ? cur.wa[mt][t].z : cur.wa[mt][t].w;
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[t][j], acc[mt], 0, 0, 0);
-        }
+      for (int mt = 0; mt < 4; ++mt) {
+        const bfq& sp = k == 0 || k == 3 || k == 5 ? s1 : (k == 1 || k == 4 ? s2 : s3);
+        acc[mt] = mfma16<KQ>(cur.wa[mt][wp[k]], sp, acc[mt]);
+      }
+      if (k >= 1 && k <= 3) fetch_w(nb1, nxt, 3 - k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.gl), 63));
+    const float fl = __expf(gC - cur.gl);        // exp(g_C - g_l): token l's weight in the update
     // wave w folds -Up of its own token tile into its partial: the four sum to -U
-    acc[0] -= w == 0 ? f32x4{cur.up.x, cur.up.y, cur.up.z, cur.up.w} : f32x4{};
-    acc[1] -= w == 1 ? f32x4{cur.up.x, cur.up.y, cur.up.z, cur.up.w} : f32x4{};
-    acc[2] -= w == 2 ? f32x4{cur.up.x, cur.up.y, cur.up.z, cur.up.w} : f32x4{};
-    acc[3] -= w == 3 ? f32x4{cur.up.x, cur.up.y, cur.up.z, cur.up.w} : f32x4{};
+    const f32x4 up = f32x4{cur.up.x, cur.up.y, cur.up.z, cur.up.w};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] -= (mt == w ? 1.f : 0.f) * up;
     float(*pb)[16][kCL] = part[blk & 1];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
       st4(&pb[w][lr][16 * mt + 4 * lq], make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]));
+    if (wv == 0) fsh[blk & 1][l] = fl;
     __syncthreads();
-    // U[16 lq + s][rs + lr] = Up - W S^T = -(sum of the partials)
-    float ub[16];
+    // U[32 s + 8 lq + e][rs + lr] = Up - W S^T = -(sum of the partials), ub[8 s + e]
+    f32x16 ub;
+    float fu[16];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const int tok = 32 * (u >> 1) + 8 * lq + 4 * (u & 1);
       float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float4 x = ld4(&pb[v][lr][16 * lq + 4 * u]);
+        const float4 x = ld4(&pb[v][lr][tok]);
         sum.x -= x.x; sum.y -= x.y; sum.z -= x.z; sum.w -= x.w;
       }
+      const float4 f4 = ld4(&fsh[blk & 1][tok]);
       ub[4 * u] = sum.x; ub[4 * u + 1] = sum.y; ub[4 * u + 2] = sum.z; ub[4 * u + 3] = sum.w;
+      fu[4 * u] = f4.x; fu[4 * u + 1] = f4.y; fu[4 * u + 2] = f4.z; fu[4 * u + 3] = f4.w;
     }
-    {                                            // U^T for gdn_out: wave w writes tokens 16 lq + 4 w ..
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = w == 0 ? ub[e] : w == 1 ? ub[4 + e] : w == 2 ? ub[8 + e] : ub[12 + e];
-      st4(p.U + boff(blk) + (rs + lr) * kC + 16 * lq + 4 * w, make_float4(x[0], x[1], x[2], x[3]));
+    {                                            // U^T for gdn_out: wave w writes tokens 32 (w / 2) + 8 lq + 4 (w % 2) ..
+      st4(p.U + boff(blk) + (rs + lr) * kC + 32 * (w >> 1) + 8 * lq + 4 * (w & 1),
+          make_float4(ub[4 * w], ub[4 * w + 1], ub[4 * w + 2], ub[4 * w + 3]));
     }
-    const float dec = __expf(cur.gC);
+    // the update's B operand: U scaled by exp(g_C - g) per token, in three bf16 parts
+    bf16x8 u1[2], u2[2], u3[2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 a = sc[t] * dec;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.ka[t][u].x, ub[4 * u], a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.ka[t][u].y, ub[4 * u + 1], a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.ka[t][u].z, ub[4 * u + 2], a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.ka[t][u].w, ub[4 * u + 3], a, 0, 0, 0);
+      for (int e = 0; e < 8; ++e) x[e] = ub[8 * s2 + e] * fu[8 * s2 + e];
+      split3<8>(x, u1[s2], u2[s2], u3[s2]);
+    }
+    const float dec = __expf(gC);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 a = s2 == 0 ? sc[t] * dec : sc[t];
+        a = mfma16<8>(cur.ka[t][s2], u3[s2], a);
+        a = mfma16<8>(cur.ka[t][s2], u2[s2], a);
+        sc[t] = mfma16<8>(cur.ka[t][s2], u1[s2], a);
       }
-      sc[t] = a;
+      if (s2 == 0) fetch_k(nb1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   Ops opa, opb;                                  // operands of even and odd blocks
   fetch(0, opa);
-  for (int blk = 0; blk < p.nb; blk += 2) {
+  // pairs of blocks, then the odd one out: the loop is entered only from its top, so the
+  // wait counts at its head see just the odd block's loads as pending
+  int blk = 0;
+  for (; blk + 1 < p.nb; blk += 2) {
     step(blk, opa, opb);
-    if (blk + 1 >= p.nb) break;
     step(blk + 1, opb, opa);
   }
+  if (blk < p.nb) step(blk, opa, opb);
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    st4(p.state_out + (bh * D + rs + lr) * D + cw + 16 * t + 4 * lq, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
+  for (int t = 0; t < NT; ++t) st4(p.state_out + srow + 4 * t, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
 }
 
 // ---- gdn_out: the outputs of one block, transposed -------------------------------------
@@ -548,7 +638,7 @@ hipError_t launch_gdn_d(const GdnParams& p, hipStream_t st) {
                                            static_cast<int>(prep_lds<D>()));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gdn_prep<D>, dim3(p.nb, p.H, p.B), dim3(kThr), prep_lds<D>(), st, p);
-  hipLaunchKernelGGL(gdn_scan<D>, dim3(D / kGdnScanRows, p.H, p.B), dim3(kThr), 0, st, p);
+  hipLaunchKernelGGL(gdn_scan<D>, dim3((D / kGdnScanRows) * p.H * p.B), dim3(kThr), 0, st, p);
   hipLaunchKernelGGL(gdn_out<D>, dim3(p.nb, p.H, p.B), dim3(kThr), 0, st, p);
   return hipGetLastError();
 }

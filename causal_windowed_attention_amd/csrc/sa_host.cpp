@@ -1015,9 +1015,9 @@ sa_status gdn_layout(int32_t B, int32_t N, int32_t H, int32_t D, GdnLayout* L) {
   size_t off = 0;
   L->nb = static_cast<int32_t>(nb);
   L->g = off; off = align_up(off + bhb * sa::kGdnBlock * 4, kAlign);
-  L->W = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
+  L->W = off; off = align_up(off + bhb * sa::kGdnBlock * D * 6, kAlign);    // three bf16 parts
   L->Up = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
-  L->Kt = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
+  L->Kt = off; off = align_up(off + bhb * sa::kGdnBlock * D * 2, kAlign);   // bf16
   L->U = off; off = align_up(off + bhb * sa::kGdnBlock * D * 4, kAlign);
   L->Sst = off; off = align_up(off + bhb * static_cast<size_t>(D) * D * 4, kAlign);
   L->total = off > kAlign ? off : kAlign;        // never 0: 0 means unsupported sizes
@@ -1045,9 +1045,9 @@ sa_status gdn_forward_impl(const GdnLayout& L, int32_t batch, int32_t tokens, in
   p.state_in = state_in; p.state_out = state_out;
   p.out = out;
   p.g = reinterpret_cast<float*>(ws + L.g);
-  p.W = reinterpret_cast<float*>(ws + L.W);
+  p.W = ws + L.W;
   p.Up = reinterpret_cast<float*>(ws + L.Up);
-  p.Kt = reinterpret_cast<float*>(ws + L.Kt);
+  p.Kt = ws + L.Kt;
   p.U = reinterpret_cast<float*>(ws + L.U);
   p.Sst = reinterpret_cast<float*>(ws + L.Sst);
   p.B = batch; p.N = tokens; p.H = heads; p.D = head_dim; p.nb = L.nb;

@@ -153,9 +153,9 @@ struct GdnParams {
   void* out;              // [B, N, H, D] bf16
   // workspace (nb = ceil(N / kGdnBlock) blocks per (b, h))
   float* g;               // [B*H][nb*64] log of the cumulative gate within each block
-  float* W;               // [B*H][nb][64 * D] T diag(gam) K (in the scan's load order)
+  void* W;                // [B*H][nb][3 * 64 * D] bf16: T diag(gam) K in three bf16 parts (scan order)
   float* Up;              // [B*H][nb][D * 64] (T V)^T (in the scan's load order)
-  float* Kt;              // [B*H][nb][D * 64] (diag(gam_C / gam) K)^T (in the scan's load order)
+  void* Kt;               // [B*H][nb][D * 64] bf16: K^T (in the scan's load order)
   float* U;               // [B*H][nb][D][64] pseudo-values, transposed (U^T)
   float* Sst;             // [B*H][nb][D][D] state at each block start
   int32_t B, N, H, D, nb;

@@ -396,9 +396,18 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
   };
   // The next block's operands are loaded in pieces between this block's MFMA groups: issued
   // together they would fill the CU's vector memory queue and hold the wave until the whole
-  // 17 KB per wave had been accepted.
+  // 17 KB per wave had been accepted. For the same reason the block's starting state is
+  // stored after the exchange barrier, not among the loads.
   // (in the order of use: W part 2, 1, 0 of all four token tiles; then Up^T and the gates;
   // then K^T by 32-token step)
+  auto fetch_w2 = [&](int blk, Ops& o, int k) {  // loads 2 k, 2 k + 1 of fetch_w's order
+    const __bf16* wsrc = static_cast<const __bf16*>(p.W) + 3 * boff(blk);
+#pragma unroll
+    for (int i = 2 * k; i < 2 * k + 2; ++i) {
+      const int pt = 2 - i / 4, mt = i % 4;
+      o.wa[mt][pt] = *reinterpret_cast<const bfq*>(wsrc + (((w * 4 + mt) * 3 + pt) * 64 + l) * KQ);
+    }
+  };
   auto fetch_w = [&](int blk, Ops& o, int pt) {
     const __bf16* wsrc = static_cast<const __bf16*>(p.W) + 3 * boff(blk);
 #pragma unroll
@@ -423,9 +432,6 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
   };
   auto step = [&](int blk, const Ops& cur, Ops& nxt) {
     const int nb1 = min(blk + 1, p.nb - 1);
-    float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) st4(Sst + (srow - bh * D * D) + 4 * t, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
     // the slice as the B operand of W S^T, in three bf16 parts
     float sv[KQ];
 #pragma unroll
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
         const bfq& sp = k == 0 || k == 3 || k == 5 ? s1 : (k == 1 || k == 4 ? s2 : s3);
         acc[mt] = mfma16<KQ>(cur.wa[mt][wp[k]], sp, acc[mt]);
       }
-      if (k >= 1 && k <= 3) fetch_w(nb1, nxt, 3 - k);
+      fetch_w2(nb1, nxt, k);
       __builtin_amdgcn_sched_barrier(0);
     }
     const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.gl), 63));
@@ -459,6 +465,11 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
       st4(&pb[w][lr][16 * mt + 4 * lq], make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]));
     if (wv == 0) fsh[blk & 1][l] = fl;
     __syncthreads();
+    {                                            // this block's starting state, for gdn_out
+      float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D + (srow - bh * D * D);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st4(Sst + 4 * t, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
+    }
     // U[32 s + 8 lq + e][rs + lr] = Up - W S^T = -(sum of the partials), ub[8 s + e]
     f32x16 ub;
     float fu[16];

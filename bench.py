@@ -139,6 +139,46 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def write_reference(torch, traffic, reps=30):
+    """A plain device copy moving the same bytes as each write kernel (traffic = read + write
+    bytes; the copy reads and writes half each), timed two ways: with one HIP event pair around
+    each launch, as the library's kernel profile times its kernels, and back to back (one event
+    pair around reps launches)."""
+    def per_launch(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for _ in range(3):
+            fn()
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+    copies = {}
+    for name, nbytes in traffic.items():
+        src = torch.ones(nbytes // 2, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        ms = per_launch(lambda: dst.copy_(src))
+        ms_b2b = back_to_back(torch, lambda: dst.copy_(src), reps)
+        copies[name] = {"traffic_bytes": nbytes, "copy_ms": ms, "copy_ms_back_to_back": ms_b2b}
+        del src, dst
+    return copies
+
+
+def back_to_back(torch, fn, reps):
+    """Mean time of reps launches of fn issued back to back between one event pair."""
+    for _ in range(3):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def probe_mfma(torch, cwa, blocks=512, iters=20000, reps=3):
     """MFMA rate the part sustains on a pure v_mfma_f32_32x32x16_bf16 stream (fixed operands),
     timed with events around the library's measurement kernel."""
@@ -544,6 +584,14 @@ def main():
         if n:
             kern[name] = ms / n
     s.set_option(cwa.SA_OPT_PROFILE, 0)
+    # back to back: commits of a chunk (each writes the next ring slot) and refreshes
+    b2b_ms = {"kv_ring_append": back_to_back(torch, lambda: s.kv_append(pool[0][1], pool[0][2]), 20)}
+    flip = [0]
+
+    def refresh():
+        flip[0] ^= 1
+        s.rope_refresh(base + flip[0] * w.frames_per_chunk, 0)
+    b2b_ms["rope_refresh"] = back_to_back(torch, refresh, 20)
 
     mfma_probe = buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = None
     if not args.headline_only:
@@ -562,6 +610,22 @@ def main():
     elem = w.batch * nc * w.heads * w.head_dim * 2
     d_t = w.head_dim - 4 * (w.head_dim // 6)
     gbs = lambda bytes_, ms: bytes_ / (ms * 1e-3) / 1e9
+    write_bytes = {"rope_apply": 6 * elem, "kv_ring_append": 4 * elem,
+                   # temporal pairs of the window's rows, read and written
+                   "rope_refresh": 2 * w.batch * w.heads * w.window_chunks * nc * d_t * 2}
+    copy_ref = write_reference(torch, write_bytes)
+    write_kernels = {}
+    for name, nbytes in write_bytes.items():
+        if name not in kern:
+            continue
+        ms, c = kern[name], copy_ref[name]
+        write_kernels[name] = {"ms": ms, "gbs": gbs(nbytes, ms), "copy_gbs": gbs(nbytes, c["copy_ms"]),
+                               "frac_of_copy": c["copy_ms"] / ms}
+        b2b = b2b_ms.get(name)
+        if b2b is not None:
+            write_kernels[name].update({"ms_back_to_back": b2b, "gbs_back_to_back": gbs(nbytes, b2b),
+                                        "copy_gbs_back_to_back": gbs(nbytes, c["copy_ms_back_to_back"]),
+                                        "frac_of_copy_back_to_back": c["copy_ms_back_to_back"] / b2b})
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(w.name, src_hash)
     attend_ms = attn_ms + kern.get("rope_apply", 0.0) + kern.get("attn_combine", 0.0)
@@ -602,13 +666,11 @@ def main():
             "kernel_source_hash": src_hash,
         },
         "kernels_ms": kern,
-        "kernels_gbs": {
-            "rope_apply": gbs(6 * elem, kern["rope_apply"]) if "rope_apply" in kern else None,
-            "kv_ring_append": gbs(4 * elem, kern["kv_ring_append"]) if "kv_ring_append" in kern else None,
-            # temporal pairs of the window's rows, read and written
-            "rope_refresh": gbs(2 * w.batch * w.heads * w.window_chunks * nc * d_t * 2,
-                                kern["rope_refresh"]) if "rope_refresh" in kern else None,
-        },
+        "kernels_gbs": {name: v["gbs"] for name, v in write_kernels.items()},
+        # per-launch event timing (the library's profile) and, for the kernels a call can issue
+        # alone, back-to-back launches; a device copy of the same bytes under each timing is
+        # the practical ceiling
+        "write_kernels": write_kernels,
         "step_zero_copy_commit": {"ms_per_step": dt_zc * 1e3 / args.steps,
                                   "tokens_per_s": w.batch * nc * args.steps / dt_zc,
                                   "what": "attend + sa_kv_append(NULL, NULL): the staged K/V committed "

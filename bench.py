@@ -457,13 +457,13 @@ def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), st
                   "rope_ms": rope_ms / max(nr, 1), "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
                   "call_p50_ms": model[n]["p50_ms"], "call_p99_ms": model[n]["p99_ms"]}
     fits = [n for n in sizes if model[n]["p99_ms"] * (1.0 + margin) <= deadline_ms]
-    # among the sizes that meet the deadline, the one with the highest throughput (a size that
-    # leaves the last wave of workgroups mostly empty can be slower per token than a smaller one)
-    n = max(fits, key=lambda m: m / model[m]["p50_ms"]) if fits else min(sizes)
+    # the largest batch that meets the deadline: the most work per call within the latency bound
+    n = max(fits) if fits else min(sizes)
     t = timed_calls(n, calls)
     sched = {"deadline_ms_per_call": deadline_ms, "model": "p99 of %d calls per size, measured at start-up" % model_calls,
              "margin": margin, "model_p99_ms": {k: v["p99_ms"] for k, v in model.items()},
-             "chosen_streams": n, "deadline_met_by_model": bool(fits),
+             "chosen_streams": n, "rule": "largest n with model p99 x (1 + margin) <= deadline",
+             "deadline_met_by_model": bool(fits),
              "predicted_p99_ms": model[n]["p99_ms"], "calls": calls,
              "p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)), "max_ms": float(t.max()),
              "miss_rate": float(np.mean(t > deadline_ms)), "mean_jitter_ms": float(np.mean(np.abs(np.diff(t)))),
@@ -472,6 +472,11 @@ def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), st
         s.close()
     return {"workload": name, "streams": res, "deadline_schedule": sched,
             "kernel": "chunk_attention_bf16_d128_ppg"}
+
+
+def note(msg):
+    """Progress of a long run, on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -515,6 +520,7 @@ def main():
         s.kv_append(k, v)
 
     # ---- full stream from empty (warm-up chunks included), once -----------------
+    note(f"{w.name}: stream from empty, then {args.warmup} + {args.steps} timed steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(w.n_chunks):
@@ -562,6 +568,7 @@ def main():
     pct = lambda q, v=step_ms: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
     # ---- per-kernel durations: HIP events on the launch stream ------------------
+    note("per-kernel durations")
     s.set_option(cwa.SA_OPT_PROFILE, 1)
     for k_id in range(cwa.SA_K_COUNT):
         s.profile_read(k_id, reset=True)
@@ -595,12 +602,19 @@ def main():
 
     mfma_probe = buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = None
     if not args.headline_only:
+        note("mfma probe")
         mfma_probe = probe_mfma(torch, cwa)
+        note("moving buffer")
         buffer_res = bench_buffer(torch, cwa, synth)
+        note("fp8 cache")
         fp8_res = bench_fp8(torch, cwa, synth)
+        note("gdn block")
         gdn_res = bench_gdn(torch, cwa, synth)
+        note("bf16 shapes")
         configs_res = bench_configs(torch, cwa, synth)
+        note("steps mode")
         steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
+        note("ragged batches")
         batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
 
     nk = st["visible_keys"]
@@ -695,6 +709,7 @@ def main():
         "batch_attend": batch_res,
     }
     if not args.no_cpu_baseline:
+        note("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         if configs_res is not None:
             # the oracle beside every bf16 shape: heads of one steady chunk for about 1.5 s each

@@ -180,23 +180,38 @@ def back_to_back(torch, fn, reps):
 
 
 def probe_mfma(torch, cwa, blocks=512, iters=20000, reps=3):
-    """MFMA rate the part sustains on a pure v_mfma_f32_32x32x16_bf16 stream (fixed operands),
-    timed with events around the library's measurement kernel."""
+    """The MFMA rate the part sustains on a pure v_mfma_f32_32x32x16_bf16 stream, on this machine
+    and in this run, for two kinds of operands: fixed per lane (benign, low toggle) and normally
+    distributed bf16 data that changes between consecutive MFMAs (the realistic case); timed
+    with events around the library's measurement kernels (best of reps)."""
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(11)
+    ops = torch.randn(6 * 64 * 8, generator=g).to(torch.bfloat16).cuda()
     flops = blocks * 4 * iters * 8 * 32768.0
-    cwa.sa_probe_mfma_bf16(out, blocks, iters)
-    best = None
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        cwa.sa_probe_mfma_bf16(out, blocks, iters)
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b)
-        best = ms if best is None else min(best, ms)
-    tf = flops / (best * 1e-3) / 1e12
-    return {"tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS, "blocks": blocks, "iters": iters,
-            "operands": "fixed per lane (benign, low toggle)"}
+    res = {"blocks": blocks, "iters": iters}
+    for kind, launch in (("fixed_operands", lambda: cwa.sa_probe_mfma_bf16(out, blocks, iters)),
+                         ("normal_operands", lambda: cwa.sa_probe_mfma_bf16_data(out, ops, blocks, iters))):
+        launch()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            launch()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        tf = flops / (best * 1e-3) / 1e12
+        res[kind] = {"tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+    return res
+
+
+def box_identity(torch):
+    """Which box a run measured: host name, device name and the device's UUID."""
+    import socket
+    p = torch.cuda.get_device_properties(0)
+    return {"host": socket.gethostname(), "device": p.name, "uuid": str(getattr(p, "uuid", "")),
+            "gcn_arch": getattr(p, "gcnArchName", "")}
 
 
 def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20, steps_mode=False):
@@ -600,10 +615,10 @@ def main():
         s.rope_refresh(base + flip[0] * w.frames_per_chunk, 0)
     b2b_ms["rope_refresh"] = back_to_back(torch, refresh, 20)
 
-    mfma_probe = buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = None
+    buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = None
+    note("mfma probe")
+    mfma_probe = probe_mfma(torch, cwa)
     if not args.headline_only:
-        note("mfma probe")
-        mfma_probe = probe_mfma(torch, cwa)
         note("moving buffer")
         buffer_res = bench_buffer(torch, cwa, synth)
         note("fp8 cache")
@@ -678,6 +693,9 @@ def main():
             "flops_per_launch": flops,
             "mean_ms": attn_ms,
             "kernel_source_hash": src_hash,
+            # the same rate against this box's measured pure-MFMA ceiling on normally distributed
+            # operands (mfma_probe.normal_operands, same run)
+            "frac_of_measured_ceiling": achieved / mfma_probe["normal_operands"]["tflops"],
         },
         "kernels_ms": kern,
         "kernels_gbs": {name: v["gbs"] for name, v in write_kernels.items()},
@@ -701,6 +719,7 @@ def main():
         "chunk_budget_ms": {fps: w.frames_per_chunk * 1000.0 / fps for fps in (24, 16)},
         "steps_within_chunk_budget_p99": {fps: w.frames_per_chunk * 1000.0 / fps / pct(0.99) for fps in (24, 16)},
         "mfma_probe": mfma_probe,
+        "box": box_identity(torch),
         "configs": configs_res,
         "fp8_attend": fp8_res,
         "gdn_forward": gdn_res,

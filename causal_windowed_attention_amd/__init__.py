@@ -25,7 +25,7 @@ __all__ = [
     "SaError", "make_config", "sa_status_string", "sa_config_check", "sa_workspace_bytes",
     "sa_stream_create", "sa_stream_destroy", "sa_chunk_attend", "sa_kv_append",
     "sa_rope_refresh", "sa_sink_update", "sa_stream_query", "sa_stream_slot",
-    "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16",
+    "sa_stream_layout", "sa_stream_set_option", "sa_profile_read", "sa_probe_mfma_bf16", "sa_probe_mfma_bf16_data",
     "sa_gdn_workspace_bytes", "sa_gdn_forward", "sa_gdn_forward_noalloc", "gdn_forward",
     "sa_buffer_attend", "sa_buffer_plan", "sa_batch_attend", "Stream",
     "SA_F32", "SA_BF16", "SA_FP8", "SA_REFRESH_SHIFT_SINK", "SA_OPT_KV_SPLITS", "SA_OPT_PROFILE",
@@ -197,6 +197,18 @@ def sa_batch_attend(handles, qs, ks, vs, outs, lses=None, stream=None) -> None:
 def sa_probe_mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
     """Launch the pure-MFMA measurement kernel (out: float32 device tensor of blocks*256)."""
     _check(L.load().sa_probe_mfma_bf16(_ptr(out), blocks, iters, _stream_ptr(stream)), "sa_probe_mfma_bf16")
+
+
+def sa_probe_mfma_bf16_data(out, operands, blocks: int, iters: int, stream=None) -> None:
+    """The pure-MFMA measurement on data operands (operands: a bf16 device tensor of 6*64*8
+    values, runs 0-3 the A operands and 4-5 the B operands of every wave's lanes)."""
+    import torch
+    if operands.dtype != torch.bfloat16 or operands.numel() != 6 * 64 * 8 or not operands.is_contiguous():
+        raise ValueError("operands: a contiguous bf16 tensor of 3072 values")
+    if operands.device != out.device:
+        raise ValueError("operands and out must be on one device")
+    _check(L.load().sa_probe_mfma_bf16_data(_ptr(out), _ptr(operands), blocks, iters, _stream_ptr(stream)),
+           "sa_probe_mfma_bf16_data")
 
 
 def sa_gdn_workspace_bytes(batch: int, tokens: int, heads: int, head_dim: int) -> int:

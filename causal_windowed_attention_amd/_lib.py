@@ -93,6 +93,7 @@ SIGNATURES = {
     "sa_profile_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(_I64), _I32]),
     "sa_probe_mfma_bf16": (ctypes.c_int, [_P, _I32, _I32, _P]),
+    "sa_probe_mfma_bf16_data": (ctypes.c_int, [_P, _P, _I32, _I32, _P]),
     "sa_buffer_attend": (ctypes.c_int, [_P, _P, _P, _P, _I32, _U32, _P, _P, _P]),
     "sa_buffer_plan": (ctypes.c_int, [_P, _I32, _U32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                       ctypes.POINTER(_I32)]),

@@ -1584,6 +1584,31 @@ __global__ __launch_bounds__(kThreads) void mfma_probe_bf16(float* out, int iter
   out[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = sum;
 }
 
+// The same MFMA stream on caller data: lane l of every wave takes four A and two B operands
+// (16 bytes each, run i of 64 lanes at ops[64 i + l]) and MFMA j of a round uses A[j % 4] and
+// B[j % 2], so the operand values change from one MFMA to the next as in a real product.
+__global__ __launch_bounds__(kThreads) void mfma_probe_bf16_data(float* out, const bf16x8* ops, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = ops[64 * i + lane];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b[i] = ops[64 * (4 + i) + lane];
+  f32x16 c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[j & 1], c[j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c[j][i];
+  out[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st) {
@@ -1616,6 +1641,12 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
 
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st) {
   hipLaunchKernelGGL(mfma_probe_bf16, dim3(blocks), dim3(kThreads), 0, st, out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe_data(float* out, const void* ops, int blocks, int iters, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_probe_bf16_data, dim3(blocks), dim3(kThreads), 0, st, out, static_cast<const bf16x8*>(ops),
+                     iters);
   return hipGetLastError();
 }
 

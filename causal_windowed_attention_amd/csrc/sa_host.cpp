@@ -995,6 +995,14 @@ sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* 
              ? SA_OK : SA_ERR_DEVICE;
 }
 
+sa_status sa_probe_mfma_bf16_data(float* d_out, const void* d_operands, int32_t blocks, int32_t iters, void* stream) {
+  if (d_out == nullptr || d_operands == nullptr || (reinterpret_cast<uintptr_t>(d_operands) & 15u) != 0 ||
+      blocks < 1 || blocks > (1 << 20) || iters < 1)
+    return SA_ERR_INVALID_ARGUMENT;
+  return sa::launch_mfma_probe_data(d_out, d_operands, blocks, iters, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SA_OK : SA_ERR_DEVICE;
+}
+
 }  // extern "C"
 
 // ---- gated delta rule (GDN) forward ----------------------------------------------------------

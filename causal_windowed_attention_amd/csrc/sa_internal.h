@@ -179,6 +179,7 @@ hipError_t launch_chunk_attention(const AttnParams& p, int dtype, hipStream_t st
 hipError_t launch_attn_combine(const CombineParams& p, int dtype, hipStream_t st);
 hipError_t launch_attn_sk_combine(const AttnParams& p, hipStream_t st);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
+hipError_t launch_mfma_probe_data(float* out, const void* ops, int blocks, int iters, hipStream_t st);
 hipError_t launch_gdn_forward(const GdnParams& p, hipStream_t st);
 // Bytes of the fixed device scratch of the workspace-free GDN forward, and its address on the
 // device of stream st (null: the current device), looked up once per device.

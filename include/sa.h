@@ -360,6 +360,18 @@ sa_status sa_profile_read(sa_stream* s, int32_t kernel_id, double* total_ms, int
 sa_status sa_probe_mfma_bf16(float* d_out, int32_t blocks, int32_t iters, void* stream);
 
 /*
+ * The same measurement on data operands: d_operands (caller-owned device memory, 16-byte
+ * aligned) holds 6 runs of 64 lanes x 8 bf16; every wave's lane l takes runs 0-3 as four A
+ * operands and runs 4-5 as two B operands, and MFMA j of a round uses A[j % 4] and B[j % 2],
+ * so operand values change between consecutive MFMAs as in a real product (normally
+ * distributed operands make it the realistic, high-power case). Same flop count, output and
+ * asynchrony as sa_probe_mfma_bf16; SA_ERR_INVALID_ARGUMENT also for a null or unaligned
+ * d_operands.
+ */
+sa_status sa_probe_mfma_bf16_data(float* d_out, const void* d_operands, int32_t blocks, int32_t iters,
+                                  void* stream);
+
+/*
  * Gated delta rule (GDN linear attention; SANA-Streaming, "Transformer a diffusione
  * ibrido": most blocks keep a fixed-size recurrent state per head, updated as the
  * stream advances, and only the final state is kept between chunks). The pages give no

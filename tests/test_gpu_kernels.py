@@ -329,3 +329,37 @@ def test_mfma_probe_computes_the_product():
     got = host(out).reshape(blocks * 4, 64)
     assert np.all(np.isfinite(got))
     np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=1e-4)
+
+
+@pytest.mark.gpu
+def test_mfma_probe_on_data_operands_computes_the_product():
+    """The data-operand measurement kernel takes lane l's A operands from runs 0-3 and B
+    operands from runs 4-5 of the caller's buffer and MFMA j uses A[j % 4], B[j % 2]: every
+    lane's output equals iters * sum over j < 8 of its 16 entries of A[j % 4] B[j % 2]."""
+    blocks, iters = 4, 16
+    g = np.random.default_rng(5)
+    ops = _bf16_round(g.standard_normal((6, 64, 8)))
+    dev_ops = torch.from_numpy(ops.astype(np.float32)).to(torch.bfloat16).cuda().reshape(-1)
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    cwa.sa_probe_mfma_bf16_data(out, dev_ops, blocks, iters)
+    torch.cuda.synchronize()
+    def mat_a(i):
+        a = np.zeros((32, 16))
+        for lane in range(64):
+            a[lane % 32, 8 * (lane // 32):8 * (lane // 32) + 8] = ops[i, lane]
+        return a
+    def mat_b(i):
+        b = np.zeros((16, 32))
+        for lane in range(64):
+            b[8 * (lane // 32):8 * (lane // 32) + 8, lane % 32] = ops[4 + i, lane]
+        return b
+    want = np.zeros(64)
+    for j in range(8):
+        c = mat_a(j % 4) @ mat_b(j % 2)
+        for lane in range(64):
+            rows = [8 * (r // 4) + 4 * (lane // 32) + r % 4 for r in range(16)]
+            want[lane] += iters * c[rows, lane % 32].sum()
+    got = host(out).reshape(blocks * 4, 64)
+    assert np.all(np.isfinite(got))
+    scale = iters * 8 * 16 * 16 * np.abs(ops).max() ** 2       # bound on the summed magnitudes
+    np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=0, atol=1e-5 * scale)

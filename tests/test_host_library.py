@@ -372,6 +372,11 @@ def test_mfma_probe_argument_errors():
     assert lib.sa_probe_mfma_bf16(fake, 0, 1, None) == L.SA_ERR_INVALID_ARGUMENT
     assert lib.sa_probe_mfma_bf16(fake, 1, 0, None) == L.SA_ERR_INVALID_ARGUMENT
     assert lib.sa_probe_mfma_bf16(fake, (1 << 20) + 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16_data(fake, None, 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16_data(None, fake, 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16_data(fake, ctypes.c_void_p(fake.value + 8), 1, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16_data(fake, fake, 0, 1, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert lib.sa_probe_mfma_bf16_data(fake, fake, 1, 0, None) == L.SA_ERR_INVALID_ARGUMENT
 
 
 def test_batch_attend_planning_semantics_and_errors():

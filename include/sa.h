@@ -381,16 +381,18 @@ sa_status sa_probe_mfma_bf16_data(float* d_out, const void* d_operands, int32_t 
  * S of size D x D (value rows, key columns) per (b, h).
  *
  * sa_gdn_workspace_bytes: device workspace sa_gdn_forward needs for these sizes (0 for
- * unsupported sizes): per 64-token block of each (b, h), fp32 gates, three 64 x D
- * products, the pseudo-values and the block's starting state (D x D).
+ * unsupported sizes): per 64-token block of each (b, h), fp32 gates, the block's
+ * products in the order the state scan reads them (T diag(gamma) K as three bf16 parts,
+ * (T V)^T in fp32, K^T in bf16), the pseudo-values and the block's starting state (D x D).
  *
  * sa_gdn_forward: q, k, v: [B, N, H, D] bf16 (token-major, like sa_chunk_attend's
  * inputs; q and k as the caller prepared them, GDN normalises them to unit length);
  * alpha, beta: [B, H, N] float32 (alpha in (0, 1], beta in [0, 1]); state_in:
  * [B, H, D, D] float32 or NULL for zeros; state_out: [B, H, D, D] float32, may equal
  * state_in; out: [B, N, H, D] bf16. N may be any count >= 0 (a ragged last block is
- * padded with alpha = 1, beta = 0). Arithmetic is fp32 (chunkwise: 64-token blocks,
- * a triangular solve per block, the state carried block to block). All buffers are
+ * padded with alpha = 1, beta = 0). Arithmetic is fp32-accurate (chunkwise: 64-token
+ * blocks, a triangular solve per block, the state carried block to block; products on
+ * the bf16 MFMA with fp32 operands split into three bf16 parts and fp32 accumulation). All buffers are
  * the caller's; nothing is allocated. With N = 0 only state_in / state_out are used
  * (the state passes through; the others may be NULL). Errors: SA_ERR_INVALID_ARGUMENT
  * for NULL or misaligned pointers (16 bytes for the bf16 tensors, the states and the

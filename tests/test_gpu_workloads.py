@@ -37,18 +37,21 @@ def _rows(nc, seed):
     return np.unique(r)
 
 
-@pytest.mark.parametrize("name", list(CHECKS))
-def test_workload_sampled_parity(name):
+@pytest.mark.parametrize("name,variant", [(n, 0) for n in CHECKS] + [("wan1.3b", 4)])
+def test_workload_sampled_parity(name, variant):
+    """variant: SA_OPT_ATTN_VARIANT (0: the default ping-pong kernel; 4: the software-pipelined
+    kernel, opt-in, held to the same bar at full size on the headline shape)."""
     w = synth.WORKLOADS[name]
     checks = set(CHECKS[name])
     heads = sorted({0, w.heads // 2, w.heads - 1})
     rows = _rows(w.tokens_per_chunk, w.cfg_id)
     pooled = w.n_chunks > 100
     distinct = synth.distinct_set_for(w, checks) if pooled else None
-    say(f"workload {name}: B {w.batch} H {w.heads} Nc {w.tokens_per_chunk} S {w.sink_chunks} "
+    say(f"workload {name} (attention variant {variant}): B {w.batch} H {w.heads} Nc {w.tokens_per_chunk} S {w.sink_chunks} "
         f"W {w.window_chunks} chunks {w.n_chunks} refresh {w.refresh_every}; heads {heads}")
 
     s = cwa.Stream(config_for(w))
+    s.set_option(cwa.SA_OPT_ATTN_VARIANT, variant)
     spec = spec_for(w, heads)
     hist = HistoryOracle(spec)
     emu = RingOracle(spec, storage="bf16") if w.outlier_channels else None

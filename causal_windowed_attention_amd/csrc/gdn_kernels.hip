@@ -58,6 +58,21 @@ __device__ __forceinline__ int up_index(int r, int i) {     // Up^T[r][i], r row
   const int l = (r & 15) + 16 * (i >> 4);
   return ((((r >> 4) * 4 + ((i & 15) >> 2)) * 64 + l) << 2) + (i & 3);
 }
+// Storage order of what the scan leaves for gdn_out, in gdn_out's operand order (32-row
+// tiles of the 32x32x16 MFMA, lane l = lc + 32 hf takes row 32 tile + lc): every load of
+// gdn_out reads 64 lanes x 16 bytes contiguously.
+//   block state S0[r][k], run (tile, s, half): lane's k = 16 s + 8 hf + 4 half + e
+//   U^T[r][t], run (tile, jt, s2, half):       lane's t = 32 jt + 16 s2 + 4 hf + 8 half + e
+template <int D>
+__device__ __forceinline__ int s0_index(int r, int k) {      // k a multiple of 4: 4 floats from here
+  constexpr int KS = D / 16;
+  const int l = (r & 31) + 32 * ((k >> 3) & 1);
+  return ((((r >> 5) * KS + (k >> 4)) * 2 + ((k >> 2) & 1)) * 64 + l) * 4;
+}
+__device__ __forceinline__ int ut_index(int r, int t) {      // t a multiple of 4: 4 floats from here
+  const int l = (r & 31) + 32 * ((t >> 2) & 1);
+  return (((((r >> 5) * 2 + (t >> 5)) * 2 + ((t >> 4) & 1)) * 2 + ((t >> 3) & 1)) * 64 + l) * 4;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -465,10 +480,11 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
       st4(&pb[w][lr][16 * mt + 4 * lq], make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]));
     if (wv == 0) fsh[blk & 1][l] = fl;
     __syncthreads();
-    {                                            // this block's starting state, for gdn_out
-      float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D + (srow - bh * D * D);
+    {                                            // this block's starting state, for gdn_out (s0_index)
+      float* Sst = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) st4(Sst + 4 * t, make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
+      for (int t = 0; t < NT; ++t)
+        st4(Sst + s0_index<D>(rs + lr, cw + KQ * lq + 4 * t), make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]));
     }
     // U[32 s + 8 lq + e][rs + lr] = Up - W S^T = -(sum of the partials), ub[8 s + e]
     f32x16 ub;
@@ -486,8 +502,8 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
       ub[4 * u] = sum.x; ub[4 * u + 1] = sum.y; ub[4 * u + 2] = sum.z; ub[4 * u + 3] = sum.w;
       fu[4 * u] = f4.x; fu[4 * u + 1] = f4.y; fu[4 * u + 2] = f4.z; fu[4 * u + 3] = f4.w;
     }
-    {                                            // U^T for gdn_out: wave w writes tokens 32 (w / 2) + 8 lq + 4 (w % 2) ..
-      st4(p.U + boff(blk) + (rs + lr) * kC + 32 * (w >> 1) + 8 * lq + 4 * (w & 1),
+    {                                            // U^T for gdn_out (ut_index): wave w writes tokens 32 (w / 2) + 8 lq + 4 (w % 2) ..
+      st4(p.U + boff(blk) + ut_index(rs + lr, 32 * (w >> 1) + 8 * lq + 4 * (w & 1)),
           make_float4(ub[4 * w], ub[4 * w + 1], ub[4 * w + 2], ub[4 * w + 3]));
     }
     // the update's B operand: U scaled by exp(g_C - g) per token, in three bf16 parts
@@ -539,7 +555,8 @@ __global__ __launch_bounds__(kThr) void gdn_scan(GdnParams p) {
 // 16-row step is the token order tau(e) = 8 (e / 4) + 4 (l / 32) + e % 4, so the U^T operand
 // is read in that order (two 4-token runs per lane). Wave w takes query tile w % 2 and
 // Dv tiles [CTW (w / 2), CTW (w / 2) + CTW) of 32 rows; every operand comes straight from
-// global memory (L2), only the gates go through LDS.
+// global memory (L2), only the gates go through LDS. The scan stores S0 and U^T in this
+// kernel's operand order (s0_index, ut_index), so each of their loads is one 1 KB run.
 template <int D>
 __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
   __shared__ float gs[kC];
@@ -556,7 +573,7 @@ __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
   const __bf16* kb = static_cast<const __bf16*>(p.k) + base;
   const size_t boff = (bh * p.nb + blk) * static_cast<size_t>(kC) * D;
   const float* S0 = p.Sst + (bh * p.nb + blk) * static_cast<size_t>(D) * D;
-  const float* Ut = p.U + boff;                                     // U^T: [D][64]
+  const float* Ut = p.U + boff;                                     // U^T in ut_index order
   if (tid < kC) gs[tid] = p.g[bh * (static_cast<size_t>(p.nb) * kC) + t0 + tid];
 
   const int qi = 32 * it + lc;                                      // this lane's query (column)
@@ -598,9 +615,9 @@ __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
     f32x16 o = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const float* src = S0 + static_cast<size_t>(c) * D + 16 * s + 8 * hf;
+      const float* src = S0 + s0_index<D>(c, 16 * s + 8 * hf);   // the second half 256 floats on
       float x[8];
-      unpack8(ld4(src), ld4(src + 4), x);
+      unpack8(ld4(src), ld4(src + 256), x);
       bf16x8 ah, al;
       split_bf16(x, ah, al);
       o = mfma_bf16(ah, bq[s], o);
@@ -612,9 +629,9 @@ __global__ __launch_bounds__(kThr) void gdn_out(GdnParams p) {
       if (jt > it) break;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const float* src = Ut + c * kC + 32 * jt + 16 * s2 + 4 * hf;
+        const float* src = Ut + ut_index(c, 32 * jt + 16 * s2 + 4 * hf);   // second run 256 floats on
         float x[8];
-        unpack8(ld4(src), ld4(src + 8), x);
+        unpack8(ld4(src), ld4(src + 256), x);
         bf16x8 ah, al;
         split_bf16(x, ah, al);
         o = mfma_bf16(ah, pbh[jt][s2], o);

@@ -256,7 +256,7 @@ def bench_buffer(torch, cwa, synth, name="long512p", n=4, steps=20, steps_mode=F
     return {"workload": name, "mode": "steps" if steps_mode else "moving buffer",
             "buffer_chunks": n, "tokens_per_call": w.batch * n * nc,
             "tokens_per_s": w.batch * n * nc / (call_ms * 1e-3), "ms_per_call": call_ms,
-            "attention_ms": attn_ms, "rope_apply_ms_per_chunk": rope_ms / max(nr, 1),
+            "attention_ms": attn_ms, "rope_apply_ms_per_call": rope_ms / max(nr, 1),
             "visible_keys_per_chunk": keys, "flops_per_call": flops, "tflops": tf,
             "frac_of_peak": tf / PEAK_BF16_TFLOPS, "kernel": "chunk_attention_bf16_d128_ppg"}
 

@@ -34,6 +34,7 @@ using sa::CombineParams;
 using sa::RefreshParams;
 using sa::RopeWriteParams;
 static_assert(sa::kMaxBatchStreams == SA_MAX_BATCH_STREAMS, "one batched RoPE launch per sa_batch_attend");
+static_assert(sa::kMaxBatchStreams >= SA_MAX_BUFFER_CHUNKS, "one batched RoPE launch per sa_buffer_attend");
 
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxPosition = 1 << 30;   // guard against int32 overflow when max_t == 0
@@ -825,18 +826,36 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
 
   if (!s->planning()) {
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    for (int j = 0; j < n_chunks; ++j) {         // rotate and store buffer chunk j
+    // Rotate and store every buffer chunk in one launch: entry j of the batched rope_apply is
+    // chunk j, with its inputs, Q scratch rows and cache slot offset to chunk j and its
+    // frames at temporal positions t_next + j F on.
+    {
       RopeWriteParams rp;
       base_write_params(s, &rp);
-      rp.q = q; rp.k = k; rp.v = v;
-      rp.qrot = s->qscratch();
-      rp.in_tokens = n_chunks * d.Nc;
-      rp.in_tok0 = j * d.Nc;
-      rp.row0 = (d.buf_slot0 + j) * d.Nc;
-      rp.q_rows = n_chunks * d.Nc;
-      rp.q_row0 = j * d.Nc;
-      fill_temporal(d, static_cast<int64_t>(s->t_next) + static_cast<int64_t>(j) * d.F, d.F, rp.t_cs);
-      st = timed(s, SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply(rp, d.dtype, hs); });
+      sa::RopeBatchParams rb;
+      std::memset(&rb, 0, sizeof(rb));
+      rb.h_cs = rp.h_cs; rb.w_cs = rp.w_cs;
+      rb.k_bh_stride = rp.k_bh_stride; rb.vt_bh_stride = rp.vt_bh_stride;
+      rb.key_stride = rp.key_stride; rb.n_tokens = d.Nc; rb.in_tokens = n_chunks * d.Nc;
+      rb.B = rp.B; rb.H = rp.H; rb.D = rp.D; rb.Hf = rp.Hf; rb.Wf = rp.Wf;
+      rb.dt = rp.dt; rb.dh = rp.dh; rb.dw = rp.dw; rb.n_frames = d.F; rb.q_rows = n_chunks * d.Nc;
+      rb.q_scale = rp.q_scale;
+      rb.n = n_chunks;
+      for (int j = 0; j < d.dt / 2; ++j) rb.theta_t[j] = freq(d, d.dt, j);
+      const size_t in_elem = d.dtype == SA_F32 ? 4 : 2;
+      const size_t chunk_in = static_cast<size_t>(d.Nc) * d.H * d.D * in_elem;    // bytes of one chunk's tokens
+      const size_t chunk_q = static_cast<size_t>(d.Nc) * d.D * d.elem;             // bytes of one chunk's Q rows
+      for (int j = 0; j < n_chunks; ++j) {
+        rb.q[j] = static_cast<const char*>(q) + j * chunk_in;
+        rb.k[j] = static_cast<const char*>(k) + j * chunk_in;
+        rb.v[j] = static_cast<const char*>(v) + j * chunk_in;
+        rb.qrot[j] = static_cast<char*>(s->qscratch()) + j * chunk_q;
+        rb.kcache[j] = s->kcache();
+        rb.vtcache[j] = s->vtcache();
+        rb.row0[j] = (d.buf_slot0 + j) * d.Nc;
+        rb.t0[j] = s->t_next + j * d.F;
+      }
+      st = timed(s, SA_K_ROPE_APPLY, hs, [&] { return sa::launch_rope_apply_batch(rb, d.dtype, hs); });
       if (st != SA_OK) return st;
     }
     AttnParams ap;

@@ -8,8 +8,8 @@
 // The rotation is RoFormer's per channel pair; the pages name 3D (t, h, w) RoPE
 // offsets and their periodic re-basing at chunk boundaries (StreamDiffusionV2,
 // "Sommario tecnico" 2.A.2). cos/sin come from host fp64 tables rounded to
-// fp32 (spatial tables in the workspace, the chunk's temporal table by value),
-// so no device trigonometry runs. Arithmetic is fp32; stores round to the cache
+// fp32 (spatial tables in the workspace, staged in LDS by each block when they
+// fit; the chunk's temporal table by value), so no device trigonometry runs. Arithmetic is fp32; stores round to the cache
 // type (bf16: round to nearest even; fp8: E4M3 of the OCP 8-bit float format,
 // clamped to +-448 and rounded to nearest even by v_cvt_pk_fp8_f32, whose
 // unclamped result above 464 would be NaN). Inputs are fp32 for an fp32 cache
@@ -49,14 +49,28 @@ template <> __device__ __forceinline__ fp8e4m3 from_f<fp8e4m3>(float x) {
   return fp8e4m3{static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xff)};
 }
 
-// (cos, sin) of the pair starting at even channel ch of a token at (frame, y, x).
+// Spatial (cos, sin) pairs a block stages in LDS: the h table ([Hf][d_h/2]) followed by the
+// w table ([Wf][d_w/2]), when both fit and the w table follows the h table in memory.
+constexpr int kMaxLdsSpatialPairs = 2048;
+
+// (cos, sin) of the pair starting at even channel ch of a token at (frame, y, x); the spatial
+// pairs come from s_hw (LDS) when hw_lds, else from the tables in global memory.
 template <typename P>
-__device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const P& p, int ch, int f, int y, int x) {
+__device__ __forceinline__ float2 pair_cs(const float2* s_tcs, const float2* s_hw, bool hw_lds, const P& p, int ch,
+                                          int f, int y, int x) {
   if (ch < p.dt) return s_tcs[f * (p.dt >> 1) + (ch >> 1)];
   ch -= p.dt;
-  if (ch < p.dh) return p.h_cs[y * (p.dh >> 1) + (ch >> 1)];
-  ch -= p.dh;
-  return p.w_cs[x * (p.dw >> 1) + (ch >> 1)];
+  const int nh = p.Hf * (p.dh >> 1);
+  const int i = ch < p.dh ? y * (p.dh >> 1) + (ch >> 1) : nh + x * (p.dw >> 1) + ((ch - p.dh) >> 1);
+  if (hw_lds) return s_hw[i];
+  return i < nh ? p.h_cs[i] : p.w_cs[i - nh];
+}
+
+// 16 bytes per lane from the `bytes` bytes at src + voffset into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds: no VGPRs; lanes past the end read zeros).
+__device__ __forceinline__ void lds_copy16(const void* src, int bytes, int voffset, void* lds) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
 // Rotated pairs of one 16-byte input vector, rounded to the storage type TS. SCALED:
@@ -138,10 +152,24 @@ __device__ __forceinline__ void rope_write_core(const P& p, int b, const void* q
   constexpr int MAXJ = 32 / VN;                  // K/Q vectors per thread (D <= 128)
   __shared__ float2 s_tcs[kMaxTemporalPairs];
   __shared__ int s_fyx[kTileTokens][3];          // (frame, y, x) of the tile's tokens
+  __shared__ __attribute__((aligned(16))) float2 s_hw[kMaxLdsSpatialPairs];
 
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * kTileTokens;
   const int h = blockIdx.y;
+
+  // ---- spatial tables -> LDS, issued before the data loads -------------------------
+  // The rotation's table lookups then read LDS after the barrier instead of going out to
+  // memory behind this block's data loads.
+  const int nh = p.Hf * (p.dh >> 1), n_hw = nh + p.Wf * (p.dw >> 1);
+  const bool hw_lds = n_hw <= kMaxLdsSpatialPairs && p.w_cs == p.h_cs + nh;
+  if (hw_lds) {
+    // 16-byte copies: an odd pair count reads 8 bytes past the w table, inside the tables'
+    // workspace region (which the host pads to 256 bytes)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), bytes = (n_hw * 8 + 15) & ~15;
+    for (int c = wave; c * 1024 < bytes; c += kThreads / 64)
+      lds_copy16(p.h_cs, bytes, c * 1024 + (tid & 63) * 16, reinterpret_cast<char*>(s_hw) + c * 1024);
+  }
 
   const size_t bh = static_cast<size_t>(b) * p.H + h;
   const T* __restrict__ kin = static_cast<const T*>(k_in);
@@ -195,6 +223,7 @@ __device__ __forceinline__ void rope_write_core(const P& p, int b, const void* q
     s_fyx[tid][1] = y;
     s_fyx[tid][2] = rem - y * p.Wf;
   }
+  if (hw_lds) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the LDS table copies have landed
   __syncthreads();
 
   // ---- K (and Q): rotate 16-byte channel vectors ----------------------------
@@ -204,7 +233,7 @@ __device__ __forceinline__ void rope_write_core(const P& p, int b, const void* q
     if (j < passes && n < p.n_tokens) {
       float2 cs[VN / 2];
 #pragma unroll
-      for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, p, c0 + 2 * e, s_fyx[tl][0], s_fyx[tl][1], s_fyx[tl][2]);
+      for (int e = 0; e < VN / 2; ++e) cs[e] = pair_cs(s_tcs, s_hw, hw_lds, p, c0 + 2 * e, s_fyx[tl][0], s_fyx[tl][1], s_fyx[tl][2]);
       *reinterpret_cast<VecS*>(kc + static_cast<size_t>(row0 + n) * p.D + c0) = rotate<TI, TS>(kv[j], cs);
       // fp8 queries are stored times q_scale (the base-2 softmax scale brought into [1, 2))
       if constexpr (HAS_Q)

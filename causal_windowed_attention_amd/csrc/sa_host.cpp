@@ -137,7 +137,7 @@ sa_status derive(const sa_config* c, Derived* d) {
   d->q_off = off; off = align_up(off + d->q_bytes, kAlign);
   d->part_off = off; off = align_up(off + d->part_bytes, kAlign);
   d->sk_off = off; off = align_up(off + d->sk_bytes, kAlign);
-  d->tab_off = off; off = align_up(off + d->tab_bytes, kAlign);
+  d->tab_off = off; off = align_up(off + d->tab_bytes, kAlign);   // padded: the RoPE kernels copy it in 16-byte pieces
   d->total = off;
   return SA_OK;
 }

@@ -170,6 +170,19 @@ def test_edge_shapes(S, W, B, variant):
                       "attend", "append", "attend"], variant=variant)
 
 
+@pytest.mark.parametrize("frame_h,frame_w,head_dim,dtype", [(5, 8, 128, "bf16"), (5, 8, 128, "f32"),
+                                                         (2, 96, 128, "bf16"), (3, 203, 64, "f32")])
+def test_spatial_table_sizes(frame_h, frame_w, head_dim, dtype):
+    """Spatial (cos, sin) tables of every size class: an odd pair count, (5 + 8) x 21 = 273, which
+    a block stages in LDS in 16-byte pieces ending past the table; and more pairs than a block
+    stages (98 x 21 = 2058, 206 x 10 = 2060), which the rotation reads from global memory."""
+    w = synth.small_variant(SMALL, name=f"tables_{frame_h}x{frame_w}_d{head_dim}_{dtype}", frame_h=frame_h,
+                            frame_w=frame_w, head_dim=head_dim, frames_per_chunk=1, batch=1, heads=2,
+                            dtype=dtype)
+    _run_sequence(w, ["attend", "append", "attend", "append", "refresh", "attend", "append", "sink_update",
+                      "attend", "append", "attend"])
+
+
 @pytest.mark.parametrize("variant", [0, 4])
 def test_one_token_chunks(variant):
     w = synth.small_variant(SMALL, name="one_token", frame_h=1, frame_w=1, frames_per_chunk=1,

@@ -106,37 +106,47 @@ __device__ __forceinline__ VecN<TS, 16 / sizeof(TI)> convert(const uint4& in) {
   return out;
 }
 
-// Transpose of a VN x VN block held as VN 16-byte vectors: in[t] = token t's VN
-// channels, out[c] = channel c's VN tokens. bf16: each output dword packs the
-// same-parity halves of two input dwords (v_perm_b32); fp32: register renaming.
+// Transpose of a VN x VN block (VN tokens x VN channels, VN elements per 16 bytes) shared by
+// lanes l and l + 32 of a wave: lane half g holds in[i] = token g VN/2 + i's VN channels and
+// gets out[c] = the VN tokens of channel g VN/2 + c. Each lane transposes its half in registers
+// (bf16: v_perm_b32 packs the same-parity halves of two input dwords; fp32: register renaming),
+// then the two lanes exchange channel halves with v_permlane32_swap, which swaps lanes 32-63 of
+// one register with lanes 0-31 of another. Every lane of the wave must run it.
 template <typename T>
-__device__ __forceinline__ void transpose_block(const uint4 (&in)[16 / sizeof(T)], uint4 (&out)[16 / sizeof(T)]) {
-  constexpr int VN = 16 / sizeof(T);
+__device__ __forceinline__ void transpose_half_block(const uint4 (&in)[8 / sizeof(T)], uint4 (&out)[8 / sizeof(T)]) {
+  constexpr int VN = 16 / sizeof(T), HV = VN / 2;
   auto dw = [](const uint4& v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; };
+  uint2 ch[VN];                                  // this lane's HV tokens of channel c
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {                // channels 2k, 2k+1
-      unsigned lo[4], hi[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {           // tokens 2jj, 2jj+1
-        lo[jj] = __builtin_amdgcn_perm(dw(in[2 * jj + 1], k), dw(in[2 * jj], k), 0x05040100u);
-        hi[jj] = __builtin_amdgcn_perm(dw(in[2 * jj + 1], k), dw(in[2 * jj], k), 0x07060302u);
-      }
-      out[2 * k] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      out[2 * k + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    for (int d = 0; d < 4; ++d) {                // channels 2d, 2d+1
+      ch[2 * d] = make_uint2(__builtin_amdgcn_perm(dw(in[1], d), dw(in[0], d), 0x05040100u),
+                             __builtin_amdgcn_perm(dw(in[3], d), dw(in[2], d), 0x05040100u));
+      ch[2 * d + 1] = make_uint2(__builtin_amdgcn_perm(dw(in[1], d), dw(in[0], d), 0x07060302u),
+                                 __builtin_amdgcn_perm(dw(in[3], d), dw(in[2], d), 0x07060302u));
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < VN; ++c) out[c] = make_uint4(dw(in[0], c), dw(in[1], c), dw(in[2], c), dw(in[3], c));
+    for (int c = 0; c < VN; ++c) ch[c] = make_uint2(dw(in[0], c), dw(in[1], c));
+  }
+  // lane half 0 keeps channels [0, HV) and takes their tokens [HV, VN) from lane l + 32;
+  // lane half 1 keeps channels [HV, VN) and takes their tokens [0, HV) from lane l - 32
+#pragma unroll
+  for (int c = 0; c < HV; ++c) {
+    const auto x = __builtin_amdgcn_permlane32_swap(ch[c].x, ch[HV + c].x, false, false);
+    const auto y = __builtin_amdgcn_permlane32_swap(ch[c].y, ch[HV + c].y, false, false);
+    out[c] = make_uint4(x[0], y[0], x[1], y[1]);
   }
 }
 
 // One block: 64 tokens of head blockIdx.y of batch entry b.
 //  * K (and Q): thread (tid % vpt) owns one 16-byte channel vector of tokens
 //    tid / vpt + j * (256 / vpt); all its loads are issued before any store.
-//  * V: thread owns a VN x VN (tokens x channels) block, transposes it in
-//    registers and stores VN 16-byte rows of V^T; lanes with consecutive token
-//    groups of one channel group write 128 contiguous bytes per channel row.
+//  * V: lanes l and l + 32 share a VN x VN (tokens x channels) block, each loading
+//    VN/2 of its tokens; the block is transposed in registers and across the lane
+//    pair, and each lane stores VN/2 16-byte rows of V^T. Every thread loads and
+//    stores as many V vectors as K vectors; the lanes of one channel group with
+//    consecutive token groups write 128 contiguous bytes per channel row.
 // Every global load is issued before the block sets up its position tables in LDS, so the
 // table set-up and its barrier run under the load latency.
 // TI: input element type; TS: cache (storage) element type. P holds the geometry (a
@@ -182,18 +192,24 @@ __device__ __forceinline__ void rope_write_core(const P& p, int b, const void* q
     return ((static_cast<size_t>(b) * p.in_tokens + in_tok0 + n) * p.H + h) * p.D + c;
   };
 
-  // ---- issue every load first: V blocks, then K (and Q) vectors ---------------
+  // ---- issue every load first: V half-blocks, then K (and Q) vectors ----------
   constexpr int TG = kTileTokens / VN;           // token groups per tile
-  constexpr int MAXB = (TG * 128 / VN + kThreads - 1) / kThreads;   // V blocks per thread (D <= 128)
+  constexpr int HV = VN / 2;                     // tokens of a V block per lane
+  constexpr int PAIRS = kThreads / 2;            // V blocks per round (one per lane pair)
+  constexpr int MAXB = (TG * 128 / VN + PAIRS - 1) / PAIRS;   // rounds (D <= 128)
+  // V blocks: TG * D / VN = 64 D / VN^2, a multiple of 32, so a wave's 32 pairs are all valid
+  // or all invalid (the lane-pair exchange needs the whole wave)
   const int nblk = TG * (p.D / VN);
   const int ntok = min(kTileTokens, p.n_tokens - n0);
-  uint4 vin_r[MAXB][VN];
+  const int vg = (tid >> 5) & 1;                 // lane half
+  const int pair0 = (tid >> 6) * 32 + (tid & 31);
+  uint4 vin_r[MAXB][HV];
 #pragma unroll
   for (int r = 0; r < MAXB; ++r) {
-    const int blk = tid + r * kThreads;
-    const int t0 = (blk % TG) * VN, cb = (blk / TG) * VN;
+    const int blk = pair0 + r * PAIRS;
+    const int t0 = (blk % TG) * VN + vg * HV, cb = (blk / TG) * VN;
 #pragma unroll
-    for (int t = 0; t < VN; ++t)
+    for (int t = 0; t < HV; ++t)
       vin_r[r][t] = blk < nblk && t0 + t < ntok ? *reinterpret_cast<const uint4*>(vin + in_off(n0 + t0 + t, cb))
                                                 : make_uint4(0, 0, 0, 0);
   }
@@ -242,22 +258,22 @@ __device__ __forceinline__ void rope_write_core(const P& p, int b, const void* q
     }
   }
 
-  // ---- V: VN x VN register transposes straight into V^T ---------------------
+  // ---- V: VN x VN transposes (registers and lane pairs) straight into V^T -----
   const bool vec_ok = (row0 % VN) == 0;          // vector-aligned V^T rows
 #pragma unroll
   for (int r = 0; r < MAXB; ++r) {
-    const int blk = tid + r * kThreads;
-    if (blk >= nblk) break;
-    const int t0 = (blk % TG) * VN, cb = (blk / TG) * VN;
-    uint4 out[VN];
-    transpose_block<T>(vin_r[r], out);
+    const int blk = pair0 + r * PAIRS;
+    if (blk >= nblk) break;                      // wave-uniform
+    const int t0 = (blk % TG) * VN, cb = (blk / TG) * VN + vg * HV;   // this lane's HV channels
+    uint4 out[HV];
+    transpose_half_block<T>(vin_r[r], out);
     if (vec_ok && t0 + VN <= ntok) {
 #pragma unroll
-      for (int c = 0; c < VN; ++c)
+      for (int c = 0; c < HV; ++c)
         *reinterpret_cast<VecS*>(vt + static_cast<size_t>(cb + c) * p.key_stride + t0) = convert<TI, TS>(out[c]);
     } else {
 #pragma unroll
-      for (int c = 0; c < VN; ++c) {
+      for (int c = 0; c < HV; ++c) {
         const VecS e = convert<TI, TS>(out[c]);
         for (int t = 0; t < VN && t0 + t < ntok; ++t) vt[static_cast<size_t>(cb + c) * p.key_stride + t0 + t] = e.e[t];
       }

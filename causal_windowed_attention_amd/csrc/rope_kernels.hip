@@ -17,9 +17,10 @@
 //
 // All four are HBM-bound streaming kernels: every input element is read once
 // and every output element written once, with 16-byte vector accesses. V is
-// transposed through LDS so that the cache holds V^T ([D][keys] per (b, h)),
-// the operand layout the attention kernel's PV product reads; its stores are
-// 16-byte vectors along the key axis when the slot offset is 16-byte aligned.
+// transposed in registers and across lane pairs so that the cache holds V^T
+// ([D][keys] per (b, h)), the operand layout the attention kernel's PV product
+// reads; its stores are 16-byte vectors along the key axis when the slot offset
+// is 16-byte aligned.
 #include "sa_internal.h"
 
 #include <type_traits>

@@ -137,3 +137,45 @@ def test_buffer_attend_full_size_sampled(steps):
     say(f"  long512p {'steps' if steps else 'buffer'} of {nb}: sampled max {a:.2e} rel {r:.2e}; lse {la:.2e}")
     assert a <= BF16_ABS and r <= BF16_REL and la <= BF16_ABS
     s.close()
+
+
+@pytest.mark.gpu
+def test_largest_cache_region():
+    """A cache region per (b, h) just under the 2^31 bytes the kernels address with 32-bit buffer
+    offsets: Nc = 65536 (one 256 x 256 frame), S = 1, W = 123 and two buffer chunks make 127 slots,
+    127 * 65536 * 128 * 2 = 2.13e9 bytes of K and as many of V^T per (b, h). The V^T rows of the high
+    channels start near the bound for every attend, and the buffer chunks take the last two slots, so
+    their K rows sit there too. Sampled rows of a chunk attend and of a two-chunk buffer attend are
+    checked against the oracle."""
+    w = synth.small_variant(synth.WORKLOADS["wan1.3b"], name="largest_region", batch=1, heads=2, frame_h=256,
+                            frame_w=256, frames_per_chunk=1, sink_chunks=1, window_chunks=123)
+    nb, nc = 2, w.tokens_per_chunk
+    cfg = config_for(w, max_buffer_chunks=nb)
+    slots = w.sink_chunks + w.window_chunks + 1 + nb
+    assert slots * nc * w.head_dim * 2 < 2 ** 31 <= (slots + 1) * nc * w.head_dim * 2
+    say("largest region: Nc", nc, "slots", slots, "workspace GB", cwa.sa_workspace_bytes(cfg) / 1e9)
+    s = cwa.Stream(cfg)
+    hist = HistoryOracle(spec_for(w))
+    for c in range(3):                                # the sink and two window chunks
+        _, k, v = synth.chunk_qkv(w, c)
+        s.kv_append(dev(k, w.dtype), dev(v, w.dtype))
+        hist.append(k, v)
+    g = np.random.default_rng(11)
+    q, k, v = synth.chunk_qkv(w, 3)
+    out = s.chunk_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(nc - 4, nc), g.choice(nc, 40, replace=False)]))
+    want, _ = hist.attend(q, k, v, rows=rows)
+    a, r = err(host(out[:, torch.as_tensor(rows, device=out.device)]), want[:, rows])
+    say(f"  chunk attend: max {a:.2e} rel {r:.2e}")
+    assert a <= BF16_ABS and r <= BF16_REL, (a, r)
+    q, k, v = _buffer(w, 40, nb)
+    out = s.buffer_attend(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(nb * nc - 4, nb * nc), [nc - 1, nc],
+                                     g.choice(nb * nc, 40, replace=False)]))
+    want, _ = hist.buffer_attend(q, k, v, rows=rows)
+    a, r = err(host(out[:, torch.as_tensor(rows, device=out.device)]), want[:, rows])
+    say(f"  buffer attend (slots {slots - nb}, {slots - 1}): max {a:.2e} rel {r:.2e}")
+    assert a <= BF16_ABS and r <= BF16_REL, (a, r)
+    s.close()

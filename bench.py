@@ -402,6 +402,59 @@ def bench_configs(torch, cwa, synth, steps=20):
     return res
 
 
+def _tiny_schedule(w, attend, append, refresh):
+    """The tiny workload's whole stream: attend and commit every chunk, with the refresh its
+    schedule puts before some chunks."""
+    for c in range(w.n_chunks):
+        if w.refresh_before(c):
+            refresh()
+        attend(c)
+        append(c)
+
+
+def bench_tiny(torch, cwa, synth, reps=20):
+    """The tiny fp32 workload (B 1, H 2, D 64, 8 x 8 frames, F 2 -> Nc 128; S 1, W 2): its whole
+    stream of 6 chunks, refresh included, on a fresh stream each repetition (created and zeroed
+    outside the timed region). Launch-latency bound: a correctness shape, with no fraction of peak."""
+    w = synth.WORKLOADS["tiny_f32"]
+    cfg = cwa.make_config(w.batch, w.heads, w.head_dim, w.frame_h, w.frame_w, w.frames_per_chunk,
+                          w.sink_chunks, w.window_chunks, dtype="f32")
+    data = [tuple(torch.from_numpy(x).cuda() for x in synth.chunk_qkv(w, c)) for c in range(w.n_chunks)]
+    out = torch.empty_like(data[0][0])
+    times = []
+    for _ in range(reps + 2):
+        s = cwa.Stream(cfg, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _tiny_schedule(w, lambda c: s.chunk_attend(*data[c], out=out), lambda c: s.kv_append(*data[c][1:]),
+                       lambda: s.rope_refresh(-1, 0))
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+        s.close()
+    t = sorted(times[2:])
+    return {"workload": w.name, "chunks": w.n_chunks, "tokens_per_chunk": w.tokens_per_chunk,
+            "ms_per_stream_p50": t[len(t) // 2], "ms_per_stream_min": t[0],
+            "ms_per_chunk": t[len(t) // 2] / w.n_chunks,
+            "tokens_per_s": w.batch * w.tokens_per_chunk * w.n_chunks / (t[len(t) // 2] * 1e-3),
+            "what": "host wall time of the whole stream (attend + commit per chunk, one refresh), launch-latency bound"}
+
+
+def tiny_oracle(synth, reps=3):
+    """The fp64 oracle over the tiny workload's whole stream (the same schedule), best of reps."""
+    from oracle import HistoryOracle, StreamSpec
+    w = synth.WORKLOADS["tiny_f32"]
+    data = [synth.chunk_qkv(w, c) for c in range(w.n_chunks)]
+    best = None
+    for _ in range(reps):
+        orc = HistoryOracle(StreamSpec.from_workload(w))
+        t0 = time.perf_counter()
+        _tiny_schedule(w, lambda c: orc.attend(*data[c]), lambda c: orc.append(*data[c][1:]),
+                       lambda: orc.refresh(None, 0))
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return best
+
+
 def bench_batch(torch, cwa, synth, name="long512p", sizes=(1, 2, 3, 4, 6, 8), steps=20, deadline_ms=1.0,
                 model_calls=60, calls=1000, margin=0.10):
     """Ragged batch: n steady-state streams (each its own cache and position) attended in one
@@ -615,7 +668,7 @@ def main():
         s.rope_refresh(base + flip[0] * w.frames_per_chunk, 0)
     b2b_ms["rope_refresh"] = back_to_back(torch, refresh, 20)
 
-    buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = None
+    buffer_res = fp8_res = gdn_res = configs_res = steps_res = batch_res = tiny_res = None
     note("mfma probe")
     mfma_probe = probe_mfma(torch, cwa)
     if not args.headline_only:
@@ -631,6 +684,8 @@ def main():
         steps_res = bench_buffer(torch, cwa, synth, steps_mode=True)
         note("ragged batches")
         batch_res = bench_batch(torch, cwa, synth, deadline_ms=args.deadline_ms)
+        note("tiny fp32 stream")
+        tiny_res = bench_tiny(torch, cwa, synth)
 
     nk = st["visible_keys"]
     flops = 4.0 * w.batch * w.heads * w.head_dim * nc * nk
@@ -726,6 +781,7 @@ def main():
         "buffer_attend": buffer_res,
         "steps_attend": steps_res,
         "batch_attend": batch_res,
+        "tiny_stream": tiny_res,
     }
     if not args.no_cpu_baseline:
         note("cpu baseline (oracle)")
@@ -737,6 +793,10 @@ def main():
                 c["oracle"] = {"seconds_per_chunk": o["seconds_per_chunk"], "tokens_per_s": o["value"],
                                "sample": o["sample"], "cores": o["cores"],
                                "gpu_over_oracle": c["tokens_per_s"] / o["value"]}
+        if tiny_res is not None:
+            # the tiny workload's whole stream, the same schedule through the oracle
+            o_s = tiny_oracle(synth)
+            tiny_res["oracle"] = {"seconds_per_stream": o_s, "gpu_over_oracle": o_s * 1e3 / tiny_res["ms_per_stream_p50"]}
     s.close()
     print(json.dumps(res), flush=True)
 

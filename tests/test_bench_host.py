@@ -44,3 +44,17 @@ def test_cpu_baseline_record():
     assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0 and r["cores"] >= 1
     assert r["seconds_per_chunk"] > 0 and "heads of one steady-state chunk" in r["sample"]
     assert abs(r["value"] * r["seconds_per_chunk"] - w.batch * w.tokens_per_chunk) < 1e-6 * r["value"]
+
+
+def test_tiny_stream_schedule_and_oracle_time():
+    w = synth.WORKLOADS["tiny_f32"]
+    ops = []
+    bench._tiny_schedule(w, lambda c: ops.append(("attend", c)), lambda c: ops.append(("append", c)),
+                         lambda: ops.append(("refresh", None)))
+    want = []
+    for c in range(w.n_chunks):
+        if c == 4:                                   # refresh every 4 chunks, none before chunk 0
+            want.append(("refresh", None))
+        want += [("attend", c), ("append", c)]
+    assert ops == want
+    assert bench.tiny_oracle(synth, reps=1) > 0

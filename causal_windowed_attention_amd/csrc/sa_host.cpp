@@ -233,6 +233,24 @@ void base_write_params(const sa_stream* s, RopeWriteParams* p) {
   p->q_rows = d.Nc;
 }
 
+// The geometry of one batched rope_apply launch over n entries of stream s's configuration:
+// each entry's chunk has Nc tokens, its inputs hold in_tokens tokens per batch entry and its Q
+// scratch q_rows rows per (b, h). The per-entry pointers, rows and positions are the caller's.
+void base_batch_params(const sa_stream* s, int32_t n, int32_t in_tokens, int32_t q_rows, sa::RopeBatchParams* p) {
+  RopeWriteParams rp;
+  base_write_params(s, &rp);
+  const Derived& d = s->d;
+  std::memset(p, 0, sizeof(*p));
+  p->h_cs = rp.h_cs; p->w_cs = rp.w_cs;
+  p->k_bh_stride = rp.k_bh_stride; p->vt_bh_stride = rp.vt_bh_stride;
+  p->key_stride = rp.key_stride; p->n_tokens = d.Nc; p->in_tokens = in_tokens;
+  p->B = rp.B; p->H = rp.H; p->D = rp.D; p->Hf = rp.Hf; p->Wf = rp.Wf;
+  p->dt = rp.dt; p->dh = rp.dh; p->dw = rp.dw; p->n_frames = d.F; p->q_rows = q_rows;
+  p->q_scale = rp.q_scale;
+  p->n = n;
+  for (int j = 0; j < d.dt / 2; ++j) p->theta_t[j] = freq(d, d.dt, j);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Launch with optional event timing on the launch stream.
@@ -830,18 +848,8 @@ sa_status sa_buffer_attend(sa_stream* s, const void* q, const void* k, const voi
     // chunk j, with its inputs, Q scratch rows and cache slot offset to chunk j and its
     // frames at temporal positions t_next + j F on.
     {
-      RopeWriteParams rp;
-      base_write_params(s, &rp);
       sa::RopeBatchParams rb;
-      std::memset(&rb, 0, sizeof(rb));
-      rb.h_cs = rp.h_cs; rb.w_cs = rp.w_cs;
-      rb.k_bh_stride = rp.k_bh_stride; rb.vt_bh_stride = rp.vt_bh_stride;
-      rb.key_stride = rp.key_stride; rb.n_tokens = d.Nc; rb.in_tokens = n_chunks * d.Nc;
-      rb.B = rp.B; rb.H = rp.H; rb.D = rp.D; rb.Hf = rp.Hf; rb.Wf = rp.Wf;
-      rb.dt = rp.dt; rb.dh = rp.dh; rb.dw = rp.dw; rb.n_frames = d.F; rb.q_rows = n_chunks * d.Nc;
-      rb.q_scale = rp.q_scale;
-      rb.n = n_chunks;
-      for (int j = 0; j < d.dt / 2; ++j) rb.theta_t[j] = freq(d, d.dt, j);
+      base_batch_params(s, n_chunks, n_chunks * d.Nc, n_chunks * d.Nc, &rb);
       const size_t in_elem = d.dtype == SA_F32 ? 4 : 2;
       const size_t chunk_in = static_cast<size_t>(d.Nc) * d.H * d.D * in_elem;    // bytes of one chunk's tokens
       const size_t chunk_q = static_cast<size_t>(d.Nc) * d.D * d.elem;             // bytes of one chunk's Q rows
@@ -935,19 +943,7 @@ sa_status sa_batch_attend(int32_t n, sa_stream* const* streams, const void* cons
     std::memset(&ap, 0, sizeof(ap));
     // one launch stages every entry's chunk in its own workspace
     sa::RopeBatchParams bp;
-    std::memset(&bp, 0, sizeof(bp));
-    {
-      RopeWriteParams rp;
-      base_write_params(s0, &rp);
-      bp.h_cs = rp.h_cs; bp.w_cs = rp.w_cs;
-      bp.k_bh_stride = rp.k_bh_stride; bp.vt_bh_stride = rp.vt_bh_stride;
-      bp.key_stride = rp.key_stride; bp.n_tokens = rp.n_tokens; bp.in_tokens = rp.in_tokens;
-      bp.B = rp.B; bp.H = rp.H; bp.D = rp.D; bp.Hf = rp.Hf; bp.Wf = rp.Wf;
-      bp.dt = rp.dt; bp.dh = rp.dh; bp.dw = rp.dw; bp.n_frames = rp.n_frames; bp.q_rows = rp.q_rows;
-      bp.q_scale = rp.q_scale;
-    }
-    bp.n = n;
-    for (int j = 0; j < d.dt / 2; ++j) bp.theta_t[j] = freq(d, d.dt, j);
+    base_batch_params(s0, n, d.Nc, d.Nc, &bp);
     for (int i = 0; i < n; ++i) {
       sa_stream* si = streams[i];
       bp.q[i] = q[i]; bp.k[i] = k[i]; bp.v[i] = v[i];

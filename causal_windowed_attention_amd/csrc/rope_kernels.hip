@@ -7,9 +7,11 @@
 //
 // The rotation is RoFormer's per channel pair; the pages name 3D (t, h, w) RoPE
 // offsets and their periodic re-basing at chunk boundaries (StreamDiffusionV2,
-// "Sommario tecnico" 2.A.2). cos/sin come from host fp64 tables rounded to
-// fp32 (spatial tables in the workspace, staged in LDS by each block when they
-// fit; the chunk's temporal table by value), so no device trigonometry runs. Arithmetic is fp32; stores round to the cache
+// "Sommario tecnico" 2.A.2). cos/sin are fp64 values rounded to fp32: the
+// spatial tables come from the host (in the workspace, staged in LDS by each
+// block when they fit), a single launch's temporal table from the host by value,
+// and a batched launch computes each entry's temporal angles in fp64 on the
+// device. Arithmetic is fp32; stores round to the cache
 // type (bf16: round to nearest even; fp8: E4M3 of the OCP 8-bit float format,
 // clamped to +-448 and rounded to nearest even by v_cvt_pk_fp8_f32, whose
 // unclamped result above 464 would be NaN). Inputs are fp32 for an fp32 cache
